@@ -1,0 +1,487 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Every test here runs on the CPU.  The pins are hand-derived values
+(``tests/golden``), closed forms, brute force on tiny inputs by an independent
+method (counting instead of sorting, exact rational arithmetic instead of
+floating point) and invariants of the definition.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+from conftest import GOLDEN
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _expand(expr, n=32):
+    i = np.arange(n)
+    k = i
+    expr = expr.replace(" mod ", " % ")
+    return np.asarray(eval(expr, {"i": i, "k": k, "np": np}), dtype=np.float64) * np.ones(n)
+
+
+# ----------------------------------------------------------------- roundings
+
+def test_bf16_round_hand_ties():
+    # bf16 keeps 8 significant bits: the spacing at 1.0 is 2^-7
+    cases = {
+        1.0 + 2.0 ** -8: 1.0,                     # tie -> even (1.0)
+        1.0 + 3 * 2.0 ** -8: 1.0 + 2.0 ** -6,     # tie -> even (up)
+        1.0 + 2.0 ** -8 + 2.0 ** -20: 1.0 + 2.0 ** -7,
+        -(1.0 + 2.0 ** -8): -1.0,
+        65504.0: 65536.0,
+    }
+    for x, want in cases.items():
+        assert float(O.bf16_round(np.float32(x))) == want, x
+
+
+def test_bf16_round_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(1)
+    a = (rng.standard_normal(100000) * np.exp(rng.uniform(-30, 30, 100000))).astype(np.float32)
+    want = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(O.bf16_round(a), want)
+
+
+def _bf16_exact(fr: Fraction) -> Fraction:
+    """Round a rational to 8 significant bits, ties to even (brute force)."""
+    if fr == 0:
+        return fr
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = 0
+    while a >= 2:
+        a /= 2
+        e += 1
+    while a < 1:
+        a *= 2
+        e -= 1
+    scaled = a * 128
+    lo = math.floor(scaled)
+    rem = scaled - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return sign * Fraction(lo, 128) * Fraction(2) ** e
+
+
+def test_act_round_bf16_from_f64_single_rounding():
+    rng = np.random.default_rng(2)
+    vals = rng.standard_normal(400) * np.exp(rng.uniform(-10, 10, 400))
+    # values just beside bf16 midpoints, where fp64 -> fp32 -> bf16 would round twice
+    mid = 1.0 + 2.0 ** -8
+    vals = np.concatenate([vals, [mid + 2.0 ** -40, mid - 2.0 ** -40, -(mid + 2.0 ** -40)]])
+    got = O.act_round(vals, "bf16")
+    for v, g in zip(vals, got):
+        assert Fraction(float(g)) == _bf16_exact(Fraction(float(v))), v
+
+
+# ------------------------------------------------------------- quantiser
+
+@pytest.mark.parametrize("case", _load("quant_blocks.json")["cases"], ids=lambda c: c["name"])
+def test_quantiser_hand_blocks(case):
+    x = np.asarray(case["x_list"]) if "x_list" in case else _expand(case["x"])
+    if "const" in case["name"]:
+        x = np.full(32, 1.25)
+    d, m, q = O.quantise_rows(x.astype(np.float32)[None, :], case["bits"])
+    assert float(d[0, 0]) == case["d"]
+    assert float(m[0, 0]) == case["m"]
+    want_q = np.asarray(case["q_list"]) if "q_list" in case else _expand(case["q"]).astype(int)
+    np.testing.assert_array_equal(q[0], want_q)
+    # dequantised values reproduce the (exactly representable) inputs
+    v = O.dequantise(d, m, q, act="f32")
+    if "const" not in case["name"] and "ties" not in case["name"]:
+        np.testing.assert_array_equal(v[0], x)
+
+
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_quantiser_reconstruction_bound(bits):
+    rng = np.random.default_rng(bits)
+    w = (rng.standard_normal((64, 256)) * np.exp(rng.uniform(-6, 2, (64, 1)))).astype(np.float32)
+    d, m, q = O.quantise_rows(w, bits)
+    L = O.LEVELS[bits]
+    assert q.max() <= L
+    v = O.dequantise(d, m, q, act="f32").reshape(64, -1, 32)
+    blk = w.astype(np.float64).reshape(64, -1, 32)
+    lo = blk.min(-1, keepdims=True)
+    d64 = d.astype(np.float64)[..., None]
+    m64 = m.astype(np.float64)[..., None]
+    # rounding to the nearest level costs at most d/2; the fp16 min and scale
+    # shift the grid by |lo - m| and by at most L * d * 2^-11
+    bound = 0.5 * d64 * (1 + 1e-6) + np.abs(lo - m64) + L * d64 * 2.0 ** -10 + 1e-30
+    assert np.all(np.abs(blk - v) <= bound)
+    # the largest and smallest weights land on the top and bottom codes
+    assert np.all(q.reshape(64, -1, 32).max(-1) >= L - 1)
+    assert np.all(q.reshape(64, -1, 32).min(-1) <= 1)
+
+
+def test_quantiser_rejects_nonfinite():
+    w = np.zeros((1, 32), np.float32)
+    w[0, 3] = np.nan
+    with pytest.raises(ValueError):
+        O.quantise_rows(w, 4)
+    w[0, 3] = 5e5  # scale 5e5/15 = 33333 still fits fp16
+    O.quantise_rows(w, 4)
+    w[0, 3] = 3e9  # (hi - lo) / 15 > 65504: fp16 scale overflows
+    with pytest.raises(ValueError):
+        O.quantise_rows(w, 4)
+
+
+def test_dequantise_is_one_fp32_rounding():
+    rng = np.random.default_rng(3)
+    d = rng.uniform(1e-4, 10, (8, 4)).astype(np.float16)
+    m = rng.uniform(-10, 10, (8, 4)).astype(np.float16)
+    q = rng.integers(0, 16, (8, 128)).astype(np.uint8)
+    v = O.dequantise(d, m, q, act="f32")
+    for r in range(8):
+        for c in range(0, 128, 7):
+            exact = Fraction(float(d[r, c // 32])) * int(q[r, c]) + Fraction(float(m[r, c // 32]))
+            # float32 rounding of the exact rational: compare against the two
+            # neighbouring float32 values
+            f = np.float32(float(exact))
+            assert abs(Fraction(float(f)) - exact) <= abs(Fraction(float(np.nextafter(f, np.float32(np.inf)))) - exact)
+            assert abs(Fraction(float(f)) - exact) <= abs(Fraction(float(np.nextafter(f, np.float32(-np.inf)))) - exact)
+            assert v[r, c] == float(f)
+    vb = O.dequantise(d, m, q, act="bf16")
+    np.testing.assert_array_equal(vb, O.bf16_round(v.astype(np.float32)).astype(np.float64))
+
+
+# ------------------------------------------------------------ code fields
+
+@pytest.mark.parametrize("case", _load("code_fields.json")["cases"], ids=lambda c: str(c["bits"]))
+def test_code_field_hand_words(case):
+    bits = case["bits"]
+    q = _expand(case["q"]).astype(np.uint8)
+    field = O.encode_codes(q, bits)
+    words = field.view("<u4")
+    assert [f"0x{int(w):08X}" for w in words] == [w.upper().replace("0X", "0x") for w in case["words"]]
+    np.testing.assert_array_equal(O.decode_codes(field, bits), q)
+
+
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_code_positions_partition_the_field(bits):
+    pos = O.code_bit_positions(bits)
+    flat = sorted(p for code in pos for p in code)
+    assert flat == list(range(32 * bits))
+    assert all(len(code) == bits for code in pos)
+
+
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_code_field_single_code_brute_force(bits):
+    # setting one code to all-ones must set exactly its listed bits
+    pos = O.code_bit_positions(bits)
+    for k in range(32):
+        q = np.zeros(32, np.uint8)
+        q[k] = O.LEVELS[bits]
+        field = O.encode_codes(q, bits)
+        as_int = int.from_bytes(field.tobytes(), "little")
+        assert as_int == sum(1 << p for p in pos[k])
+
+
+# ------------------------------------------------------------------ tiles
+
+@pytest.mark.parametrize("case", _load("tile_index.json")["cases"])
+def test_tile_index_hand(case):
+    S, R, C = case["S"], case["R"], case["C"]
+    q = np.zeros((S, R, C), np.uint8)
+    d = np.zeros((S, R, C // 32), np.float16)
+    m = np.zeros((S, R, C // 32), np.float16)
+    d[case["s"], case["r"], case["j"]] = np.float16(1.5)
+    q[case["s"], case["r"], 32 * case["j"]] = 3
+    codes, dm = O.pack_tiles(q, d, m, 4)
+    hit = np.nonzero(dm)[0]
+    assert list(hit) == [case["index"]]
+    assert dm[case["index"]] == np.float16(1.5).view(np.uint16)
+    nz = np.nonzero(codes)[0]
+    assert list(nz // 16) == [case["index"]]
+
+
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_tile_pack_is_a_bijection(bits):
+    S, R, C = 2, 32, 256
+    nb = C // 32
+    ident = np.arange(S * R * nb).reshape(S, R, nb)
+    # encode each block's identity in d (exact in fp16 below 2048) and m
+    d = (ident % 2048).astype(np.float16)
+    m = (ident // 2048).astype(np.float16)
+    q = np.zeros((S, R, C), np.uint8)
+    _, dm = O.pack_tiles(q, d, m, bits)
+    got = (dm & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.int64) + \
+        2048 * ((dm >> 16).astype(np.uint16).view(np.float16).astype(np.int64))
+    assert sorted(got.tolist()) == list(range(S * R * nb))
+
+
+# ------------------------------------------------------------------ tiers
+
+def _brute_tiers(pop, n_slots):
+    E = len(pop)
+    tm = []
+    for e in range(E):
+        rank = sum(1 for f in range(E) if pop[f] > pop[e] or (pop[f] == pop[e] and f < e))
+        if rank < n_slots[0]:
+            tm.append((0, rank))
+        elif rank < n_slots[0] + n_slots[1]:
+            tm.append((1, rank - n_slots[0]))
+        else:
+            tm.append((2, rank - n_slots[0] - n_slots[1]))
+    return tm
+
+
+def test_tiers_brute_force():
+    rng = np.random.default_rng(4)
+    for E, ns in ((8, (2, 4, 2)), (13, (3, 7, 3)), (64, (16, 32, 16)), (5, (5, 0, 0))):
+        pop = rng.integers(0, 4, E).astype(np.uint64)      # many ties
+        tm, se = O.build_tiers(pop, ns)
+        want = _brute_tiers(pop.tolist(), ns)
+        assert [(int(v) >> 16, int(v) & 0xFFFF) for v in tm] == want
+        # slot_expert inverts the ranking
+        for e in range(E):
+            tier, slot = want[e]
+            assert se[[0, ns[0], ns[0] + ns[1]][tier] + slot] == e
+
+
+def test_tiers_uniform_popularity_identity():
+    tm, se = O.build_tiers(np.zeros(64, np.uint64), (64, 0, 0))
+    assert tm.tolist() == list(range(64))
+    assert se.tolist() == list(range(64))
+
+
+def test_tiers_reject_bad_counts():
+    with pytest.raises(ValueError):
+        O.build_tiers(np.zeros(8, np.uint64), (2, 2, 2))
+
+
+# ----------------------------------------------------------------- router
+
+def test_router_keys_exact_vs_fp64():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 64)).astype(np.float32).astype(np.float64)
+    w = (rng.standard_normal((6, 64)) * 0.02).astype(np.float32).astype(np.float64)
+    b = rng.standard_normal(6).astype(np.float32).astype(np.float64)
+    exact = O.router_keys(x, w, b, exact=True)
+    fast = O.router_keys(x, w, b)
+    np.testing.assert_allclose(fast, exact, rtol=0, atol=1e-14)
+    # hand check of one key with exact rationals
+    fr = sum(Fraction(float(a)) * Fraction(float(c)) for a, c in zip(x[1], w[4])) + Fraction(float(b[4]))
+    assert exact[1, 4] == float(fr)
+
+
+def _brute_topk(keys_row, k):
+    E = len(keys_row)
+
+    def better(a, b):           # is expert a ranked before expert b?
+        ka, kb = keys_row[a], keys_row[b]
+        if math.isnan(kb) and not math.isnan(ka):
+            return True
+        if math.isnan(ka):
+            return math.isnan(kb) and a < b
+        return ka > kb or (ka == kb and a < b)
+
+    rank = {e: sum(1 for f in range(E) if f != e and better(f, e)) for e in range(E)}
+    return [e for e, _ in sorted(rank.items(), key=lambda kv: kv[1])][:k]
+
+
+def test_topk_brute_force_with_ties_and_nan():
+    rng = np.random.default_rng(6)
+    for trial in range(200):
+        E = int(rng.integers(1, 12))
+        k = int(rng.integers(1, E + 1))
+        keys = rng.integers(-3, 3, E).astype(np.float64)     # many exact ties
+        if trial % 5 == 0:
+            keys[rng.integers(0, E)] = np.nan
+        if trial % 7 == 0:
+            keys[rng.integers(0, E)] = -0.0
+        got = O.select_topk(keys[None, :], k)[0].tolist()
+        assert got == _brute_topk(keys.tolist(), k), (keys, k)
+
+
+def test_duplicated_router_rows_tie_to_lower_id():
+    rng = np.random.default_rng(7)
+    H, E = 64, 8
+    w = (rng.standard_normal((E, H)) * 0.02).astype(np.float32).astype(np.float64)
+    w[5] = w[2]                      # identical rows -> identical exact keys
+    w[6] = w[2]
+    x = rng.standard_normal((4, H)).astype(np.float32).astype(np.float64)
+    # make experts 2/5/6 the best by scaling
+    w[[2, 5, 6]] *= 50
+    keys = O.router_keys(x, w, None, exact=True)
+    assert np.all(keys[:, 2] == keys[:, 5]) and np.all(keys[:, 2] == keys[:, 6])
+    ids = O.select_topk(keys, 3)
+    for t in range(4):
+        if keys[t, 2] > np.max(np.delete(keys[t], [2, 5, 6])):
+            assert ids[t].tolist() == [2, 5, 6]
+
+
+def test_gate_weights_invariants():
+    rng = np.random.default_rng(8)
+    keys = rng.standard_normal((50, 32)) * 3
+    for k in (1, 2, 10, 32):
+        ids = O.select_topk(keys, k)
+        g = O.gate_weights(keys, ids)
+        assert np.all(np.abs(g.sum(1) - 1) <= 1e-15)
+        assert np.all(np.diff(g, axis=1) <= 0)        # rank order -> non-increasing weights
+        if k == 1:
+            assert np.all(g == 1.0)
+        if k == 32:
+            assert np.all(np.sort(ids, 1) == np.arange(32))
+    # closed form for two experts: g0 = 1/(1+e^(k1-k0))
+    kk = np.array([[0.25, 1.5, -2.0]])
+    ids = O.select_topk(kk, 2)
+    g = O.gate_weights(kk, ids)
+    assert ids.tolist() == [[1, 0]]
+    assert abs(g[0, 0] - 1 / (1 + math.exp(0.25 - 1.5))) < 1e-15
+
+
+# ------------------------------------------------------------------- sort
+
+def test_sort_routes_vs_lexsort_and_brute_force():
+    rng = np.random.default_rng(9)
+    for T, K, E in ((1, 1, 1), (7, 3, 5), (64, 4, 64), (300, 10, 512)):
+        ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+        off, sr = O.sort_routes(ids, E)
+        flat = ids.reshape(-1)
+        want = np.lexsort((np.arange(flat.size), flat))
+        np.testing.assert_array_equal(sr, want)
+        assert off[0] == 0 and off[-1] == T * K and np.all(np.diff(off) >= 0)
+        for e in range(0, E, max(1, E // 17)):
+            bucket = sr[off[e]:off[e + 1]]
+            assert np.all(flat[bucket] == e) and np.all(np.diff(bucket) > 0)
+            assert off[e] == int(np.sum(flat < e))
+
+
+# ------------------------------------------------------------------ layer
+
+def _const_block(rows, cols, q_val, d_val):
+    return (np.full((rows, cols // 32), d_val, np.float16),
+            np.zeros((rows, cols // 32), np.float16),
+            np.full((rows, cols), q_val, np.uint8))
+
+
+def _closed_form_layer():
+    H, I = 64, 32
+    w_router = np.zeros((2, H))
+    w_router[0] = 2.0 ** -7
+    w_router[1] = 2.0 ** -6
+
+    def experts(e):
+        return O.ExpertBlocks(
+            bits=4,
+            gate=_const_block(I, H, 1, 0.5),
+            up=_const_block(I, H, 1, 0.25),
+            down=_const_block(H, I, 1, 0.125 if e == 0 else 0.0625))
+
+    shared = (np.full((I, H), 2.0 ** -5), np.full((I, H), 2.0 ** -6), np.full((H, I), 2.0 ** -5))
+    return O.OracleLayer(act="bf16", w_router=w_router, bias=None, top_k=2,
+                         experts=experts, shared=shared)
+
+
+def test_layer_closed_form():
+    spec = _load("layer_closed_form.json")
+    layer = _closed_form_layer()
+    x = np.stack([np.ones(64), 2 * np.ones(64)])
+    out = O.moe_layer(x, layer, exact_keys=True)
+    assert out["ids"].tolist() == [spec["ids"], spec["ids"]]
+    # token 0 (x = 1): y = 1024 (1 + 1/(1 + e^0.5)) + 225/128
+    y0 = 1024 * (1 + 1 / (1 + math.exp(0.5))) + 225 / 128
+    # token 1 (x = 2): keys 2.0, 1.0; h = bf16(silu(64)*32) = 2048; routed outs
+    # 8192 and 4096; shared h_s = bf16(2*4/(1+e^-4)) = 251/32
+    y1 = 4096 * (1 + 1 / (1 + math.exp(1.0))) + 251 / 32
+    np.testing.assert_allclose(out["y"][0], y0, rtol=1e-15)
+    np.testing.assert_allclose(out["y"][1], y1, rtol=1e-15)
+
+
+def _random_layer(E, K, H, I, act, seed, shared=True, bits=4):
+    rng = np.random.default_rng(seed)
+    w_router = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    w_router = O.bf16_round(w_router) if act == "bf16" else w_router
+    blocks = {}
+    for e in range(E):
+        mats = []
+        for rows, cols in ((I, H), (I, H), (H, I)):
+            w = (rng.standard_normal((rows, cols)) / np.sqrt(cols)).astype(np.float32)
+            mats.append(O.quantise_rows(w, bits))
+        blocks[e] = O.ExpertBlocks(bits, *mats)
+    sh = None
+    if shared:
+        sh = tuple(O.act_round(rng.standard_normal((r, c)) / np.sqrt(c), act)
+                   for r, c in ((I, H), (I, H), (H, I)))
+    return O.OracleLayer(act=act, w_router=w_router.astype(np.float64), bias=None, top_k=K,
+                         experts=lambda e: blocks[e], shared=sh), blocks
+
+
+def test_layer_single_expert_is_dense_swiglu():
+    layer, blocks = _random_layer(E=1, K=1, H=128, I=64, act="bf16", seed=10, shared=False)
+    rng = np.random.default_rng(11)
+    x = O.act_round(rng.standard_normal((5, 128)), "bf16")
+    y = O.moe_layer(x, layer)["y"]
+    gw, uw, dw = (O.dequantise(*m, act="bf16") for m in (blocks[0].gate, blocks[0].up, blocks[0].down))
+    g = np.matmul(x, gw.T)
+    u = np.matmul(x, uw.T)
+    h = O.act_round(g / (1 + np.exp(-g)) * u, "bf16")
+    np.testing.assert_allclose(y, np.matmul(h, dw.T), rtol=1e-13, atol=1e-13)
+
+
+def test_layer_zero_input():
+    layer, _ = _random_layer(E=6, K=2, H=128, I=64, act="bf16", seed=12)
+    layer.bias = np.linspace(-1, 1, 6)
+    out = O.moe_layer(np.zeros((3, 128)), layer)
+    np.testing.assert_array_equal(out["keys"], np.tile(layer.bias, (3, 1)))
+    assert out["ids"].tolist() == [[5, 4]] * 3
+    np.testing.assert_array_equal(out["y"], 0.0)
+
+
+def test_layer_identical_experts_independent_of_routing():
+    layer, blocks = _random_layer(E=5, K=3, H=128, I=64, act="bf16", seed=13)
+    same = blocks[0]
+    layer.experts = lambda e: same
+    layer._cache.clear()
+    rng = np.random.default_rng(14)
+    x = O.act_round(rng.standard_normal((4, 128)), "bf16")
+    y = O.moe_layer(x, layer)["y"]
+    gw, uw, dw = (O.dequantise(*m, act="bf16") for m in (same.gate, same.up, same.down))
+    _, out = O.expert_ffn(x, gw, uw, dw, "bf16")
+    _, out_s = O.expert_ffn(x, *layer.shared, act="bf16")
+    np.testing.assert_allclose(y, out + out_s, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_two_bit_codes_in_four_bit_container():
+    # 2-bit codes are valid 4-bit codes: storing them in the 4-bit tier with the
+    # same d and m must give the same layer output
+    layer, blocks = _random_layer(E=4, K=2, H=128, I=64, act="bf16", seed=15, bits=2)
+    rng = np.random.default_rng(16)
+    x = O.act_round(rng.standard_normal((3, 128)), "bf16")
+    y2 = O.moe_layer(x, layer)["y"]
+    # round-trip the codes through the 4-bit field
+    def widen(mat):
+        d, m, q = mat
+        f = O.encode_codes(q.reshape(q.shape[0], -1, 32), 4)
+        return d, m, O.decode_codes(f, 4).reshape(q.shape)
+    wide = {e: O.ExpertBlocks(4, widen(b.gate), widen(b.up), widen(b.down)) for e, b in blocks.items()}
+    layer.experts = lambda e: wide[e]
+    layer._cache.clear()
+    np.testing.assert_array_equal(O.moe_layer(x, layer)["y"], y2)
+
+
+def test_layer_relabelling_invariance():
+    layer, blocks = _random_layer(E=7, K=3, H=128, I=64, act="bf16", seed=17)
+    rng = np.random.default_rng(18)
+    x = O.act_round(rng.standard_normal((6, 128)), "bf16")
+    layer.bias = rng.standard_normal(7)
+    y = O.moe_layer(x, layer)["y"]
+    perm = rng.permutation(7)                 # new id j holds old expert perm[j]
+    layer2 = O.OracleLayer(act="bf16", w_router=layer.w_router[perm], bias=layer.bias[perm],
+                           top_k=3, experts=lambda j: blocks[int(perm[j])], shared=layer.shared)
+    out2 = O.moe_layer(x, layer2)
+    np.testing.assert_allclose(out2["y"], y, rtol=1e-12, atol=1e-12)
+    ids1 = O.moe_layer(x, layer)["ids"]
+    np.testing.assert_array_equal(perm[out2["ids"]], ids1)
