@@ -41,6 +41,7 @@ __all__ = [
     "OracleLayer",
     "expert_ffn",
     "moe_layer",
+    "output_cast",
 ]
 
 #: Highest code of a b-bit block: L = 2**b - 1.
@@ -530,3 +531,13 @@ def moe_layer(x, layer: OracleLayer, tokens: Optional[Sequence[int]] = None,
         _, out_s = expert_ffn(x[rows], *layer.shared, act=layer.act)
         y += out_s
     return {"keys": keys, "ids": ids, "g": g, "y": y}
+
+
+def output_cast(y, out_dtype: str) -> np.ndarray:
+    """The layer's last step: the float64 output rounded once to the output
+    dtype ("f32" or "bf16", round to nearest even), returned as float64.
+
+    The output of a bf16 layer is itself a bf16 tensor; its comparison with
+    the oracle is with this rounded value (rounding alone moves a vector of
+    unit-scale values by ~1.6e-3 relative L2)."""
+    return act_round(y, out_dtype)

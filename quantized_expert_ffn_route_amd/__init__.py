@@ -1,0 +1,320 @@
+"""Python binding of ``libmoe.so``: the routed, popularity-tiered, dequantised
+MoE FFN layer for AMD Instinct MI355X (gfx950).
+
+Argument marshalling only: every step of the layer runs in the HIP library
+(``csrc/``), whose C ABI is declared in ``include/moe.h``.  The names mirror
+the C entry points: :func:`route`, :func:`build_tiers`,
+:func:`forward_decode`, :func:`forward_prefill`.  Device buffers are torch
+tensors; work is enqueued on torch's current HIP stream.  If the library has
+not been built, every call raises :class:`MoeLibraryMissing` -- there is no
+fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_int32, c_size_t, c_uint64, c_void_p
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_ENOSPC", "MOE_EHIP",
+    "MOE_F32", "MOE_BF16", "MOE_GATE", "MOE_UP", "MOE_DOWN", "MOE_CODES", "MOE_DM",
+    "MOE_SRC_F32", "MOE_SRC_CODES",
+    "MoeError", "MoeLibraryMissing", "MoeDims", "MoeLayer", "MoeExpertSource",
+    "lib", "library_path", "status_string", "dims", "tier_table_bytes",
+    "build_tiers", "route", "forward_decode", "forward_prefill", "workspace_bytes",
+    "DeviceLayer",
+]
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16 = 0, 1
+MOE_GATE, MOE_UP, MOE_DOWN = 0, 1, 2
+MOE_CODES, MOE_DM = 0, 1
+MOE_SRC_F32, MOE_SRC_CODES = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libmoe.so")
+
+
+class MoeLibraryMissing(RuntimeError):
+    pass
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class MoeDims(ctypes.Structure):
+    _fields_ = [("hidden", c_int32), ("inter", c_int32), ("n_experts", c_int32),
+                ("top_k", c_int32), ("has_shared", c_int32), ("act", c_int32)]
+
+
+class MoeLayer(ctypes.Structure):
+    _fields_ = [("w_router", c_void_p), ("b_router", c_void_p), ("tier_map", c_void_p),
+                ("n_slots", c_int32 * 3), ("tier_bits", c_int32 * 3),
+                ("codes", (c_void_p * 3) * 3), ("dm", (c_void_p * 3) * 3),
+                ("w_shared", c_void_p * 3)]
+
+
+class MoeExpertSource(ctypes.Structure):
+    _fields_ = [("kind", c_int32), ("w", c_void_p * 3), ("q", c_void_p * 3),
+                ("d", c_void_p * 3), ("m", c_void_p * 3)]
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded ``libmoe.so`` (raises :class:`MoeLibraryMissing` if absent)."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise MoeLibraryMissing(
+                f"{path} is not built; run `python -m quantized_expert_ffn_route_amd.build`")
+        L = ctypes.CDLL(path)
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_tier_table_bytes.restype = c_size_t
+        L.moe_tier_table_bytes.argtypes = [POINTER(MoeDims), c_int32, c_int32, c_int32, c_int32]
+        L.moe_build_tiers.restype = ctypes.c_int
+        L.moe_build_tiers.argtypes = [POINTER(MoeDims), c_void_p, POINTER(c_int32), POINTER(c_int32),
+                                      POINTER(MoeExpertSource), c_void_p, c_void_p,
+                                      POINTER(MoeLayer), c_int32, c_void_p]
+        L.moe_route.restype = ctypes.c_int
+        L.moe_route.argtypes = [POINTER(MoeDims), POINTER(MoeLayer), c_void_p, c_int32, c_void_p,
+                                c_void_p, c_void_p, POINTER(c_size_t), c_void_p]
+        L.moe_forward_decode.restype = ctypes.c_int
+        L.moe_forward_decode.argtypes = [POINTER(MoeDims), POINTER(MoeLayer), c_void_p, c_int32,
+                                         c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                         POINTER(c_size_t), c_void_p]
+        L.moe_forward_prefill.restype = ctypes.c_int
+        L.moe_forward_prefill.argtypes = [POINTER(MoeDims), POINTER(MoeLayer), c_void_p, c_int32,
+                                          c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_void_p, POINTER(c_size_t), c_void_p]
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def dims(hidden: int, inter: int, n_experts: int, top_k: int, has_shared: bool, act: str) -> MoeDims:
+    return MoeDims(hidden, inter, n_experts, top_k, int(bool(has_shared)),
+                   MOE_BF16 if act == "bf16" else MOE_F32)
+
+
+def tier_table_bytes(d: MoeDims, bits: int, n_slots: int, mat: int, which: int) -> int:
+    return int(lib().moe_tier_table_bytes(ctypes.byref(d), bits, n_slots, mat, which))
+
+
+def _ptr(t) -> Optional[int]:
+    """Device/host address of a torch tensor or NumPy array (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream
+    import torch
+
+    if not torch.cuda.is_available():
+        return None
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _i32x3(v: Sequence[int]):
+    return (c_int32 * 3)(*[int(a) for a in v])
+
+
+def build_tiers(d: MoeDims, popularity, n_slots, tier_bits, source: Optional[MoeExpertSource] = None,
+                dst: Optional[MoeLayer] = None, dst_on_device: bool = False, stream=None):
+    """``moe_build_tiers``: returns ``(tier_map, slot_expert)`` as int32 arrays.
+
+    ``source``/``dst`` as in the C header; the caller keeps the arrays that
+    ``source`` points to alive for the call.
+    """
+    pop = np.ascontiguousarray(popularity, dtype=np.uint64)
+    E = d.n_experts
+    tmap = np.zeros(E, dtype=np.int32)
+    sexp = np.zeros(E, dtype=np.int32)
+    rc = lib().moe_build_tiers(ctypes.byref(d), pop.ctypes.data, _i32x3(n_slots), _i32x3(tier_bits),
+                               ctypes.byref(source) if source is not None else None,
+                               tmap.ctypes.data, sexp.ctypes.data,
+                               ctypes.byref(dst) if dst is not None else None, int(dst_on_device),
+                               _stream(stream) if dst_on_device else None)
+    _check(rc, "moe_build_tiers")
+    return tmap, sexp
+
+
+def workspace_bytes(kind: str, d: MoeDims, layer: MoeLayer, T: int, y_dt: int = MOE_F32) -> int:
+    """Workspace size of ``route`` / ``decode`` / ``prefill`` for T tokens."""
+    n = c_size_t(0)
+    L = lib()
+    if kind == "route":
+        rc = L.moe_route(ctypes.byref(d), ctypes.byref(layer), None, T, None, None, None,
+                         ctypes.byref(n), None)
+    elif kind == "decode":
+        rc = L.moe_forward_decode(ctypes.byref(d), ctypes.byref(layer), None, T, None, y_dt, None,
+                                  None, None, ctypes.byref(n), None)
+    elif kind == "prefill":
+        rc = L.moe_forward_prefill(ctypes.byref(d), ctypes.byref(layer), None, T, None, y_dt, None,
+                                   None, None, None, None, ctypes.byref(n), None)
+    else:
+        raise ValueError(kind)
+    _check(rc, f"workspace_bytes({kind})")
+    return int(n.value)
+
+
+def _ws(ws, kind, d, layer, T, y_dt):
+    if ws is not None:
+        return ws
+    import torch
+
+    n = workspace_bytes(kind, d, layer, T, y_dt)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+
+
+def route(d: MoeDims, layer: MoeLayer, x, topk_ids, topk_w, ws=None, stream=None) -> None:
+    """``moe_route`` on torch tensors (x [T][H], ids [T][K] int32, w [T][K] fp32)."""
+    T = int(x.shape[0])
+    ws = _ws(ws, "route", d, layer, T, MOE_F32)
+    n = c_size_t(ws.numel())
+    rc = lib().moe_route(ctypes.byref(d), ctypes.byref(layer), _ptr(x), T, _ptr(topk_ids),
+                         _ptr(topk_w), _ptr(ws), ctypes.byref(n), _stream(stream))
+    _check(rc, "moe_route")
+
+
+def forward_decode(d: MoeDims, layer: MoeLayer, x, y, y_dt: int, topk_ids=None, topk_w=None,
+                   ws=None, stream=None) -> None:
+    """``moe_forward_decode`` on torch tensors."""
+    T = int(x.shape[0])
+    ws = _ws(ws, "decode", d, layer, T, y_dt)
+    n = c_size_t(ws.numel())
+    rc = lib().moe_forward_decode(ctypes.byref(d), ctypes.byref(layer), _ptr(x), T, _ptr(y), y_dt,
+                                  _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ctypes.byref(n),
+                                  _stream(stream))
+    _check(rc, "moe_forward_decode")
+
+
+def forward_prefill(d: MoeDims, layer: MoeLayer, x, y, y_dt: int, topk_ids=None, topk_w=None,
+                    expert_offsets=None, sorted_routes=None, ws=None, stream=None) -> None:
+    """``moe_forward_prefill`` on torch tensors."""
+    T = int(x.shape[0])
+    ws = _ws(ws, "prefill", d, layer, T, y_dt)
+    n = c_size_t(ws.numel())
+    rc = lib().moe_forward_prefill(ctypes.byref(d), ctypes.byref(layer), _ptr(x), T, _ptr(y), y_dt,
+                                   _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets),
+                                   _ptr(sorted_routes), _ptr(ws), ctypes.byref(n), _stream(stream))
+    _check(rc, "moe_forward_prefill")
+
+
+class DeviceLayer:
+    """Device tables of one layer held as torch tensors, plus the C view.
+
+    Allocation only: the tier build and every computation run in the library.
+    ``router`` is ``(w [E][H] in the act dtype, bias [E] fp32 or None)`` as
+    torch tensors or NumPy arrays (bf16 given as uint16 bit patterns);
+    ``shared`` likewise ``(gate, up, down)`` or None.
+    """
+
+    def __init__(self, d: MoeDims, n_slots, tier_bits, router, shared=None, device="cuda"):
+        import torch
+
+        self.d = d
+        self.n_slots = tuple(int(v) for v in n_slots)
+        self.tier_bits = tuple(int(v) for v in tier_bits)
+        act_t = torch.bfloat16 if d.act == MOE_BF16 else torch.float32
+        self.act_dtype = act_t
+
+        def to_dev(a, dt):
+            if a is None:
+                return None
+            if isinstance(a, np.ndarray):
+                t = torch.from_numpy(np.ascontiguousarray(a))
+                if dt == torch.bfloat16 and t.dtype in (torch.uint16, torch.int16):
+                    t = t.view(torch.int16).view(torch.bfloat16)
+                return t.to(device=device, dtype=dt).contiguous()
+            return a.to(device=device, dtype=dt).contiguous()
+
+        self.w_router = to_dev(router[0], act_t)
+        self.b_router = to_dev(router[1], torch.float32)
+        self.tier_map = torch.zeros(d.n_experts, dtype=torch.int32, device=device)
+        self.codes = [[None] * 3 for _ in range(3)]
+        self.dm = [[None] * 3 for _ in range(3)]
+        for t in range(3):
+            if self.n_slots[t] == 0:
+                continue
+            for m in range(3):
+                nc = tier_table_bytes(d, self.tier_bits[t], self.n_slots[t], m, MOE_CODES)
+                nd = tier_table_bytes(d, self.tier_bits[t], self.n_slots[t], m, MOE_DM)
+                self.codes[t][m] = torch.zeros(nc, dtype=torch.uint8, device=device)
+                self.dm[t][m] = torch.zeros(nd // 4, dtype=torch.int32, device=device)
+        self.shared = None if shared is None else [to_dev(s, act_t) for s in shared]
+
+    def c_struct(self) -> MoeLayer:
+        L = MoeLayer()
+        L.w_router = _ptr(self.w_router)
+        L.b_router = _ptr(self.b_router)
+        L.tier_map = _ptr(self.tier_map)
+        L.n_slots = _i32x3(self.n_slots)
+        L.tier_bits = _i32x3(self.tier_bits)
+        for t in range(3):
+            for m in range(3):
+                L.codes[t][m] = _ptr(self.codes[t][m])
+                L.dm[t][m] = _ptr(self.dm[t][m])
+        if self.shared is not None:
+            for m in range(3):
+                L.w_shared[m] = _ptr(self.shared[m])
+        return L
+
+    def load_experts(self, popularity, source: MoeExpertSource, stream=None):
+        """Rank, quantise/pack and upload the expert tables (moe_build_tiers)."""
+        dst = self.c_struct()
+        return build_tiers(self.d, popularity, self.n_slots, self.tier_bits, source, dst,
+                           dst_on_device=True, stream=stream)
+
+
+def source_f32(gate, up, down):
+    """MoeExpertSource over host fp32 arrays [E][rows][cols] (kept alive by caller)."""
+    s = MoeExpertSource()
+    s.kind = MOE_SRC_F32
+    for m, a in enumerate((gate, up, down)):
+        assert a.dtype == np.float32 and a.flags.c_contiguous
+        s.w[m] = a.ctypes.data
+    return s
+
+
+def source_codes(q, d, m):
+    """MoeExpertSource over host codes / fp16 scale / fp16 min arrays per matrix."""
+    s = MoeExpertSource()
+    s.kind = MOE_SRC_CODES
+    for i in range(3):
+        assert q[i].dtype == np.uint8 and q[i].flags.c_contiguous
+        for a in (d[i], m[i]):
+            assert a.dtype in (np.float16, np.uint16) and a.flags.c_contiguous
+        s.q[i] = q[i].ctypes.data
+        s.d[i] = d[i].ctypes.data
+        s.m[i] = m[i].ctypes.data
+    return s
+
+
+__all__ += ["source_f32", "source_codes"]

@@ -1,0 +1,109 @@
+// Internal declarations shared by the host library and the HIP kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// Tokens handled together by the decode kernels: the M side of one 16x16
+// MFMA tile.
+constexpr int kGroup = 16;
+// Tier index used for the shared expert (dense weights in the act dtype).
+constexpr int kDenseTier = 3;
+
+// One expert of a decode group together with the tokens that route to it.
+struct Item {
+  int32_t expert;          // expert id, -1 for the shared expert
+  int32_t tier;            // 0..2 quantised tier, kDenseTier, or -1 (skip)
+  int32_t slot;            // slot inside the tier table
+  int32_t bits;            // code width of the tier (0 for dense)
+  int32_t route[kGroup];   // row of h for token t of the group, or -1
+  float gw[kGroup];        // mixing weight of token t (0 when not routed)
+};
+
+// Kernel-side view of the expert tables of one layer.
+struct Tables {
+  const uint8_t* codes[3][3];
+  const uint32_t* dm[3][3];
+  int32_t bits[3];
+  int32_t n_slots[3];
+  const void* dense[3];    // shared expert gate / up / down (act dtype)
+};
+
+// ---- launchers (defined in the .hip files; all enqueue on `s`) ----
+
+// keys[t][e] = x[t] . w[e] + b[e] in float64, for t < T (any T).
+void launch_router_keys(int act, const void* x, const void* w, const float* b, double* keys,
+                        int T, int H, int E, hipStream_t s);
+
+// Top-K + softmax weights for T tokens (any T): ids[t][k], w[t][k].
+void launch_topk(const double* keys, int T, int E, int K, int32_t* ids, float* w, hipStream_t s);
+
+// Decode group (T <= kGroup): top-K, weights, then the union of experts as
+// work items (ascending expert id, then the shared expert).
+void launch_topk_items(const double* keys, int T, int E, int K, const int32_t* tier_map,
+                       const int32_t n_slots[3], const int32_t tier_bits[3], int has_shared,
+                       int32_t* ids, float* w, Item* items, int32_t* n_items, hipStream_t s);
+
+// Decode gate/up over the work items: h[route][I] = act(silu(gate) * up).
+void launch_decode_gateup(int act, const Item* items, const int32_t* n_items, int max_items,
+                          const void* x, int T, const Tables& tb, void* h, int H, int I,
+                          hipStream_t s);
+
+// Decode down + combine: y[t][H] = sum over items of gw * (W_d h).
+void launch_decode_down(int act, int y_dt, const Item* items, const int32_t* n_items,
+                        int max_items, const void* h, int T, const Tables& tb, void* y,
+                        int H, int I, hipStream_t s);
+
+// ---- prefill ----
+
+// Stable counting sort of the routes by expert.
+//   chunk_mask: [n_chunks][E] uint64, chunk_base: [n_chunks][E] int32.
+void launch_sort_routes(const int32_t* ids, int T, int K, int E, uint64_t* chunk_mask,
+                        int32_t* chunk_base, int32_t* offsets, int32_t* sorted_routes,
+                        int32_t* route_pos, hipStream_t s);
+
+// Routed gate/up grouped GEMM: for every expert bucket, h[pos][I] for the
+// sorted positions pos of that bucket.
+void launch_prefill_gateup(int act, const int32_t* offsets, const int32_t* sorted_routes,
+                           const int32_t* tier_map, int E, int K, const void* x, const Tables& tb,
+                           void* h, int H, int I, hipStream_t s);
+
+// Shared expert gate/up for all T tokens: h_s[t][I].
+void launch_prefill_shared_gateup(int act, const void* x, int T, const Tables& tb, void* h_s,
+                                  int H, int I, hipStream_t s);
+
+// Shared expert down: y_acc[t][H] = W_sd h_s[t] (plain stores, fp32).
+void launch_prefill_shared_down(int act, const void* h_s, int T, const Tables& tb, float* y_acc,
+                                int H, int I, hipStream_t s);
+
+// Routed down + weighted scatter: y_acc[t] += g * (W_d h[pos]) (fp32 atomics).
+void launch_prefill_down(int act, const int32_t* offsets, const int32_t* sorted_routes,
+                         const int32_t* tier_map, const float* topk_w, int E, int K,
+                         const void* h, const Tables& tb, float* y_acc, int H, int I,
+                         hipStream_t s);
+
+// y_acc (fp32) -> y in the act dtype (bf16), n elements.
+void launch_cast_out(const float* y_acc, void* y, size_t n, hipStream_t s);
+
+// Zero n floats.
+void launch_zero(float* p, size_t n, hipStream_t s);
+
+// ---- host packer (pack.cpp; no HIP calls) ----
+
+// Quantise one block of 32 floats; returns MOE_OK or MOE_EINVAL.
+int quantise_block(const float* x, int bits, uint16_t* d, uint16_t* m, uint8_t* q);
+// Pack 32 codes (each <= 2^bits - 1) into a 4*bits-byte code field.
+void encode_codes(const uint8_t* q, int bits, uint8_t* field);
+// Index of block (slot, row, block column) in a tier table of R x C matrices.
+inline size_t tile_block_index(size_t slot, int r, int j, int R, int C) {
+  size_t tile = (slot * (size_t)(R / 16) + (size_t)(r / 16)) * (size_t)(C / 128) + (size_t)(j / 4);
+  return tile * 64 + (size_t)(16 * (j % 4) + (r % 16));
+}
+
+}  // namespace moe

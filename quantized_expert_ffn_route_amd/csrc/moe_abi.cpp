@@ -1,0 +1,452 @@
+// C ABI of the tiered MoE layer: argument validation, workspace layout, the
+// host tier build (A0) and the launch sequences of route / decode / prefill.
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+#include <numeric>
+#include <thread>
+#include <vector>
+
+#include "internal.hpp"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline size_t act_bytes(int act) { return act == MOE_BF16 ? 2 : 4; }
+
+void mat_shape(const moe_dims* d, int mat, int* rows, int* cols) {
+  if (mat == MOE_DOWN) {
+    *rows = d->hidden;
+    *cols = d->inter;
+  } else {
+    *rows = d->inter;
+    *cols = d->hidden;
+  }
+}
+
+int check_dims(const moe_dims* d) {
+  if (!d) return MOE_EINVAL;
+  if (d->hidden <= 0 || d->inter <= 0 || d->n_experts <= 0 || d->top_k <= 0) return MOE_EINVAL;
+  if (d->n_experts > 65535) return MOE_EINVAL;
+  if (d->top_k > d->n_experts || d->top_k > 64) return MOE_EINVAL;
+  if (d->has_shared != 0 && d->has_shared != 1) return MOE_EINVAL;
+  if (d->act != MOE_F32 && d->act != MOE_BF16) return MOE_EINVAL;
+  if (d->hidden % 128 || d->inter % 128) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_tiers(const moe_dims* d, const int32_t n_slots[3], const int32_t tier_bits[3]) {
+  int64_t sum = 0;
+  for (int t = 0; t < 3; t++) {
+    if (n_slots[t] < 0) return MOE_EINVAL;
+    sum += n_slots[t];
+    if (n_slots[t] > 0 && tier_bits[t] != 2 && tier_bits[t] != 3 && tier_bits[t] != 4)
+      return MOE_EINVAL;
+  }
+  return sum == d->n_experts ? MOE_OK : MOE_EINVAL;
+}
+
+int check_layer(const moe_dims* d, const moe_layer* L) {
+  if (!L) return MOE_EINVAL;
+  if (!L->w_router || !aligned(L->w_router, 16) || !L->tier_map) return MOE_EINVAL;
+  if (L->b_router && !aligned(L->b_router, 4)) return MOE_EINVAL;
+  int rc = check_tiers(d, L->n_slots, L->tier_bits);
+  if (rc) return rc;
+  for (int t = 0; t < 3; t++) {
+    if (L->n_slots[t] == 0) continue;
+    for (int m = 0; m < 3; m++)
+      if (!L->codes[t][m] || !L->dm[t][m] || !aligned(L->codes[t][m], 16) || !aligned(L->dm[t][m], 16))
+        return MOE_EINVAL;
+  }
+  if (d->has_shared)
+    for (int m = 0; m < 3; m++)
+      if (!L->w_shared[m] || !aligned(L->w_shared[m], 16)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+Tables make_tables(const moe_dims* d, const moe_layer* L) {
+  Tables tb;
+  std::memset(&tb, 0, sizeof(tb));
+  for (int t = 0; t < 3; t++) {
+    tb.bits[t] = L->tier_bits[t];
+    tb.n_slots[t] = L->n_slots[t];
+    for (int m = 0; m < 3; m++) {
+      tb.codes[t][m] = L->codes[t][m];
+      tb.dm[t][m] = L->dm[t][m];
+    }
+  }
+  for (int m = 0; m < 3; m++) tb.dense[m] = d->has_shared ? L->w_shared[m] : nullptr;
+  return tb;
+}
+
+// Workspace carving: every region 256-byte aligned.
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off += align_up(bytes);
+    return o;
+  }
+};
+
+struct RouteWs {
+  size_t keys, total;
+};
+RouteWs route_ws(const moe_dims* d, int64_t T) {
+  Carve c;
+  RouteWs w;
+  w.keys = c.take((size_t)T * d->n_experts * sizeof(double));
+  w.total = c.off;
+  return w;
+}
+
+struct DecodeWs {
+  size_t keys, ids, w, items, n_items, h, total;
+  int max_items;
+};
+DecodeWs decode_ws(const moe_dims* d) {
+  Carve c;
+  DecodeWs w;
+  const int G = kGroup, K = d->top_k;
+  w.max_items = G * K + 1;
+  w.keys = c.take((size_t)G * d->n_experts * sizeof(double));
+  w.ids = c.take((size_t)G * K * sizeof(int32_t));
+  w.w = c.take((size_t)G * K * sizeof(float));
+  w.items = c.take((size_t)w.max_items * sizeof(Item));
+  w.n_items = c.take(sizeof(int32_t));
+  w.h = c.take((size_t)(G * K + G) * d->inter * act_bytes(d->act));
+  w.total = c.off;
+  return w;
+}
+
+struct PrefillWs {
+  size_t keys, ids, w, chunk_mask, chunk_base, offsets, sorted, route_pos, h, h_s, y_acc, total;
+};
+PrefillWs prefill_ws(const moe_dims* d, int64_t T, int y_dt) {
+  Carve c;
+  PrefillWs w;
+  const int64_t K = d->top_k, E = d->n_experts, n_chunks = (T + 63) / 64;
+  w.keys = c.take((size_t)T * E * sizeof(double));
+  w.ids = c.take((size_t)T * K * sizeof(int32_t));
+  w.w = c.take((size_t)T * K * sizeof(float));
+  w.chunk_mask = c.take((size_t)n_chunks * E * sizeof(uint64_t));
+  w.chunk_base = c.take((size_t)n_chunks * E * sizeof(int32_t));
+  w.offsets = c.take((size_t)(E + 1) * sizeof(int32_t));
+  w.sorted = c.take((size_t)T * K * sizeof(int32_t));
+  w.route_pos = c.take((size_t)T * K * sizeof(int32_t));
+  w.h = c.take((size_t)T * K * d->inter * act_bytes(d->act));
+  w.h_s = c.take(d->has_shared ? (size_t)T * d->inter * act_bytes(d->act) : 0);
+  w.y_acc = c.take(y_dt == MOE_F32 ? 0 : (size_t)T * d->hidden * sizeof(float));
+  w.total = c.off;
+  return w;
+}
+
+// Common checks of the forward / route calls.  Returns MOE_OK and sets
+// *size_only when the caller asked for the workspace size.
+int check_ws(void* ws, size_t* ws_bytes, size_t need, bool* size_only) {
+  if (!ws_bytes) return MOE_EINVAL;
+  if (!ws) {
+    *ws_bytes = need;
+    *size_only = true;
+    return MOE_OK;
+  }
+  *size_only = false;
+  if (!aligned(ws, kAlign)) return MOE_EINVAL;
+  if (*ws_bytes < need) return MOE_ENOSPC;
+  return MOE_OK;
+}
+
+inline int hip_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: unsupported shape or dtype";
+    case MOE_ENOSPC: return "MOE_ENOSPC: workspace too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP runtime error";
+    default: return "unknown moe_status";
+  }
+}
+
+size_t moe_tier_table_bytes(const moe_dims* dims, int32_t bits, int32_t n_slots, int32_t mat,
+                            int32_t which) {
+  if (check_dims(dims) != MOE_OK || n_slots < 0 || mat < 0 || mat > 2) return 0;
+  if (bits != 2 && bits != 3 && bits != 4) return 0;
+  int rows, cols;
+  mat_shape(dims, mat, &rows, &cols);
+  const size_t blocks = (size_t)n_slots * rows * (cols / 32);
+  if (which == MOE_CODES) return blocks * 4 * bits;
+  if (which == MOE_DM) return blocks * 4;
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// A0: tier build.
+// ---------------------------------------------------------------------------
+
+int moe_build_tiers(const moe_dims* dims, const uint64_t* popularity, const int32_t n_slots[3],
+                    const int32_t tier_bits[3], const moe_expert_source* src,
+                    int32_t* tier_map_out, int32_t* slot_expert_out, moe_layer* dst,
+                    int32_t dst_on_device, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!popularity || !n_slots || !tier_bits || !tier_map_out) return MOE_EINVAL;
+  rc = check_tiers(dims, n_slots, tier_bits);
+  if (rc) return rc;
+  const int E = dims->n_experts;
+  // rank: popularity descending, lower id first on equal counts
+  std::vector<int32_t> order(E);
+  std::iota(order.begin(), order.end(), 0);
+  std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    return popularity[a] != popularity[b] ? popularity[a] > popularity[b] : a < b;
+  });
+  const int start[3] = {0, n_slots[0], n_slots[0] + n_slots[1]};
+  std::vector<int32_t> tmap(E);
+  for (int rank = 0; rank < E; rank++) {
+    const int tier = rank < start[1] ? 0 : (rank < start[2] ? 1 : 2);
+    tmap[order[rank]] = (tier << 16) | (rank - start[tier]);
+  }
+  if (!src || !dst) {
+    std::memcpy(tier_map_out, tmap.data(), E * sizeof(int32_t));
+    if (slot_expert_out) std::memcpy(slot_expert_out, order.data(), E * sizeof(int32_t));
+    return MOE_OK;
+  }
+  if (src->kind != MOE_SRC_F32 && src->kind != MOE_SRC_CODES) return MOE_EINVAL;
+  for (int m = 0; m < 3; m++) {
+    if (src->kind == MOE_SRC_F32 && !src->w[m]) return MOE_EINVAL;
+    if (src->kind == MOE_SRC_CODES && (!src->q[m] || !src->d[m] || !src->m[m])) return MOE_EINVAL;
+  }
+  for (int t = 0; t < 3; t++)
+    if (n_slots[t] > 0)
+      for (int m = 0; m < 3; m++)
+        if (!dst->codes[t][m] || !dst->dm[t][m]) return MOE_EINVAL;
+  if (dst_on_device && !dst->tier_map) return MOE_EINVAL;
+
+  std::atomic<int> status{MOE_OK};
+  // pack one (tier, matrix, slot) expert matrix into `codes`/`dm`
+  auto pack_one = [&](int t, int m, int slot, uint8_t* codes, uint32_t* dm) {
+    const int bits = tier_bits[t], L = (1 << bits) - 1;
+    const int e = order[start[t] + slot];
+    int R, C;
+    mat_shape(dims, m, &R, &C);
+    const int nb = C / 32;
+    uint8_t q[32], field[16];
+    for (int r = 0; r < R; r++) {
+      for (int j = 0; j < nb; j++) {
+        uint16_t db, mb;
+        const size_t blk = ((size_t)e * R + r) * nb + j;
+        if (src->kind == MOE_SRC_F32) {
+          if (quantise_block(src->w[m] + blk * 32, bits, &db, &mb, q) != MOE_OK) {
+            status = MOE_EINVAL;
+            return;
+          }
+        } else {
+          const uint8_t* qs = src->q[m] + blk * 32;
+          for (int i = 0; i < 32; i++) {
+            if (qs[i] > L) {
+              status = MOE_EINVAL;
+              return;
+            }
+            q[i] = qs[i];
+          }
+          db = src->d[m][blk];
+          mb = src->m[m][blk];
+          if ((db & 0x7C00u) == 0x7C00u || (mb & 0x7C00u) == 0x7C00u) {
+            status = MOE_EINVAL;
+            return;
+          }
+        }
+        encode_codes(q, bits, field);
+        const size_t idx = tile_block_index(slot, r, j, R, C);
+        std::memcpy(codes + idx * 4 * bits, field, 4 * bits);
+        dm[idx] = (uint32_t)db | ((uint32_t)mb << 16);
+      }
+    }
+  };
+
+  // host destination buffers (staging when the tables live on the device)
+  std::vector<std::vector<uint8_t>> stage_codes(9), stage_dm(9);
+  uint8_t* hc[3][3] = {};
+  uint32_t* hd[3][3] = {};
+  for (int t = 0; t < 3; t++) {
+    if (n_slots[t] == 0) continue;
+    for (int m = 0; m < 3; m++) {
+      const size_t cb = moe_tier_table_bytes(dims, tier_bits[t], n_slots[t], m, MOE_CODES);
+      const size_t db = moe_tier_table_bytes(dims, tier_bits[t], n_slots[t], m, MOE_DM);
+      if (dst_on_device) {
+        stage_codes[3 * t + m].assign(cb, 0);
+        stage_dm[3 * t + m].assign(db, 0);
+        hc[t][m] = stage_codes[3 * t + m].data();
+        hd[t][m] = reinterpret_cast<uint32_t*>(stage_dm[3 * t + m].data());
+      } else {
+        hc[t][m] = dst->codes[t][m];
+        hd[t][m] = dst->dm[t][m];
+      }
+    }
+  }
+  struct Job { int t, m, slot; };
+  std::vector<Job> jobs;
+  for (int t = 0; t < 3; t++)
+    for (int m = 0; m < 3; m++)
+      for (int s = 0; s < n_slots[t]; s++) jobs.push_back({t, m, s});
+  std::atomic<size_t> next{0};
+  const unsigned nthreads =
+      std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  std::vector<std::thread> pool;
+  for (unsigned i = 0; i < nthreads; i++)
+    pool.emplace_back([&] {
+      for (size_t j; (j = next++) < jobs.size() && status == MOE_OK;)
+        pack_one(jobs[j].t, jobs[j].m, jobs[j].slot, hc[jobs[j].t][jobs[j].m], hd[jobs[j].t][jobs[j].m]);
+    });
+  for (auto& th : pool) th.join();
+  if (status != MOE_OK) return status;
+
+  if (dst_on_device) {
+    for (int t = 0; t < 3; t++) {
+      if (n_slots[t] == 0) continue;
+      for (int m = 0; m < 3; m++) {
+        if (hipMemcpyAsync(dst->codes[t][m], hc[t][m], stage_codes[3 * t + m].size(),
+                           hipMemcpyHostToDevice, stream) != hipSuccess ||
+            hipMemcpyAsync(dst->dm[t][m], hd[t][m], stage_dm[3 * t + m].size(),
+                           hipMemcpyHostToDevice, stream) != hipSuccess)
+          return MOE_EHIP;
+      }
+    }
+    if (hipMemcpyAsync(dst->tier_map, tmap.data(), E * sizeof(int32_t), hipMemcpyHostToDevice,
+                       stream) != hipSuccess)
+      return MOE_EHIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return MOE_EHIP;
+  } else if (dst->tier_map) {
+    std::memcpy(dst->tier_map, tmap.data(), E * sizeof(int32_t));
+  }
+  std::memcpy(tier_map_out, tmap.data(), E * sizeof(int32_t));
+  if (slot_expert_out) std::memcpy(slot_expert_out, order.data(), E * sizeof(int32_t));
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// A1-A2: route.
+// ---------------------------------------------------------------------------
+
+int moe_route(const moe_dims* dims, const moe_layer* layer, const void* x, int32_t T,
+              int32_t* topk_ids, float* topk_w, void* ws, size_t* ws_bytes, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_layer(dims, layer))) return rc;
+  if (T < 0 || (int64_t)T * dims->top_k > INT32_MAX) return MOE_EINVAL;
+  const RouteWs w = route_ws(dims, T);
+  bool size_only;
+  if ((rc = check_ws(ws, ws_bytes, w.total, &size_only)) || size_only) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16) || !topk_ids || !topk_w) return MOE_EINVAL;
+  char* base = static_cast<char*>(ws);
+  double* keys = reinterpret_cast<double*>(base + w.keys);
+  launch_router_keys(dims->act, x, layer->w_router, layer->b_router, keys, T, dims->hidden,
+                     dims->n_experts, stream);
+  launch_topk(keys, T, dims->n_experts, dims->top_k, topk_ids, topk_w, stream);
+  return hip_status();
+}
+
+// ---------------------------------------------------------------------------
+// Decode: groups of up to 16 tokens, four launches per group.
+// ---------------------------------------------------------------------------
+
+int moe_forward_decode(const moe_dims* dims, const moe_layer* layer, const void* x, int32_t T,
+                       void* y, int32_t y_dt, int32_t* topk_ids, float* topk_w, void* ws,
+                       size_t* ws_bytes, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_layer(dims, layer))) return rc;
+  if (T < 0 || (int64_t)T * dims->top_k > INT32_MAX) return MOE_EINVAL;
+  if (y_dt != MOE_F32 && y_dt != dims->act) return MOE_EINVAL;
+  const DecodeWs w = decode_ws(dims);
+  bool size_only;
+  if ((rc = check_ws(ws, ws_bytes, w.total, &size_only)) || size_only) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16) || !y || !aligned(y, 16)) return MOE_EINVAL;
+  char* base = static_cast<char*>(ws);
+  const int H = dims->hidden, K = dims->top_k, E = dims->n_experts;
+  const Tables tb = make_tables(dims, layer);
+  const size_t xb = act_bytes(dims->act), yb = y_dt == MOE_BF16 ? 2 : 4;
+  for (int t0 = 0; t0 < T; t0 += kGroup) {
+    const int nt = std::min(kGroup, T - t0);
+    const char* xg = static_cast<const char*>(x) + (size_t)t0 * H * xb;
+    char* yg = static_cast<char*>(y) + (size_t)t0 * H * yb;
+    double* keys = reinterpret_cast<double*>(base + w.keys);
+    int32_t* ids = topk_ids ? topk_ids + (size_t)t0 * K : reinterpret_cast<int32_t*>(base + w.ids);
+    float* wts = topk_w ? topk_w + (size_t)t0 * K : reinterpret_cast<float*>(base + w.w);
+    Item* items = reinterpret_cast<Item*>(base + w.items);
+    int32_t* n_items = reinterpret_cast<int32_t*>(base + w.n_items);
+    void* h = base + w.h;
+    launch_router_keys(dims->act, xg, layer->w_router, layer->b_router, keys, nt, H, E, stream);
+    launch_topk_items(keys, nt, E, K, layer->tier_map, layer->n_slots, layer->tier_bits,
+                      dims->has_shared, ids, wts, items, n_items, stream);
+    launch_decode_gateup(dims->act, items, n_items, nt * K + dims->has_shared, xg, nt, tb, h, H,
+                         dims->inter, stream);
+    launch_decode_down(dims->act, y_dt, items, n_items, w.max_items, h, nt, tb, yg, H,
+                       dims->inter, stream);
+  }
+  return hip_status();
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: route, counting sort, grouped GEMMs, weighted scatter-combine.
+// ---------------------------------------------------------------------------
+
+int moe_forward_prefill(const moe_dims* dims, const moe_layer* layer, const void* x, int32_t T,
+                        void* y, int32_t y_dt, int32_t* topk_ids, float* topk_w,
+                        int32_t* expert_offsets, int32_t* sorted_routes, void* ws,
+                        size_t* ws_bytes, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_layer(dims, layer))) return rc;
+  if (dims->n_experts > 4096) return MOE_EUNSUPPORTED;
+  if (T < 0 || (int64_t)T * dims->top_k > INT32_MAX) return MOE_EINVAL;
+  if (y_dt != MOE_F32 && y_dt != dims->act) return MOE_EINVAL;
+  const PrefillWs w = prefill_ws(dims, T, y_dt);
+  bool size_only;
+  if ((rc = check_ws(ws, ws_bytes, w.total, &size_only)) || size_only) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16) || !y || !aligned(y, 16)) return MOE_EINVAL;
+  char* base = static_cast<char*>(ws);
+  const int H = dims->hidden, I = dims->inter, K = dims->top_k, E = dims->n_experts;
+  const Tables tb = make_tables(dims, layer);
+  double* keys = reinterpret_cast<double*>(base + w.keys);
+  int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(base + w.ids);
+  float* wts = topk_w ? topk_w : reinterpret_cast<float*>(base + w.w);
+  int32_t* offsets = expert_offsets ? expert_offsets : reinterpret_cast<int32_t*>(base + w.offsets);
+  int32_t* sorted = sorted_routes ? sorted_routes : reinterpret_cast<int32_t*>(base + w.sorted);
+  int32_t* route_pos = reinterpret_cast<int32_t*>(base + w.route_pos);
+  void* h = base + w.h;
+  void* h_s = base + w.h_s;
+  float* y_acc = y_dt == MOE_F32 ? static_cast<float*>(y) : reinterpret_cast<float*>(base + w.y_acc);
+
+  launch_router_keys(dims->act, x, layer->w_router, layer->b_router, keys, T, H, E, stream);
+  launch_topk(keys, T, E, K, ids, wts, stream);
+  launch_sort_routes(ids, T, K, E, reinterpret_cast<uint64_t*>(base + w.chunk_mask),
+                     reinterpret_cast<int32_t*>(base + w.chunk_base), offsets, sorted, route_pos,
+                     stream);
+  launch_prefill_gateup(dims->act, offsets, sorted, layer->tier_map, E, K, x, tb, h, H, I, stream);
+  if (dims->has_shared) {
+    launch_prefill_shared_gateup(dims->act, x, T, tb, h_s, H, I, stream);
+    launch_prefill_shared_down(dims->act, h_s, T, tb, y_acc, H, I, stream);
+  } else {
+    launch_zero(y_acc, (size_t)T * H, stream);
+  }
+  launch_prefill_down(dims->act, offsets, sorted, layer->tier_map, wts, E, K, h, tb, y_acc, H, I,
+                      stream);
+  if (y_dt != MOE_F32) launch_cast_out(y_acc, y, (size_t)T * H, stream);
+  return hip_status();
+}
+
+}  // extern "C"

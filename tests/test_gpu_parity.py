@@ -1,0 +1,278 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: expert ids, tier maps and the counting sort bit-exact; mixing weights
+within 1e-6; layer outputs within max-abs 2e-2 and relative L2 1e-3 (bf16
+activations), and relative L2 1e-5 for fp32 activations, where only fp32
+accumulation order separates the two sides.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+
+from layers import act_f64, make_layer, rel_l2
+
+torch = pytest.importorskip("torch")
+M = pytest.importorskip("quantized_expert_ffn_route_amd")
+
+pytestmark = pytest.mark.gpu
+
+MID = synth.LayerSpec(hidden=512, inter=256, n_experts=32, top_k=4, has_shared=True, act="bf16",
+                      n_slots=(8, 16, 8))
+
+
+def dev(a, act):
+    if act == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def check_y(y_gpu, y_ref, act, what=""):
+    y = y_gpu.float().cpu().numpy().astype(np.float64) if hasattr(y_gpu, "cpu") else y_gpu
+    err = np.max(np.abs(y - y_ref))
+    rl = rel_l2(y, y_ref)
+    print(f"  {what}: max-abs {err:.3e}  rel-L2 {rl:.3e}", flush=True)
+    assert np.all(np.isfinite(y))
+    assert err <= 2e-2, (what, err)
+    assert rl <= (1e-5 if act == "f32" else 1e-3), (what, rl)
+
+
+def run_route(tl, x):
+    spec = tl.spec
+    T = x.shape[0]
+    ids = torch.empty((T, spec.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, spec.top_k), dtype=torch.float32, device="cuda")
+    M.route(tl.dl.d, tl.dl.c_struct(), dev(x, spec.act), ids, w)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+def run_decode(tl, x, y_dt=None):
+    spec = tl.spec
+    T = x.shape[0]
+    y_dt = M.MOE_F32 if y_dt is None else y_dt
+    y = torch.empty((T, spec.hidden), dtype=torch.float32 if y_dt == M.MOE_F32 else torch.bfloat16,
+                    device="cuda")
+    ids = torch.empty((T, spec.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, spec.top_k), dtype=torch.float32, device="cuda")
+    M.forward_decode(tl.dl.d, tl.dl.c_struct(), dev(x, spec.act), y, y_dt, ids, w)
+    torch.cuda.synchronize()
+    return y, ids.cpu().numpy(), w.cpu().numpy()
+
+
+def run_prefill(tl, x, y_dt=None):
+    spec = tl.spec
+    T = x.shape[0]
+    y_dt = M.MOE_F32 if y_dt is None else y_dt
+    y = torch.empty((T, spec.hidden), dtype=torch.float32 if y_dt == M.MOE_F32 else torch.bfloat16,
+                    device="cuda")
+    ids = torch.empty((T, spec.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, spec.top_k), dtype=torch.float32, device="cuda")
+    off = torch.empty(spec.n_experts + 1, dtype=torch.int32, device="cuda")
+    srt = torch.empty(T * spec.top_k, dtype=torch.int32, device="cuda")
+    M.forward_prefill(tl.dl.d, tl.dl.c_struct(), dev(x, spec.act), y, y_dt, ids, w, off, srt)
+    torch.cuda.synchronize()
+    return y, ids.cpu().numpy(), w.cpu().numpy(), off.cpu().numpy(), srt.cpu().numpy()
+
+
+# ------------------------------------------------------------------ layers
+
+@pytest.fixture(scope="module")
+def tiny():
+    print("\n[fixture] tiny layer", flush=True)
+    return make_layer(synth.TINY, seed=0)
+
+
+@pytest.fixture(scope="module")
+def mid():
+    print("\n[fixture] mid layer", flush=True)
+    return make_layer(MID, seed=5)
+
+
+@pytest.fixture(scope="module")
+def full():
+    print("\n[fixture] full-size layer (random blocks)", flush=True)
+    return make_layer(synth.FULL, seed=0, source="codes", n_calib=4096)
+
+
+# ------------------------------------------------------------------ routing
+
+def test_route_tiny_exact(tiny):
+    x = synth.tokens(tiny.spec, 8, 10)
+    ids, w = run_route(tiny, x)
+    keys, oids, g = O.route(act_f64(x, "f32"), tiny.ol.w_router, tiny.ol.bias, tiny.spec.top_k, exact=True)
+    np.testing.assert_array_equal(ids, oids)
+    assert np.max(np.abs(w - g)) <= 1e-6
+
+
+def test_route_ties_take_lower_id(mid):
+    # duplicate router rows: equal keys must resolve to the lower expert id
+    def dup(w_r, b):
+        w_r = w_r.copy()
+        b = b.copy()
+        for src, dst in ((3, 17), (3, 29), (8, 9)):
+            w_r[dst] = w_r[src]
+            b[dst] = b[src]
+        b[[3, 17, 29]] += 3.0        # make the tied experts the winners
+        return w_r, b
+    tl = make_layer(MID, seed=6, router_override=dup)
+    x = synth.tokens(MID, 40, 11)
+    ids, w = run_route(tl, x)
+    _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, MID.top_k, exact=True)
+    np.testing.assert_array_equal(ids, oids)
+    assert np.all(ids[:, :3] == [3, 17, 29])
+    assert np.max(np.abs(w - g)) <= 1e-6
+
+
+def test_route_full_size_exact(full):
+    x = synth.tokens(full.spec, 512, 12)
+    ids, w = run_route(full, x)
+    _, oids, g = O.route(act_f64(x, "bf16"), full.ol.w_router, full.ol.bias, full.spec.top_k)
+    np.testing.assert_array_equal(ids, oids)
+    assert np.max(np.abs(w - g)) <= 1e-6
+
+
+def test_tier_map_matches_oracle(full, mid, tiny):
+    for tl in (full, mid, tiny):
+        want, _ = O.build_tiers(tl.popularity, tl.spec.n_slots)
+        np.testing.assert_array_equal(tl.tier_map, want)
+        np.testing.assert_array_equal(tl.dl.tier_map.cpu().numpy(), want)
+
+
+# ------------------------------------------------------------------ decode
+
+def test_decode_tiny(tiny):
+    x = synth.tokens(tiny.spec, 8, 13)
+    y, ids, w = run_decode(tiny, x)
+    ref = O.moe_layer(act_f64(x, "f32"), tiny.ol)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    check_y(y, ref["y"], "f32", "decode tiny T=8")
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 21, 40])
+def test_decode_mid_ragged(mid, T):
+    x = synth.tokens(mid.spec, T, 14 + T)
+    y, ids, w = run_decode(mid, x)
+    ref = O.moe_layer(act_f64(x, "bf16"), mid.ol)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    assert np.max(np.abs(w - ref["g"])) <= 1e-6
+    check_y(y, ref["y"], "bf16", f"decode mid T={T}")
+    # bf16 output is the RNE rounding of the same fp32 sums
+    yb, _, _ = run_decode(mid, x, M.MOE_BF16)
+    want = O.bf16_round(y.cpu().numpy())
+    np.testing.assert_array_equal(yb.float().cpu().numpy(), want)
+
+
+def test_decode_full_single_tokens(full):
+    xs = synth.tokens(full.spec, 4, 15)
+    ref = O.moe_layer(act_f64(xs, "bf16"), full.ol)
+    for t in range(4):
+        y, ids, w = run_decode(full, xs[t:t + 1])
+        np.testing.assert_array_equal(ids, ref["ids"][t:t + 1])
+        check_y(y, ref["y"][t:t + 1], "bf16", f"decode full T=1 token {t}")
+
+
+@pytest.mark.parametrize("T", [4, 8, 16])
+def test_verify_full_correlated(full, T):
+    x = synth.correlated_tokens(full.spec, T, 16 + T)
+    y, ids, w = run_decode(full, x)
+    ref = O.moe_layer(act_f64(x, "bf16"), full.ol)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    print(f"  union of experts at T={T}: {len(np.unique(ids))}", flush=True)
+    check_y(y, ref["y"], "bf16", f"verify full T={T}")
+
+
+def test_decode_deterministic(mid):
+    x = synth.tokens(mid.spec, 16, 17)
+    y1, _, _ = run_decode(mid, x)
+    y2, _, _ = run_decode(mid, x)
+    assert torch.equal(y1, y2)
+
+
+def test_decode_zero_tokens(mid):
+    y = torch.empty((0, mid.spec.hidden), dtype=torch.float32, device="cuda")
+    x = torch.empty((0, mid.spec.hidden), dtype=torch.bfloat16, device="cuda")
+    M.forward_decode(mid.dl.d, mid.dl.c_struct(), x, y, M.MOE_F32)
+    M.forward_prefill(mid.dl.d, mid.dl.c_struct(), x, y, M.MOE_F32)
+    torch.cuda.synchronize()
+
+
+def test_low_bit_codes_in_wider_tables_identical():
+    # codes drawn at 2 bits, stored once in 2-bit tables and once in 4-bit
+    # tables with the same scales and mins: outputs must be bit-identical
+    spec2 = MID.with_(tier_bits=(2, 2, 2))
+    spec4 = MID.with_(tier_bits=(4, 4, 4))
+    a = make_layer(spec2, seed=7, source="codes")
+    import layers
+    per = [synth.expert_codes(spec2, 2, 7 + 2, e) for e in range(MID.n_experts)]
+    names = ("gate", "up", "down")
+    q = [np.ascontiguousarray(np.stack([per[e][n][2] for e in range(MID.n_experts)])) for n in names]
+    dd = [np.ascontiguousarray(np.stack([per[e][n][0] for e in range(MID.n_experts)])) for n in names]
+    mm = [np.ascontiguousarray(np.stack([per[e][n][1] for e in range(MID.n_experts)])) for n in names]
+    w_router, bias = synth.router(MID, 7)
+    b = M.DeviceLayer(a.dl.d, spec4.n_slots, spec4.tier_bits, (w_router, bias),
+                      synth.shared_expert(MID, 7 + 3))
+    b.load_experts(a.popularity, M.source_codes(q, dd, mm))
+    x = synth.tokens(MID, 19, 18)
+    ya, _, _ = run_decode(a, x)
+    tb = layers.TestLayer(spec=spec4, ol=None, dl=b, tier_map=None, popularity=None)
+    yb, _, _ = run_decode(tb, x)
+    assert torch.equal(ya, yb)
+    pa = run_prefill(a, x)[0]
+    pb = run_prefill(tb, x)[0]
+    check_y(pb, pa.cpu().numpy().astype(np.float64), "bf16", "prefill 2-bit vs 4-bit tables")
+
+
+# ------------------------------------------------------------------ prefill
+
+def test_prefill_tiny(tiny):
+    x = synth.tokens(tiny.spec, 300, 19)
+    y, ids, w, off, srt = run_prefill(tiny, x)
+    ref = O.moe_layer(act_f64(x, "f32"), tiny.ol)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    o_off, o_srt = O.sort_routes(ids, tiny.spec.n_experts)
+    np.testing.assert_array_equal(off, o_off)
+    np.testing.assert_array_equal(srt, o_srt)
+    check_y(y, ref["y"], "f32", "prefill tiny T=300")
+
+
+@pytest.mark.parametrize("T", [1, 63, 333])
+def test_prefill_mid(mid, T):
+    x = synth.tokens(mid.spec, T, 20 + T)
+    y, ids, w, off, srt = run_prefill(mid, x)
+    ref = O.moe_layer(act_f64(x, "bf16"), mid.ol)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    o_off, o_srt = O.sort_routes(ids, mid.spec.n_experts)
+    np.testing.assert_array_equal(off, o_off)
+    np.testing.assert_array_equal(srt, o_srt)
+    check_y(y, ref["y"], "bf16", f"prefill mid T={T}")
+    yb = run_prefill(mid, x, M.MOE_BF16)[0]
+    check_y(yb, O.output_cast(ref["y"], "bf16"), "bf16", f"prefill mid T={T} bf16 out")
+
+
+def test_prefill_full_4096_sampled(full):
+    T = 4096
+    x = synth.tokens(full.spec, T, 21)
+    y, ids, w, off, srt = run_prefill(full, x, M.MOE_BF16)
+    xs = act_f64(x, "bf16")
+    keys, oids, g = O.route(xs, full.ol.w_router, full.ol.bias, full.spec.top_k)
+    np.testing.assert_array_equal(ids, oids)
+    assert np.max(np.abs(w - g)) <= 1e-6
+    o_off, o_srt = O.sort_routes(ids, full.spec.n_experts)
+    np.testing.assert_array_equal(off, o_off)
+    np.testing.assert_array_equal(srt, o_srt)
+    sample = [0, 1, 777, 2048, 3000, 4095]
+    ref = O.moe_layer(xs, full.ol, tokens=sample, routing=(keys, oids, g))
+    check_y(y[sample], O.output_cast(ref["y"], "bf16"), "bf16", "prefill full T=4096 (sampled rows)")
+
+
+def test_decode_equals_prefill(mid, full):
+    for tl, T in ((mid, 16), (full, 8)):
+        x = synth.tokens(tl.spec, T, 22)
+        yd, idd, wd = run_decode(tl, x)
+        yp, idp, wp, _, _ = run_prefill(tl, x)
+        np.testing.assert_array_equal(idd, idp)
+        np.testing.assert_array_equal(wd, wp)
+        check_y(yp, yd.cpu().numpy().astype(np.float64), "bf16", "prefill vs decode")

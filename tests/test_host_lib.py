@@ -1,0 +1,260 @@
+"""CPU tests of the C-ABI library: symbols, validation, workspace queries and
+the host tier build, bit-exact against the oracle.  No GPU is needed: these
+paths make no HIP call (moe_build_tiers with host destinations, argument
+validation, ws == NULL size queries)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+import quantized_expert_ffn_route_amd as M
+
+from conftest import ROOT
+
+pytestmark = pytest.mark.skipif(not os.path.exists(M.library_path()),
+                                reason="libmoe.so not built (run __graft_entry__.build())")
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_header_symbol():
+    names = _header_functions()
+    assert {"moe_route", "moe_build_tiers", "moe_forward_decode", "moe_forward_prefill"} <= set(names)
+    lib = ctypes.CDLL(M.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in (M.MOE_OK, M.MOE_EINVAL, M.MOE_EUNSUPPORTED, M.MOE_ENOSPC, M.MOE_EHIP):
+        assert M.status_string(s).startswith("MOE_")
+
+
+def test_tier_table_bytes_closed_form():
+    d = M.dims(2048, 512, 512, 10, True, "bf16")
+    # one expert's three matrices: 3 * 2048 * 512 weights = 98304 blocks
+    per_expert = {b: sum(M.tier_table_bytes(d, b, 1, m, w) for m in range(3) for w in range(2))
+                  for b in (4, 3, 2)}
+    assert per_expert == {4: 1966080, 3: 1572864, 2: 1179648}
+    full = sum(M.tier_table_bytes(d, b, n, m, w) for b, n in ((4, 128), (3, 256), (2, 128))
+               for m in range(3) for w in range(2))
+    assert full == 768 * 2 ** 20
+    assert M.tier_table_bytes(d, 5, 1, 0, 0) == 0
+
+
+def _fake_layer(d, n_slots=(1, 0, 0), tier_bits=(4, 3, 2)):
+    """A layer struct whose pointers are non-null and aligned (never dereferenced)."""
+    L = M.MoeLayer()
+    fake = 1 << 20
+    L.w_router = fake
+    L.tier_map = fake
+    L.n_slots = (ctypes.c_int32 * 3)(*n_slots)
+    L.tier_bits = (ctypes.c_int32 * 3)(*tier_bits)
+    for t in range(3):
+        for m in range(3):
+            L.codes[t][m] = fake
+            L.dm[t][m] = fake
+    for m in range(3):
+        L.w_shared[m] = fake
+    return L
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_validation_errors_without_gpu():
+    lib = M.lib()
+    n = ctypes.c_size_t(0)
+
+    def route(d, L, T=4):
+        return lib.moe_route(ctypes.byref(d), ctypes.byref(L), None, T, None, None, None,
+                             ctypes.byref(n), None)
+
+    ok = M.dims(256, 128, 64, 4, False, "f32")
+    assert route(ok, _fake_layer(ok, (64, 0, 0))) == M.MOE_OK and n.value > 0
+    # H not a multiple of 128 / K > E / K > 64 / E > 65535 / bad act
+    assert route(M.dims(96, 128, 64, 4, False, "f32"), _fake_layer(ok, (64, 0, 0))) == M.MOE_EUNSUPPORTED
+    assert route(M.dims(256, 128, 4, 5, False, "f32"), _fake_layer(ok, (4, 0, 0))) == M.MOE_EINVAL
+    assert route(M.dims(256, 128, 128, 65, False, "f32"), _fake_layer(ok, (128, 0, 0))) == M.MOE_EINVAL
+    assert route(M.dims(256, 128, 70000, 4, False, "f32"), _fake_layer(ok, (70000, 0, 0))) == M.MOE_EINVAL
+    bad_act = M.dims(256, 128, 64, 4, False, "f32")
+    bad_act.act = 7
+    assert route(bad_act, _fake_layer(ok, (64, 0, 0))) == M.MOE_EINVAL
+    # tier counts must sum to E, widths must be 2..4
+    assert route(ok, _fake_layer(ok, (32, 0, 0))) == M.MOE_EINVAL
+    assert route(ok, _fake_layer(ok, (32, 32, 0), (4, 5, 2))) == M.MOE_EINVAL
+    # null / misaligned table pointers
+    L = _fake_layer(ok, (64, 0, 0))
+    L.codes[0][1] = None
+    assert route(ok, L) == M.MOE_EINVAL
+    L = _fake_layer(ok, (64, 0, 0))
+    L.dm[0][2] = (1 << 20) + 4
+    assert route(ok, L) == M.MOE_EINVAL
+    # shared expert required when has_shared
+    sh = M.dims(256, 128, 64, 4, True, "f32")
+    L = _fake_layer(sh, (64, 0, 0))
+    L.w_shared[1] = None
+    assert route(sh, L) == M.MOE_EINVAL
+    # negative T; T == 0 still answers the size query
+    assert route(ok, _fake_layer(ok, (64, 0, 0)), T=-1) == M.MOE_EINVAL
+    assert route(ok, _fake_layer(ok, (64, 0, 0)), T=0) == M.MOE_OK
+
+
+def test_forward_argument_checks_without_gpu():
+    lib = M.lib()
+    d = M.dims(256, 128, 64, 4, False, "f32")
+    L = _fake_layer(d, (64, 0, 0))
+    n = ctypes.c_size_t(0)
+    # size query
+    assert lib.moe_forward_decode(ctypes.byref(d), ctypes.byref(L), None, 8, None, M.MOE_F32, None,
+                                  None, None, ctypes.byref(n), None) == M.MOE_OK
+    dec = n.value
+    assert dec > 0
+    # bf16 output requires bf16 activations
+    assert lib.moe_forward_decode(ctypes.byref(d), ctypes.byref(L), None, 8, None, M.MOE_BF16, None,
+                                  None, None, ctypes.byref(n), None) == M.MOE_EINVAL
+    # too small a workspace, misaligned workspace, null ws_bytes
+    fake_ws = 1 << 24
+    small = ctypes.c_size_t(dec - 1)
+    x = y = 1 << 22
+    assert lib.moe_forward_decode(ctypes.byref(d), ctypes.byref(L), x, 8, y, M.MOE_F32, None, None,
+                                  fake_ws, ctypes.byref(small), None) == M.MOE_ENOSPC
+    big = ctypes.c_size_t(dec)
+    assert lib.moe_forward_decode(ctypes.byref(d), ctypes.byref(L), x, 8, y, M.MOE_F32, None, None,
+                                  fake_ws + 16, ctypes.byref(big), None) == M.MOE_EINVAL
+    assert lib.moe_forward_decode(ctypes.byref(d), ctypes.byref(L), x, 8, y, M.MOE_F32, None, None,
+                                  fake_ws, None, None) == M.MOE_EINVAL
+    # misaligned x
+    assert lib.moe_forward_decode(ctypes.byref(d), ctypes.byref(L), x + 2, 8, y, M.MOE_F32, None,
+                                  None, fake_ws, ctypes.byref(big), None) == M.MOE_EINVAL
+    # prefill: size grows with T, E > 4096 unsupported
+    s1, s2 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.moe_forward_prefill(ctypes.byref(d), ctypes.byref(L), None, 64, None, M.MOE_F32, None,
+                                   None, None, None, None, ctypes.byref(s1), None) == M.MOE_OK
+    assert lib.moe_forward_prefill(ctypes.byref(d), ctypes.byref(L), None, 4096, None, M.MOE_F32,
+                                   None, None, None, None, None, ctypes.byref(s2), None) == M.MOE_OK
+    assert s2.value > s1.value
+    dbig = M.dims(256, 128, 5000, 4, False, "f32")
+    Lb = _fake_layer(dbig, (5000, 0, 0))
+    assert lib.moe_forward_prefill(ctypes.byref(dbig), ctypes.byref(Lb), None, 64, None, M.MOE_F32,
+                                   None, None, None, None, None, ctypes.byref(s1), None) == M.MOE_EUNSUPPORTED
+
+
+# ------------------------------------------------------------ host tier build
+
+def _host_tables(d, n_slots, tier_bits):
+    codes = [[None] * 3 for _ in range(3)]
+    dm = [[None] * 3 for _ in range(3)]
+    L = M.MoeLayer()
+    L.n_slots = (ctypes.c_int32 * 3)(*n_slots)
+    L.tier_bits = (ctypes.c_int32 * 3)(*tier_bits)
+    for t in range(3):
+        if n_slots[t] == 0:
+            continue
+        for m in range(3):
+            codes[t][m] = np.zeros(M.tier_table_bytes(d, tier_bits[t], n_slots[t], m, M.MOE_CODES), np.uint8)
+            dm[t][m] = np.zeros(M.tier_table_bytes(d, tier_bits[t], n_slots[t], m, M.MOE_DM) // 4, np.uint32)
+            L.codes[t][m] = codes[t][m].ctypes.data
+            L.dm[t][m] = dm[t][m].ctypes.data
+    return L, codes, dm
+
+
+def _oracle_tables(blocks_by_expert, slot_expert, n_slots, tier_bits):
+    """Oracle packing of every tier table from per-expert (d, m, q)."""
+    out = {}
+    start = [0, n_slots[0], n_slots[0] + n_slots[1]]
+    for t in range(3):
+        if n_slots[t] == 0:
+            continue
+        for m in range(3):
+            experts = [slot_expert[start[t] + s] for s in range(n_slots[t])]
+            q = np.stack([blocks_by_expert[e][m][2] for e in experts])
+            dd = np.stack([blocks_by_expert[e][m][0] for e in experts])
+            mm = np.stack([blocks_by_expert[e][m][1] for e in experts])
+            out[(t, m)] = O.pack_tiles(q, dd, mm, tier_bits[t])
+    return out
+
+
+def test_build_tiers_map_only_matches_oracle():
+    rng = np.random.default_rng(20)
+    for E, ns in ((64, (64, 0, 0)), (512, (128, 256, 128)), (10, (3, 4, 3))):
+        pop = rng.integers(0, 5, E).astype(np.uint64)
+        d = M.dims(256, 128, E, 4, False, "f32")
+        tmap, sexp = M.build_tiers(d, pop, ns, (4, 3, 2))
+        want_map, want_se = O.build_tiers(pop, ns)
+        np.testing.assert_array_equal(tmap, want_map)
+        np.testing.assert_array_equal(sexp, want_se)
+
+
+@pytest.mark.parametrize("tier_bits", [(4, 3, 2), (2, 4, 3)])
+def test_build_tiers_f32_bit_exact_vs_oracle(tier_bits):
+    spec = synth.TINY.with_(n_experts=12, n_slots=(3, 6, 3))
+    d = M.dims(spec.hidden, spec.inter, spec.n_experts, spec.top_k, False, spec.act)
+    gate, up, down = synth.expert_weights_f32(spec, seed=21)
+    pop = np.random.default_rng(22).integers(0, 100, spec.n_experts).astype(np.uint64)
+    L, codes, dm = _host_tables(d, spec.n_slots, tier_bits)
+    src = M.source_f32(gate, up, down)
+    tmap, sexp = M.build_tiers(d, pop, spec.n_slots, tier_bits, src, L, dst_on_device=False)
+    want_map, want_se = O.build_tiers(pop, spec.n_slots)
+    np.testing.assert_array_equal(tmap, want_map)
+    bits_of = {e: tier_bits[int(want_map[e]) >> 16] for e in range(spec.n_experts)}
+    blocks = {e: [O.quantise_rows(w[e], bits_of[e]) for w in (gate, up, down)]
+              for e in range(spec.n_experts)}
+    want = _oracle_tables(blocks, want_se, spec.n_slots, tier_bits)
+    for (t, m), (wc, wd) in want.items():
+        np.testing.assert_array_equal(codes[t][m], wc, err_msg=f"codes tier {t} mat {m}")
+        np.testing.assert_array_equal(dm[t][m], wd, err_msg=f"dm tier {t} mat {m}")
+
+
+def test_build_tiers_codes_source_bit_exact_vs_oracle():
+    spec = synth.TINY.with_(hidden=256, inter=128, n_experts=8, n_slots=(2, 4, 2))
+    tier_bits = (4, 3, 2)
+    d = M.dims(spec.hidden, spec.inter, spec.n_experts, spec.top_k, False, spec.act)
+    pop = np.arange(spec.n_experts, dtype=np.uint64)[::-1].copy()
+    tmap, sexp = M.build_tiers(d, pop, spec.n_slots, tier_bits)
+    bits_of = [tier_bits[int(v) >> 16] for v in tmap]
+    per = [synth.expert_codes(spec, bits_of[e], seed=23, expert=e) for e in range(spec.n_experts)]
+    q = [np.ascontiguousarray(np.stack([per[e][n][2] for e in range(spec.n_experts)]))
+         for n in ("gate", "up", "down")]
+    dd = [np.ascontiguousarray(np.stack([per[e][n][0] for e in range(spec.n_experts)]))
+          for n in ("gate", "up", "down")]
+    mm = [np.ascontiguousarray(np.stack([per[e][n][1] for e in range(spec.n_experts)]))
+          for n in ("gate", "up", "down")]
+    L, codes, dm = _host_tables(d, spec.n_slots, tier_bits)
+    M.build_tiers(d, pop, spec.n_slots, tier_bits, M.source_codes(q, dd, mm), L)
+    blocks = {e: [per[e][n] for n in ("gate", "up", "down")] for e in range(spec.n_experts)}
+    want = _oracle_tables(blocks, sexp, spec.n_slots, tier_bits)
+    for (t, m), (wc, wd) in want.items():
+        np.testing.assert_array_equal(codes[t][m], wc)
+        np.testing.assert_array_equal(dm[t][m], wd)
+
+
+def test_build_tiers_rejects_bad_input():
+    spec = synth.TINY.with_(n_experts=4, n_slots=(4, 0, 0))
+    d = M.dims(spec.hidden, spec.inter, 4, 2, False, "f32")
+    gate, up, down = synth.expert_weights_f32(spec, seed=24)
+    L, codes, dm = _host_tables(d, (4, 0, 0), (4, 3, 2))  # keep the buffers alive
+    pop = np.zeros(4, np.uint64)
+    gate[2, 5, 7] = np.inf
+    with pytest.raises(M.MoeError) as e:
+        M.build_tiers(d, pop, (4, 0, 0), (4, 3, 2), M.source_f32(gate, up, down), L)
+    assert e.value.status == M.MOE_EINVAL
+    with pytest.raises(M.MoeError):
+        M.build_tiers(d, pop, (2, 1, 0), (4, 3, 2))           # counts do not sum to E
+    # a code above the tier's largest code
+    q = [np.zeros((4, r, c), np.uint8) for r, c in ((128, 256), (128, 256), (256, 128))]
+    dd = [np.ones((4, r, c // 32), np.float16) for r, c in ((128, 256), (128, 256), (256, 128))]
+    mm = [np.zeros((4, r, c // 32), np.float16) for r, c in ((128, 256), (128, 256), (256, 128))]
+    q[1][3, 0, 0] = 16
+    with pytest.raises(M.MoeError):
+        M.build_tiers(d, pop, (4, 0, 0), (4, 3, 2), M.source_codes(q, dd, mm), L)

@@ -485,3 +485,11 @@ def test_layer_relabelling_invariance():
     np.testing.assert_allclose(out2["y"], y, rtol=1e-12, atol=1e-12)
     ids1 = O.moe_layer(x, layer)["ids"]
     np.testing.assert_array_equal(perm[out2["ids"]], ids1)
+
+
+def test_output_cast_is_one_rounding():
+    y = np.array([1.0 + 2.0 ** -8 + 2.0 ** -30, -3.0000001, 0.0, 1e-3])
+    got = O.output_cast(y, "bf16")
+    for v, g in zip(y, got):
+        assert Fraction(float(g)) == _bf16_exact(Fraction(float(v)))
+    np.testing.assert_array_equal(O.output_cast(y, "f32"), y.astype(np.float32).astype(np.float64))
