@@ -1,0 +1,366 @@
+#!/usr/bin/env python3
+"""Throughput of the routed, tiered, dequantised MoE layer on one MI355X.
+
+Metric: MoE-layer tokens/s for batch-1 decode of one full-size layer
+(hidden 2048, 512 experts, top-10 + 1 shared, intermediate 512, bf16
+activations, experts tiered 128/256/128 at 4/3/2 bits in blocks of 32).
+
+One step = one token decoded through a stack of 48 independent full-size
+layers (distinct weights, 36 GiB of packed tiers resident in HBM), so every
+layer reads its experts from HBM rather than from the 256 MB last-level
+cache; value = 48 * steps / elapsed seconds.  Each token/layer pair has its
+own N(0,1) input row.  The 48 layer calls of one token are captured in one
+HIP graph; 16 graphs (16 token rows) are replayed round-robin.
+
+Also reported: per-kernel durations from the library's launch trace (HIP
+events attached to each kernel dispatch) over an eager pass of the same
+16 x 48 calls right after the timed region, the HBM roofline of the dominant
+decode kernel, prefill of 4096 tokens through one layer (rotating over the
+stack) with the MFMA roofline of its grouped GEMM, and the CPU oracle timed
+on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 64] [--warmup 16]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+for p in (ROOT, os.path.join(ROOT, "tests")):
+    if p not in sys.path:
+        sys.path.insert(0, p)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+N_LAYERS = 48
+N_GRAPHS = 16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--prefill-steps", type=int, default=8)
+    ap.add_argument("--prefill-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
+    ap.add_argument("--seed", type=int, default=1234)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# synthetic full-size layers, generated on the device
+# ---------------------------------------------------------------------------
+
+def make_stack(M, torch, spec, n_layers, seed):
+    """48 full-size layers with seeded random tables (torch Philox on the GPU).
+
+    Tier tables: iid uniform code bytes (every byte pattern is a valid code
+    field), scales d = sigma / std(q) * U(0.8, 1.2) and mins
+    m = -d L / 2 + N(0, (0.05 sigma)^2), sigma = 1/sqrt(fan_in), so the
+    dequantised weights have std ~ 1/sqrt(fan_in).  Router N(0, 0.02^2) in
+    bf16 with bias 0.27 * N(0, 1); shared expert N(0, 1/fan_in) in bf16.
+    Popularity per layer: route counts of 4096 N(0,1) calibration tokens
+    (moe_route), ranked into tiers by moe_build_tiers.
+    """
+    import synth
+
+    d = M.dims(spec.hidden, spec.inter, spec.n_experts, spec.top_k, True, "bf16")
+    H, I, E = spec.hidden, spec.inter, spec.n_experts
+    gen = torch.Generator(device="cuda")
+    layers = []
+    calib_ids = torch.empty((4096, spec.top_k), dtype=torch.int32, device="cuda")
+    calib_w = torch.empty((4096, spec.top_k), dtype=torch.float32, device="cuda")
+    for l in range(n_layers):
+        gen.manual_seed(seed * 1000 + l)
+        w_r = (torch.randn((E, H), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+        bias = (torch.randn(E, generator=gen, device="cuda") * synth.DEFAULT_BIAS_BETA).float()
+        shared = [(torch.randn(shape, generator=gen, device="cuda") / np.sqrt(shape[1])).to(torch.bfloat16)
+                  for shape in ((I, H), (I, H), (H, I))]
+        lay = M.DeviceLayer(d, spec.n_slots, spec.tier_bits, (w_r, bias), shared)
+        for t in range(3):
+            bits = spec.tier_bits[t]
+            L = (1 << bits) - 1
+            std_q = float(np.sqrt(((L + 1) ** 2 - 1) / 12.0))
+            for m in range(3):
+                fan_in = H if m != M.MOE_DOWN else I
+                sigma = 1.0 / np.sqrt(fan_in)
+                c = lay.codes[t][m]
+                c.copy_(torch.randint(0, 256, c.shape, generator=gen, device="cuda", dtype=torch.uint8))
+                n = lay.dm[t][m].numel()
+                dd = (sigma / std_q) * (0.8 + 0.4 * torch.rand(n, generator=gen, device="cuda"))
+                mm = -dd * (L / 2.0) + 0.05 * sigma * torch.randn(n, generator=gen, device="cuda")
+                db = dd.half().view(torch.int16).to(torch.int32) & 0xFFFF
+                mb = mm.half().view(torch.int16).to(torch.int32) & 0xFFFF
+                lay.dm[t][m].copy_(db | (mb << 16))
+        xc = torch.randn((4096, H), generator=gen, device="cuda").to(torch.bfloat16)
+        M.route(d, lay.c_struct(), xc, calib_ids, calib_w)
+        pop = torch.bincount(calib_ids.flatten().long(), minlength=E).cpu().numpy().astype(np.uint64)
+        tmap, _ = M.build_tiers(d, pop, spec.n_slots, spec.tier_bits)
+        lay.tier_map.copy_(torch.from_numpy(tmap))
+        lay.popularity = pop
+        lay.tmap_host = tmap
+        lay.cs = lay.c_struct()
+        layers.append(lay)
+        if l % 8 == 7:
+            log(f"built layers 0..{l}")
+    torch.cuda.synchronize()
+    return d, layers
+
+
+def table_bytes(spec, bits, mat):
+    rows, cols = (spec.hidden, spec.inter) if mat == 2 else (spec.inter, spec.hidden)
+    blocks = rows * cols // 32
+    return blocks * (4 * bits + 4)
+
+
+def decode_kernel_bytes(spec, layer, ids_row):
+    """Algorithmic HBM bytes of each decode kernel for one token (T = 1).
+
+    router_keys: router weights + bias + x + keys written.  topk_items: keys
+    read, ids/weights/items written.  decode_gateup: gate+up blocks (codes and
+    scale/min) of the K chosen experts at their tier widths + the shared
+    expert's bf16 gate/up + x + h written.  decode_down: down blocks of the K
+    experts + shared bf16 down + h read + y written (bf16).
+    """
+    H, I, E, K = spec.hidden, spec.inter, spec.n_experts, spec.top_k
+    bits = [spec.tier_bits[int(layer.tmap_host[e]) >> 16] for e in ids_row]
+    gu = sum(table_bytes(spec, b, 0) + table_bytes(spec, b, 1) for b in bits) + 2 * I * H * 2
+    dn = sum(table_bytes(spec, b, 2) for b in bits) + H * I * 2
+    return {
+        "router_keys": E * H * 2 + E * 4 + H * 2 + E * 8,
+        "topk_items": E * 8 + K * 8 + (K + 1) * 136,
+        "decode_gateup": gu + H * 2 + (K + 1) * I * 2,
+        "decode_down": dn + (K + 1) * I * 2 + H * 2,
+    }
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(n_tokens, seed):
+    import oracle as O
+    import synth
+    from threadpoolctl import threadpool_limits
+
+    spec = synth.FULL
+    cores = len(os.sched_getaffinity(0))
+    w_router, bias = synth.router(spec, seed)
+    shared = synth.shared_expert(spec, seed + 3)
+    wr64 = O.bf16_bits_to_f64(w_router)
+    xc = O.bf16_bits_to_f64(synth.tokens(spec, 4096, seed + 1))
+    ids_c = O.select_topk(O.router_keys(xc, wr64, bias), spec.top_k)
+    pop = np.bincount(ids_c.ravel(), minlength=spec.n_experts).astype(np.uint64)
+    tmap, _ = O.build_tiers(pop, spec.n_slots)
+    x = O.bf16_bits_to_f64(synth.tokens(spec, n_tokens, seed + 4))
+    routing = O.route(x, wr64, bias, spec.top_k)
+    touched = sorted(set(int(e) for e in routing[1].ravel()))
+    blocks = {}
+    for e in touched:            # input generation, outside the timed region
+        b = spec.tier_bits[int(tmap[e]) >> 16]
+        p = synth.expert_codes(spec, b, seed + 2, e)
+        blocks[e] = O.ExpertBlocks(b, p["gate"], p["up"], p["down"])
+    layer = O.OracleLayer(act="bf16", w_router=wr64, bias=bias, top_k=spec.top_k,
+                          experts=lambda e: blocks[e],
+                          shared=tuple(O.bf16_bits_to_f64(s) for s in shared))
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        for t in range(n_tokens):       # batch-1 decode: one token per call
+            O.moe_layer(x[t:t + 1], layer)
+        dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "MoE-layer tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_tokens} batch-1 decode tokens through one full-size layer (host-generated "
+                      f"seeded blocks of the same shapes and tiers); NumPy fp64, BLAS on {cores} "
+                      f"threads, element-wise dequantisation single-threaded; {dt:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "single-GPU build: this benchmark runs on exactly one GPU "
+                          "(--gpus 1); multi-GPU sharding is not implemented"}))
+        sys.exit(2)
+    import torch
+    import synth
+    import quantized_expert_ffn_route_amd as M
+
+    M.lib()                       # fail loudly if the HIP library is missing
+    spec = synth.FULL
+    H, I, K = spec.hidden, spec.inter, spec.top_k
+    log("building the 48-layer stack")
+    d, layers = make_stack(M, torch, spec, N_LAYERS, args.seed)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(args.seed + 7)
+    X = torch.randn((N_GRAPHS, N_LAYERS, 1, H), generator=gen, device="cuda").to(torch.bfloat16)
+    Y = torch.empty((N_LAYERS, 1, H), dtype=torch.bfloat16, device="cuda")
+    IDS = torch.empty((N_GRAPHS, N_LAYERS, 1, K), dtype=torch.int32, device="cuda")
+    WTS = torch.empty((N_GRAPHS, N_LAYERS, 1, K), dtype=torch.float32, device="cuda")
+    ws_n = M.workspace_bytes("decode", d, layers[0].cs, 1, M.MOE_BF16)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+
+    def token_pass(g):
+        for l in range(N_LAYERS):
+            M.forward_decode(d, layers[l].cs, X[g, l], Y[l], M.MOE_BF16, IDS[g, l], WTS[g, l], ws=ws)
+
+    per_graph = 4 * N_LAYERS                     # kernels per token pass
+    graphs = None
+    if not args.eager:
+        graphs = []
+        for g in range(N_GRAPHS):
+            token_pass(g)                            # warm code objects and caches
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                token_pass(g)
+            graphs.append(graph)
+    torch.cuda.synchronize()
+
+    def step(k):
+        if graphs is None:
+            token_pass(k % N_GRAPHS)
+        else:
+            graphs[k % N_GRAPHS].replay()
+
+    log(f"warmup {args.warmup} steps")
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for k in range(args.steps):
+        step(k)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = ev0.elapsed_time(ev1) / 1e3
+    value = N_LAYERS * args.steps / wall
+
+    # Per-kernel durations: the same 16 x 48 token/layer calls launched
+    # eagerly with HIP events attached to every kernel dispatch (ROCm has no
+    # event-record nodes inside graphs, so the replayed graphs cannot carry
+    # them).  The events time each kernel's own execution.
+    trace = M.Trace(N_GRAPHS * per_graph)
+    with trace:
+        for g in range(N_GRAPHS):
+            token_pass(g)
+    torch.cuda.synchronize()
+    durs = trace.durations_ms(0)
+    ids_host = IDS.cpu().numpy()
+    per_kernel = {}
+    for i, (name, ms) in enumerate(durs):
+        g, rem = divmod(i, per_graph)
+        l = rem // 4
+        nbytes = decode_kernel_bytes(spec, layers[l], ids_host[g, l, 0])[name]
+        pk = per_kernel.setdefault(name, {"n": 0, "ms": 0.0, "bytes": 0})
+        pk["n"] += 1
+        pk["ms"] += ms
+        pk["bytes"] += nbytes
+    kernels = {}
+    for name, pk in per_kernel.items():
+        avg_us = 1e3 * pk["ms"] / pk["n"]
+        avg_b = pk["bytes"] / pk["n"]
+        kernels[name] = {"avg_us": round(avg_us, 3), "bytes": int(avg_b),
+                         "GB/s": round(avg_b / (avg_us * 1e-6) / 1e9, 1), "launches": pk["n"]}
+    dom = kernels.get("decode_gateup")
+    roofline = None
+    if dom:
+        roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "k_decode_gateup", "bytes_per_launch": dom["bytes"],
+                    "avg_us": dom["avg_us"]}
+    layer_bytes = sum(k["bytes"] for k in kernels.values()) if kernels else None
+    log(f"decode: {value:.0f} layer-tokens/s, {1e6 * wall / (N_LAYERS * args.steps):.2f} us/layer")
+
+    prefill = None
+    if not args.no_prefill:
+        T = args.prefill_tokens
+        Xp = torch.randn((T, H), generator=gen, device="cuda").to(torch.bfloat16)
+        Yp = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        wsp = torch.empty(M.workspace_bytes("prefill", d, layers[0].cs, T, M.MOE_BF16),
+                          dtype=torch.uint8, device="cuda")
+        for k in range(2):
+            M.forward_prefill(d, layers[k].cs, Xp, Yp, M.MOE_BF16, ws=wsp)
+        torch.cuda.synchronize()
+        ptrace = M.Trace(64 * args.prefill_steps)
+        t0 = time.perf_counter()
+        with ptrace:
+            for k in range(args.prefill_steps):
+                M.forward_prefill(d, layers[k % N_LAYERS].cs, Xp, Yp, M.MOE_BF16, ws=wsp)
+        torch.cuda.synchronize()
+        pwall = time.perf_counter() - t0
+        pk = {}
+        for name, ms in ptrace.durations_ms():
+            pk.setdefault(name, []).append(ms)
+        routed_gu_flops = 2.0 * T * K * 2 * I * H
+        layer_flops = 2.0 * T * (K * 3 * I * H + 3 * I * H + spec.n_experts * H)
+        gu_us = 1e3 * float(np.mean(pk["prefill_gateup"]))
+        prefill = {
+            "workload": f"prefill {T} tokens, one full-size layer (rotating over the stack)",
+            "tokens_per_s": round(T * args.prefill_steps / pwall, 1),
+            "ms_per_layer": round(1e3 * pwall / args.prefill_steps, 3),
+            "layer_tflops": round(layer_flops / (pwall / args.prefill_steps) / 1e12, 1),
+            "kernels_avg_us": {n: round(1e3 * float(np.mean(v)), 2) for n, v in pk.items()},
+            "roofline": {"bound": "mfma", "kernel": "k_prefill<routed gate/up>",
+                         "achieved": round(routed_gu_flops / (gu_us * 1e-6) / 1e12, 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(routed_gu_flops / (gu_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "flops_per_launch": routed_gu_flops, "avg_us": round(gu_us, 2),
+                         "traffic": None},
+        }
+        log(f"prefill: {prefill['tokens_per_s']:.0f} tokens/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(args.cpu_tokens, args.seed)
+
+    line = {
+        "metric": "MoE-layer tokens/s (batch-1 decode, 4k prefill) + % HBM/MFMA roofline",
+        "value": round(value, 1),
+        "unit": "MoE-layer tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * wall / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random 4/3/2-bit blocks, bf16 router/shared, N(0,1) tokens)",
+        "config": {"workload": "one full-size MoE layer, batch-1 decode (hidden 2048, 512 experts, "
+                               "top-10 + 1 shared, intermediate 512, tiers 128/256/128 at 4/3/2 bits)"
+                               ", timed as one token through 48 distinct layers per step",
+                   "layers_per_step": N_LAYERS, "tokens_per_step": 1,
+                   "us_per_layer": round(1e6 * wall / (N_LAYERS * args.steps), 3),
+                   "gpu_event_s": round(gpu_s, 6), "graphs": not args.eager,
+                   "layer_bytes": layer_bytes},
+        "roofline": roofline,
+        "kernels": kernels,
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

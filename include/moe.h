@@ -16,7 +16,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every pointer named "device" is device memory owned by the caller; the
- *   library never allocates device memory and keeps no global state.
+ *   library never allocates device memory and keeps no global state apart
+ *   from the optional launch trace of moe_set_trace.
  * - Forward calls and moe_route only enqueue work on `stream` and return;
  *   they never synchronise, print or abort.  They may be captured into a HIP
  *   graph (they issue kernels only; no memset or memcpy nodes).
@@ -228,6 +229,37 @@ int moe_forward_prefill(const moe_dims* dims, const moe_layer* layer, const void
                         int32_t T, void* y, int32_t y_dt, int32_t* topk_ids,
                         float* topk_w, int32_t* expert_offsets, int32_t* sorted_routes,
                         void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/* Kernels of the library, as reported by the launch trace. */
+typedef enum {
+  MOE_K_ROUTER_KEYS = 1,           /* A1: float64 router GEMV                   */
+  MOE_K_TOPK = 2,                  /* A2: top-K + weights, many tokens          */
+  MOE_K_TOPK_ITEMS = 3,            /* A2+A3: top-K + decode work items          */
+  MOE_K_DECODE_GATEUP = 4,         /* A5: decode gate/up + SwiGLU               */
+  MOE_K_DECODE_DOWN = 5,           /* A6: decode down + combine                 */
+  MOE_K_SORT_COUNT = 6,            /* A4: per-chunk expert masks                */
+  MOE_K_SORT_SCAN = 7,             /* A4: bucket offsets                        */
+  MOE_K_SORT_SCATTER = 8,          /* A4: stable scatter                        */
+  MOE_K_PREFILL_GATEUP = 9,        /* A7: routed grouped gate/up GEMM           */
+  MOE_K_PREFILL_SHARED_GATEUP = 10,/* A7: shared expert gate/up GEMM            */
+  MOE_K_PREFILL_SHARED_DOWN = 11,  /* A8: shared expert down GEMM (initialises) */
+  MOE_K_PREFILL_DOWN = 12,         /* A8: routed down GEMM + weighted scatter   */
+  MOE_K_CAST = 13,                 /* fp32 accumulator -> bf16 output           */
+  MOE_K_ZERO = 14                  /* zero the fp32 accumulator                 */
+} moe_kernel_id;
+
+/* Launch trace, for measurement harnesses (not part of the computation).
+ * While installed, every kernel this library launches on a stream that is
+ * not being captured into a graph carries events[2i] and events[2i+1] as the
+ * start and stop events of its dispatch (hipExtLaunchKernel: they time the
+ * kernel's own execution), with i = (*n_used)++ and tags[i] set to its
+ * moe_kernel_id, for the first capacity/2 launches.  Launches captured into
+ * a graph are not traced: event-record nodes inside graphs are not available
+ * on ROCm.  Events must be created without hipEventDisableTiming.
+ * events == NULL removes the trace.  Process-wide, not thread-safe.  Returns
+ * MOE_EINVAL for a negative capacity or missing tags / n_used when
+ * events != NULL. */
+int moe_set_trace(hipEvent_t* events, int32_t* tags, int32_t capacity, int32_t* n_used);
 
 /* Human-readable name of a moe_status value (static string). */
 const char* moe_status_string(int status);

@@ -26,7 +26,7 @@ __all__ = [
     "MoeError", "MoeLibraryMissing", "MoeDims", "MoeLayer", "MoeExpertSource",
     "lib", "library_path", "status_string", "dims", "tier_table_bytes",
     "build_tiers", "route", "forward_decode", "forward_prefill", "workspace_bytes",
-    "DeviceLayer",
+    "DeviceLayer", "Trace", "KERNEL_NAMES",
 ]
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
@@ -34,6 +34,14 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_GATE, MOE_UP, MOE_DOWN = 0, 1, 2
 MOE_CODES, MOE_DM = 0, 1
 MOE_SRC_F32, MOE_SRC_CODES = 0, 1
+
+#: Kernel ids reported by the launch trace (moe_kernel_id in moe.h).
+KERNEL_NAMES = {
+    1: "router_keys", 2: "topk", 3: "topk_items", 4: "decode_gateup", 5: "decode_down",
+    6: "sort_count", 7: "sort_scan", 8: "sort_scatter", 9: "prefill_gateup",
+    10: "prefill_shared_gateup", 11: "prefill_shared_down", 12: "prefill_down", 13: "cast",
+    14: "zero",
+}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -96,6 +104,8 @@ def lib():
         L.moe_forward_decode.argtypes = [POINTER(MoeDims), POINTER(MoeLayer), c_void_p, c_int32,
                                          c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                                          POINTER(c_size_t), c_void_p]
+        L.moe_set_trace.restype = ctypes.c_int
+        L.moe_set_trace.argtypes = [c_void_p, c_void_p, c_int32, c_void_p]
         L.moe_forward_prefill.restype = ctypes.c_int
         L.moe_forward_prefill.argtypes = [POINTER(MoeDims), POINTER(MoeLayer), c_void_p, c_int32,
                                           c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -225,6 +235,45 @@ def forward_prefill(d: MoeDims, layer: MoeLayer, x, y, y_dt: int, topk_ids=None,
                                    _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets),
                                    _ptr(sorted_routes), _ptr(ws), ctypes.byref(n), _stream(stream))
     _check(rc, "moe_forward_prefill")
+
+
+class Trace:
+    """Launch trace (``moe_set_trace``): HIP events on every kernel dispatch.
+
+    Use as a context manager around eager calls (launches captured into a
+    graph are not traced); afterwards ``durations_ms()`` lists
+    ``(kernel_name, ms)`` per traced launch.  Needs torch with a GPU.
+    """
+
+    def __init__(self, capacity_launches: int):
+        import torch
+
+        self.capacity = int(capacity_launches)
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * self.capacity)]
+        for e in self.events:
+            e.record()                          # materialise the hipEvent_t
+        self._ev_arr = (c_void_p * (2 * self.capacity))(*[e.cuda_event for e in self.events])
+        self._tags = np.zeros(self.capacity, dtype=np.int32)
+        self._used = np.zeros(1, dtype=np.int32)
+
+    def __enter__(self):
+        _check(lib().moe_set_trace(self._ev_arr, self._tags.ctypes.data, 2 * self.capacity,
+                                   self._used.ctypes.data), "moe_set_trace")
+        return self
+
+    def __exit__(self, *exc):
+        lib().moe_set_trace(None, None, 0, None)
+
+    @property
+    def used(self) -> int:
+        return int(self._used[0])
+
+    def durations_ms(self, start: int = 0):
+        out = []
+        for i in range(start, self.used):
+            ms = self.events[2 * i].elapsed_time(self.events[2 * i + 1])
+            out.append((KERNEL_NAMES.get(int(self._tags[i]), str(int(self._tags[i]))), ms))
+        return out
 
 
 class DeviceLayer:

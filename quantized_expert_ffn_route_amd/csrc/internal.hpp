@@ -4,6 +4,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "moe.h"
@@ -34,6 +35,25 @@ struct Tables {
   int32_t n_slots[3];
   const void* dense[3];    // shared expert gate / up / down (act dtype)
 };
+
+// ---- launch trace (moe_set_trace); defined in moe_abi.cpp ----
+// Returns the start/stop events of the next trace slot for a kernel launched
+// on `s`, or leaves them null (no trace installed, slots used up, or `s` is
+// being captured into a graph).
+void trace_slot(int kernel_id, hipStream_t s, hipEvent_t* start, hipEvent_t* stop);
+
+// Launches a kernel; when traced, the events are attached to the dispatch
+// itself (hipExtLaunchKernel), so they time the kernel's execution only.
+#define MOE_LAUNCH(KID, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                           \
+  do {                                                                                     \
+    hipEvent_t moe_e0_ = nullptr, moe_e1_ = nullptr;                                       \
+    ::moe::trace_slot((KID), (STREAM), &moe_e0_, &moe_e1_);                                \
+    if (moe_e0_)                                                                           \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, moe_e0_, moe_e1_, 0,       \
+                            __VA_ARGS__);                                                  \
+    else                                                                                   \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);                 \
+  } while (0)
 
 // ---- launchers (defined in the .hip files; all enqueue on `s`) ----
 

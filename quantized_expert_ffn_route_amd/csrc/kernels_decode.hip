@@ -263,10 +263,10 @@ void launch_decode_gateup(int act, const Item* items, const int32_t* n_items, in
                           hipStream_t s) {
   dim3 grid(max_items * (I / 16));
   if (act == MOE_BF16)
-    hipLaunchKernelGGL(k_decode_gateup<bf16_t>, grid, dim3(256), 0, s, items, n_items,
+    MOE_LAUNCH(MOE_K_DECODE_GATEUP, k_decode_gateup<bf16_t>, grid, dim3(256), 0, s, items, n_items,
                        (const bf16_t*)x, T, tb, (bf16_t*)h, H, I);
   else
-    hipLaunchKernelGGL(k_decode_gateup<float>, grid, dim3(256), 0, s, items, n_items,
+    MOE_LAUNCH(MOE_K_DECODE_GATEUP, k_decode_gateup<float>, grid, dim3(256), 0, s, items, n_items,
                        (const float*)x, T, tb, (float*)h, H, I);
 }
 
@@ -277,13 +277,13 @@ void launch_decode_down(int act, int y_dt, const Item* items, const int32_t* n_i
   dim3 grid(H / 16);
   if (act == MOE_BF16) {
     if (y_dt == MOE_BF16)
-      hipLaunchKernelGGL((k_decode_down<bf16_t, bf16_t>), grid, dim3(512), 0, s, items, n_items,
+      MOE_LAUNCH(MOE_K_DECODE_DOWN, (k_decode_down<bf16_t, bf16_t>), grid, dim3(512), 0, s, items, n_items,
                          (const bf16_t*)h, T, tb, (bf16_t*)y, H, I);
     else
-      hipLaunchKernelGGL((k_decode_down<bf16_t, float>), grid, dim3(512), 0, s, items, n_items,
+      MOE_LAUNCH(MOE_K_DECODE_DOWN, (k_decode_down<bf16_t, float>), grid, dim3(512), 0, s, items, n_items,
                          (const bf16_t*)h, T, tb, (float*)y, H, I);
   } else {
-    hipLaunchKernelGGL((k_decode_down<float, float>), grid, dim3(512), 0, s, items, n_items,
+    MOE_LAUNCH(MOE_K_DECODE_DOWN, (k_decode_down<float, float>), grid, dim3(512), 0, s, items, n_items,
                        (const float*)h, T, tb, (float*)y, H, I);
   }
 }

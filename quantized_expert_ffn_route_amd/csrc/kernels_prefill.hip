@@ -86,43 +86,20 @@ __device__ __forceinline__ void load_b(BFrag<A>& b, const Tables& tb, int tier, 
   }
 }
 
+// One workgroup's work: weight rows [nt*128, nt*128 + 128) of one expert
+// (or of the shared expert) against `nrows` token rows starting at `row0`.
 template <typename A, int BITS, int MODE>
-__global__ __launch_bounds__(256) void k_prefill(PArgs a) {
+__device__ __forceinline__ void prefill_body(const PArgs& a, int row0, int nrows, int tier, int slot,
+                                             int nt, uint32_t* __restrict__ sA) {
   constexpr bool GATEUP = MODE == kRoutedGateUp || MODE == kSharedGateUp;
-  constexpr bool ROUTED = MODE == kRoutedGateUp || MODE == kRoutedDown;
   constexpr int NMAT = GATEUP ? 2 : 1;
   constexpr int ROWS = PTraits<A>::ROWS, RU = PTraits<A>::ROW_U32;
   constexpr int MT = ROWS / 16;
-  __shared__ uint32_t sA[ROWS * RU];
-
   const int Kc = GATEUP ? a.H : a.I;        // contraction length
   const int Nr = GATEUP ? a.I : a.H;        // weight rows (output features)
-  const int NT = Nr / 128, nbg = Kc / 128;
+  const int nbg = Kc / 128;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lm = lane & 15, lg = lane >> 4;
-
-  // XCD-aware mapping: the workgroups that share one expert's (or one token
-  // chunk's) rows land on the same XCD, whose L2 then serves the re-reads.
-  const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
-  const int grp = (j / NT) * 8 + xcd, nt = j % NT;
-
-  int row0, nrows, tier = 0, slot = 0, bits = 0;
-  if constexpr (ROUTED) {
-    if (grp >= a.E) return;
-    row0 = a.offsets[grp];
-    nrows = a.offsets[grp + 1] - row0;
-    if (nrows == 0) return;
-    const int tm = a.tier_map[grp];
-    tier = tm >> 16;
-    slot = tm & 0xFFFF;
-    if (tier < 0 || tier > 2 || slot >= a.tb.n_slots[tier]) return;
-    bits = a.tb.bits[tier];
-    if (bits != BITS) return;  // another launch handles this width
-  } else {
-    row0 = grp * ROWS;
-    if (row0 >= a.T) return;
-    nrows = min(ROWS, a.T - row0);
-  }
   const A* src = reinterpret_cast<const A*>(a.src);
   const int n0 = nt * 128 + wave * 32;      // first weight row of this wave
 
@@ -234,24 +211,49 @@ __global__ __launch_bounds__(256) void k_prefill(PArgs a) {
 }
 
 template <typename A, int MODE>
+__global__ __launch_bounds__(256) void k_prefill(PArgs a) {
+  constexpr bool GATEUP = MODE == kRoutedGateUp || MODE == kSharedGateUp;
+  constexpr bool ROUTED = MODE == kRoutedGateUp || MODE == kRoutedDown;
+  constexpr int ROWS = PTraits<A>::ROWS, RU = PTraits<A>::ROW_U32;
+  __shared__ uint32_t sA[ROWS * RU];
+  const int Nr = GATEUP ? a.I : a.H;
+  const int NT = Nr / 128;
+  // XCD-aware mapping: the workgroups that share one expert's (or one token
+  // chunk's) rows land on the same XCD, whose L2 then serves the re-reads.
+  const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
+  const int grp = (j / NT) * 8 + xcd, nt = j % NT;
+  if constexpr (ROUTED) {
+    if (grp >= a.E) return;
+    const int row0 = a.offsets[grp];
+    const int nrows = a.offsets[grp + 1] - row0;
+    if (nrows == 0) return;
+    const int tm = a.tier_map[grp];
+    const int tier = tm >> 16, slot = tm & 0xFFFF;
+    if (tier < 0 || tier > 2 || slot >= a.tb.n_slots[tier]) return;
+    // the tier's code width is uniform over the workgroup
+    switch (a.tb.bits[tier]) {
+      case 4: prefill_body<A, 4, MODE>(a, row0, nrows, tier, slot, nt, sA); break;
+      case 3: prefill_body<A, 3, MODE>(a, row0, nrows, tier, slot, nt, sA); break;
+      default: prefill_body<A, 2, MODE>(a, row0, nrows, tier, slot, nt, sA); break;
+    }
+  } else {
+    const int row0 = grp * ROWS;
+    if (row0 >= a.T) return;
+    prefill_body<A, 0, MODE>(a, row0, min(ROWS, a.T - row0), 0, 0, nt, sA);
+  }
+}
+
+template <typename A, int MODE>
 void launch_mode(const PArgs& a, int n_groups, hipStream_t s) {
   constexpr bool GATEUP = MODE == kRoutedGateUp || MODE == kSharedGateUp;
   const int Nr = GATEUP ? a.I : a.H;
   const int NT = Nr / 128;
   dim3 grid(((n_groups + 7) / 8) * 8 * NT);
-  if constexpr (MODE == kRoutedGateUp || MODE == kRoutedDown) {
-    // one kernel per tier width present: experts of other tiers exit early
-    bool seen[5] = {false, false, false, false, false};
-    for (int t = 0; t < 3; t++) {
-      if (a.tb.n_slots[t] == 0 || seen[a.tb.bits[t]]) continue;
-      seen[a.tb.bits[t]] = true;
-      if (a.tb.bits[t] == 4) hipLaunchKernelGGL((k_prefill<A, 4, MODE>), grid, dim3(256), 0, s, a);
-      if (a.tb.bits[t] == 3) hipLaunchKernelGGL((k_prefill<A, 3, MODE>), grid, dim3(256), 0, s, a);
-      if (a.tb.bits[t] == 2) hipLaunchKernelGGL((k_prefill<A, 2, MODE>), grid, dim3(256), 0, s, a);
-    }
-  } else {
-    hipLaunchKernelGGL((k_prefill<A, 0, MODE>), grid, dim3(256), 0, s, a);
-  }
+  constexpr int kid = MODE == kRoutedGateUp   ? MOE_K_PREFILL_GATEUP
+                      : MODE == kSharedGateUp ? MOE_K_PREFILL_SHARED_GATEUP
+                      : MODE == kSharedDown   ? MOE_K_PREFILL_SHARED_DOWN
+                                              : MOE_K_PREFILL_DOWN;
+  MOE_LAUNCH(kid, (k_prefill<A, MODE>), grid, dim3(256), 0, s, a);
 }
 
 PArgs make_args(const int32_t* offsets, const int32_t* sorted, const int32_t* tier_map,
@@ -318,11 +320,11 @@ void launch_prefill_down(int act, const int32_t* offsets, const int32_t* sorted_
 }
 
 void launch_cast_out(const float* y_acc, void* y, size_t n, hipStream_t s) {
-  hipLaunchKernelGGL(k_cast_out, dim3(1024), dim3(256), 0, s, y_acc, (bf16_t*)y, n);
+  MOE_LAUNCH(MOE_K_CAST, k_cast_out, dim3(1024), dim3(256), 0, s, y_acc, (bf16_t*)y, n);
 }
 
 void launch_zero(float* p, size_t n, hipStream_t s) {
-  hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, s, p, n);
+  MOE_LAUNCH(MOE_K_ZERO, k_zero, dim3(1024), dim3(256), 0, s, p, n);
 }
 
 }  // namespace moe

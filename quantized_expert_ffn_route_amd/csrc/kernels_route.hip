@@ -79,10 +79,10 @@ void launch_router_keys(int act, const void* x, const void* w, const float* b, d
                         int T, int H, int E, hipStream_t s) {
   dim3 grid((E + 3) / 4, (T + kGroup - 1) / kGroup);
   if (act == MOE_BF16)
-    hipLaunchKernelGGL(k_router_keys<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x,
+    MOE_LAUNCH(MOE_K_ROUTER_KEYS, k_router_keys<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x,
                        (const bf16_t*)w, b, keys, T, H, E);
   else
-    hipLaunchKernelGGL(k_router_keys<float>, grid, dim3(256), 0, s, (const float*)x,
+    MOE_LAUNCH(MOE_K_ROUTER_KEYS, k_router_keys<float>, grid, dim3(256), 0, s, (const float*)x,
                        (const float*)w, b, keys, T, H, E);
 }
 
@@ -181,19 +181,19 @@ __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ keys, 
   }
 }
 
-#define MOE_TOPK_DISPATCH(KERNEL, ...)                                                           \
+#define MOE_TOPK_DISPATCH(KID, KERNEL, ...)                                                      \
   do {                                                                                        \
-    if (E <= 64) hipLaunchKernelGGL(KERNEL<1>, __VA_ARGS__);                                  \
-    else if (E <= 128) hipLaunchKernelGGL(KERNEL<2>, __VA_ARGS__);                            \
-    else if (E <= 256) hipLaunchKernelGGL(KERNEL<4>, __VA_ARGS__);                            \
-    else if (E <= 512) hipLaunchKernelGGL(KERNEL<8>, __VA_ARGS__);                            \
-    else if (E <= 1024) hipLaunchKernelGGL(KERNEL<16>, __VA_ARGS__);                          \
-    else hipLaunchKernelGGL(KERNEL<0>, __VA_ARGS__);                                          \
+    if (E <= 64) MOE_LAUNCH(KID, KERNEL<1>, __VA_ARGS__);                                     \
+    else if (E <= 128) MOE_LAUNCH(KID, KERNEL<2>, __VA_ARGS__);                               \
+    else if (E <= 256) MOE_LAUNCH(KID, KERNEL<4>, __VA_ARGS__);                               \
+    else if (E <= 512) MOE_LAUNCH(KID, KERNEL<8>, __VA_ARGS__);                               \
+    else if (E <= 1024) MOE_LAUNCH(KID, KERNEL<16>, __VA_ARGS__);                             \
+    else MOE_LAUNCH(KID, KERNEL<0>, __VA_ARGS__);                                             \
   } while (0)
 
 void launch_topk(const double* keys, int T, int E, int K, int32_t* ids, float* w, hipStream_t s) {
   dim3 grid((T + 15) / 16);
-  MOE_TOPK_DISPATCH(k_topk, grid, dim3(1024), 0, s, keys, T, E, K, ids, w);
+  MOE_TOPK_DISPATCH(MOE_K_TOPK, k_topk, grid, dim3(1024), 0, s, keys, T, E, K, ids, w);
 }
 
 // ---------------------------------------------------------------------------
@@ -309,7 +309,7 @@ void launch_topk_items(const double* keys, int T, int E, int K, const int32_t* t
                        int32_t* ids, float* w, Item* items, int32_t* n_items, hipStream_t s) {
   const int3 ns = make_int3(n_slots[0], n_slots[1], n_slots[2]);
   const int3 tb = make_int3(tier_bits[0], tier_bits[1], tier_bits[2]);
-  MOE_TOPK_DISPATCH(k_topk_items, dim3(1), dim3(1024), 0, s, keys, T, E, K, tier_map, ns, tb,
+  MOE_TOPK_DISPATCH(MOE_K_TOPK_ITEMS, k_topk_items, dim3(1), dim3(1024), 0, s, keys, T, E, K, tier_map, ns, tb,
                     has_shared, ids, w, items, n_items);
 }
 
@@ -423,10 +423,10 @@ void launch_sort_routes(const int32_t* ids, int T, int K, int E, uint64_t* chunk
                         int32_t* chunk_base, int32_t* offsets, int32_t* sorted_routes,
                         int32_t* route_pos, hipStream_t s) {
   const int n_chunks = (T + 63) / 64;
-  hipLaunchKernelGGL(k_sort_count, dim3(n_chunks), dim3(256), E * sizeof(uint64_t), s, ids, T, K, E,
+  MOE_LAUNCH(MOE_K_SORT_COUNT, k_sort_count, dim3(n_chunks), dim3(256), E * sizeof(uint64_t), s, ids, T, K, E,
                      chunk_mask, chunk_base);
-  hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(1024), 0, s, n_chunks, E, chunk_base, offsets);
-  hipLaunchKernelGGL(k_sort_scatter, dim3(n_chunks), dim3(256), 0, s, ids, T, K, E, chunk_mask,
+  MOE_LAUNCH(MOE_K_SORT_SCAN, k_sort_scan, dim3(1), dim3(1024), 0, s, n_chunks, E, chunk_base, offsets);
+  MOE_LAUNCH(MOE_K_SORT_SCATTER, k_sort_scatter, dim3(n_chunks), dim3(256), 0, s, ids, T, K, E, chunk_mask,
                      chunk_base, sorted_routes, route_pos);
 }
 

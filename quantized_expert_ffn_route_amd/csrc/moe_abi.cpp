@@ -161,9 +161,41 @@ int check_ws(void* ws, size_t* ws_bytes, size_t need, bool* size_only) {
   return MOE_OK;
 }
 
+// Launch errors are read from hipGetLastError(); clear_hip_error() at the
+// start of a launch sequence keeps errors left by unrelated HIP calls of the
+// process from being reported as this library's.
+inline void clear_hip_error() { (void)hipGetLastError(); }
 inline int hip_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+struct Trace {
+  hipEvent_t* events = nullptr;
+  int32_t* tags = nullptr;
+  int32_t capacity = 0;
+  int32_t* n_used = nullptr;
+};
+Trace g_trace;
+
 }  // namespace
+
+namespace moe {
+
+void trace_slot(int kernel_id, hipStream_t s, hipEvent_t* start, hipEvent_t* stop) {
+  Trace& t = g_trace;
+  *start = *stop = nullptr;
+  if (!t.events || *t.n_used >= t.capacity / 2) return;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+    (void)hipGetLastError();  // query unsupported on this stream: not capturing
+    st = hipStreamCaptureStatusNone;
+  }
+  if (st != hipStreamCaptureStatusNone) return;  // no timing events inside graphs
+  const int i = (*t.n_used)++;
+  t.tags[i] = kernel_id;
+  *start = t.events[2 * i];
+  *stop = t.events[2 * i + 1];
+}
+
+}  // namespace moe
 
 extern "C" {
 
@@ -176,6 +208,15 @@ const char* moe_status_string(int status) {
     case MOE_EHIP: return "MOE_EHIP: HIP runtime error";
     default: return "unknown moe_status";
   }
+}
+
+int moe_set_trace(hipEvent_t* events, int32_t* tags, int32_t capacity, int32_t* n_used) {
+  if (events && (capacity < 0 || !tags || !n_used)) return MOE_EINVAL;
+  g_trace.events = events;
+  g_trace.tags = events ? tags : nullptr;
+  g_trace.capacity = events ? capacity : 0;
+  g_trace.n_used = events ? n_used : nullptr;
+  return MOE_OK;
 }
 
 size_t moe_tier_table_bytes(const moe_dims* dims, int32_t bits, int32_t n_slots, int32_t mat,
@@ -349,6 +390,7 @@ int moe_route(const moe_dims* dims, const moe_layer* layer, const void* x, int32
   if ((rc = check_ws(ws, ws_bytes, w.total, &size_only)) || size_only) return rc;
   if (T == 0) return MOE_OK;
   if (!x || !aligned(x, 16) || !topk_ids || !topk_w) return MOE_EINVAL;
+  clear_hip_error();
   char* base = static_cast<char*>(ws);
   double* keys = reinterpret_cast<double*>(base + w.keys);
   launch_router_keys(dims->act, x, layer->w_router, layer->b_router, keys, T, dims->hidden,
@@ -374,6 +416,7 @@ int moe_forward_decode(const moe_dims* dims, const moe_layer* layer, const void*
   if ((rc = check_ws(ws, ws_bytes, w.total, &size_only)) || size_only) return rc;
   if (T == 0) return MOE_OK;
   if (!x || !aligned(x, 16) || !y || !aligned(y, 16)) return MOE_EINVAL;
+  clear_hip_error();
   char* base = static_cast<char*>(ws);
   const int H = dims->hidden, K = dims->top_k, E = dims->n_experts;
   const Tables tb = make_tables(dims, layer);
@@ -418,6 +461,7 @@ int moe_forward_prefill(const moe_dims* dims, const moe_layer* layer, const void
   if ((rc = check_ws(ws, ws_bytes, w.total, &size_only)) || size_only) return rc;
   if (T == 0) return MOE_OK;
   if (!x || !aligned(x, 16) || !y || !aligned(y, 16)) return MOE_EINVAL;
+  clear_hip_error();
   char* base = static_cast<char*>(ws);
   const int H = dims->hidden, I = dims->inter, K = dims->top_k, E = dims->n_experts;
   const Tables tb = make_tables(dims, layer);
