@@ -243,9 +243,10 @@ typedef enum {
   MOE_K_PREFILL_GATEUP = 9,        /* A7: routed grouped gate/up GEMM           */
   MOE_K_PREFILL_SHARED_GATEUP = 10,/* A7: shared expert gate/up GEMM            */
   MOE_K_PREFILL_SHARED_DOWN = 11,  /* A8: shared expert down GEMM (initialises) */
-  MOE_K_PREFILL_DOWN = 12,         /* A8: routed down GEMM + weighted scatter   */
-  MOE_K_CAST = 13,                 /* fp32 accumulator -> bf16 output           */
-  MOE_K_ZERO = 14                  /* zero the fp32 accumulator                 */
+  MOE_K_PREFILL_DOWN = 12,         /* A8: routed down GEMM, fp32 row per route  */
+  MOE_K_ROUTER_APPROX = 13,        /* A1: bf16 MFMA router keys (approximate)   */
+  MOE_K_TOPK_RECHECK = 14,         /* A1+A2: float64 rescoring + exact top-K    */
+  MOE_K_COMBINE = 15               /* A8: shared + weighted routed rows -> y    */
 } moe_kernel_id;
 
 /* Launch trace, for measurement harnesses (not part of the computation).

@@ -39,8 +39,8 @@ MOE_SRC_F32, MOE_SRC_CODES = 0, 1
 KERNEL_NAMES = {
     1: "router_keys", 2: "topk", 3: "topk_items", 4: "decode_gateup", 5: "decode_down",
     6: "sort_count", 7: "sort_scan", 8: "sort_scatter", 9: "prefill_gateup",
-    10: "prefill_shared_gateup", 11: "prefill_shared_down", 12: "prefill_down", 13: "cast",
-    14: "zero",
+    10: "prefill_shared_gateup", 11: "prefill_shared_down", 12: "prefill_down",
+    13: "router_approx", 14: "topk_recheck", 15: "combine",
 }
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

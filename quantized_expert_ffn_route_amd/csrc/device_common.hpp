@@ -176,4 +176,164 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
+// ---------------------------------------------------------------------------
+// Top-K ordering and a DPP wave argmax.
+// ---------------------------------------------------------------------------
+
+// Monotone map of a key to uint64: larger key -> larger value; -0 == +0;
+// NaN maps to 0, below every number.
+__device__ __forceinline__ uint64_t order_key(double k) {
+  if (k != k) return 0ull;
+  if (k == 0.0) k = 0.0;
+  const uint64_t u = (uint64_t)__double_as_longlong(k);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// Inverse of order_key (0 -> NaN).
+__device__ __forceinline__ double key_of_order(uint64_t u) {
+  if (u == 0ull) return __longlong_as_double(0x7FF8000000000000ll);
+  const uint64_t b = (u >> 63) ? (u & 0x7FFFFFFFFFFFFFFFull) : ~u;
+  return __longlong_as_double((long long)b);
+}
+
+// (key descending, id ascending)
+__device__ __forceinline__ bool ranks_before(uint64_t au, uint32_t aid, uint64_t bu, uint32_t bid) {
+  return au > bu || (au == bu && aid < bid);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp_step(uint64_t& u, uint32_t& id) {
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)u);
+  const uint32_t hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+  const uint32_t oid = dpp_u32<CTRL>(id);
+  const uint64_t ou = ((uint64_t)hi << 32) | lo;
+  if (ranks_before(ou, oid, u, id)) {
+    u = ou;
+    id = oid;
+  }
+}
+
+__device__ __forceinline__ void argmax_readlane(uint64_t& bu, uint32_t& bid, uint64_t u, uint32_t id,
+                                                int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  const uint32_t oid = (uint32_t)__builtin_amdgcn_readlane((int)id, lane);
+  const uint64_t ou = ((uint64_t)hi << 32) | lo;
+  if (ranks_before(ou, oid, bu, bid)) {
+    bu = ou;
+    bid = oid;
+  }
+}
+
+// Wave-wide best (key, id) pair: quads, then rows of 16 by two row
+// rotations, then the four rows through readlane.  Returns the same result
+// in every lane.
+__device__ __forceinline__ void wave_argmax(uint64_t& u, uint32_t& id) {
+  argmax_dpp_step<0xB1>(u, id);   // quad_perm [1,0,3,2]
+  argmax_dpp_step<0x4E>(u, id);   // quad_perm [2,3,0,1]
+  argmax_dpp_step<0x124>(u, id);  // row_ror:4
+  argmax_dpp_step<0x128>(u, id);  // row_ror:8
+  uint64_t bu = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 0) << 32) |
+                (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 0);
+  uint32_t bid = (uint32_t)__builtin_amdgcn_readlane((int)id, 0);
+  argmax_readlane(bu, bid, u, id, 16);
+  argmax_readlane(bu, bid, u, id, 32);
+  argmax_readlane(bu, bid, u, id, 48);
+  u = bu;
+  id = bid;
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Sorted-list top-K of one wave.  Each lane holds KPL (key, id) pairs
+// (expert ids lane, lane+64, ...), sorts them once (descending by
+// (key, -id)), and every round takes the wave argmax of the lane heads; the
+// winning lane (ids are unique) shifts its list.  Lanes r < rounds end with
+// the r-th best id in *sel_id and its order key in *sel_u.
+// ---------------------------------------------------------------------------
+
+template <int KPL>
+struct SortedKeys {
+  uint64_t u[KPL];
+  uint32_t id[KPL];
+  __device__ __forceinline__ void cswap(int a, int b) {
+    if (ranks_before(u[b], id[b], u[a], id[a])) {
+      const uint64_t tu = u[a];
+      const uint32_t ti = id[a];
+      u[a] = u[b];
+      id[a] = id[b];
+      u[b] = tu;
+      id[b] = ti;
+    }
+  }
+  __device__ __forceinline__ void sort() {
+    if constexpr (KPL == 2) {
+      cswap(0, 1);
+    } else if constexpr (KPL == 4) {
+      cswap(0, 1); cswap(2, 3); cswap(0, 2); cswap(1, 3); cswap(1, 2);
+    } else if constexpr (KPL == 8) {
+      // 19-comparator optimal network (depth 6)
+      cswap(0, 2); cswap(1, 3); cswap(4, 6); cswap(5, 7);
+      cswap(0, 4); cswap(1, 5); cswap(2, 6); cswap(3, 7);
+      cswap(0, 1); cswap(2, 3); cswap(4, 5); cswap(6, 7);
+      cswap(2, 4); cswap(3, 5);
+      cswap(1, 4); cswap(3, 6);
+      cswap(1, 2); cswap(3, 4); cswap(5, 6);
+    }
+  }
+};
+
+// Mixing weights over the K selected keys (lane r holds key r): softmax in
+// float64, stored fp32.
+__device__ __forceinline__ float topk_weight(double key, int lane, int K) {
+  const double k0 = __shfl(key, 0, 64);
+  const double z = lane < K ? exp(key - k0) : 0.0;
+  const double sum = wave_sum_f64(z);
+  return (float)(z / sum);
+}
+
+template <int KPL>
+__device__ __forceinline__ void topk_sorted(const double* __restrict__ krow, int E, int rounds,
+                                            int lane, int* sel_id, uint64_t* sel_u) {
+  static_assert(KPL == 1 || KPL == 2 || KPL == 4 || KPL == 8, "KPL");
+  SortedKeys<KPL> L;
+#pragma unroll
+  for (int j = 0; j < KPL; j++) {
+    const int e = lane + 64 * j;
+    L.u[j] = e < E ? order_key(krow[e]) : 0ull;
+    L.id[j] = e < E ? (uint32_t)e : 0xFFFFFFFFu;
+  }
+  L.sort();
+  int my_id = -1;
+  uint64_t my_u = 0;
+  for (int r = 0; r < rounds; r++) {
+    uint64_t bu = L.u[0];
+    uint32_t bid = L.id[0];
+    wave_argmax(bu, bid);
+    if (lane == r) {
+      my_id = (int)bid;
+      my_u = bu;
+    }
+    if (L.id[0] == bid) {  // this lane's head won: drop it
+#pragma unroll
+      for (int j = 0; j + 1 < KPL; j++) {
+        L.u[j] = L.u[j + 1];
+        L.id[j] = L.id[j + 1];
+      }
+      L.u[KPL - 1] = 0ull;
+      L.id[KPL - 1] = 0xFFFFFFFFu;
+    }
+  }
+  *sel_id = my_id;
+  *sel_u = my_u;
+}
+
 }  // namespace moe

@@ -75,6 +75,13 @@ void launch_decode_gateup(int act, const Item* items, const int32_t* n_items, in
                           const void* x, int T, const Tables& tb, void* h, int H, int I,
                           hipStream_t s);
 
+// Batch-1 decode (one token): top-K + weights + work items fused with the
+// gate/up of each item (E <= 512, K <= 64).  Items are in rank order.
+void launch_decode1_gateup(int act, const double* keys, int E, int K, const int32_t* tier_map,
+                           const int32_t n_slots[3], const int32_t tier_bits[3], int has_shared,
+                           const void* x, const Tables& tb, void* h, int H, int I, int32_t* ids,
+                           float* w, Item* items, int32_t* n_items, hipStream_t s);
+
 // Decode down + combine: y[t][H] = sum over items of gw * (W_d h).
 void launch_decode_down(int act, int y_dt, const Item* items, const int32_t* n_items,
                         int max_items, const void* h, int T, const Tables& tb, void* y,
@@ -98,21 +105,33 @@ void launch_prefill_gateup(int act, const int32_t* offsets, const int32_t* sorte
 void launch_prefill_shared_gateup(int act, const void* x, int T, const Tables& tb, void* h_s,
                                   int H, int I, hipStream_t s);
 
-// Shared expert down: y_acc[t][H] = W_sd h_s[t] (plain stores, fp32).
-void launch_prefill_shared_down(int act, const void* h_s, int T, const Tables& tb, float* y_acc,
+// Shared expert down: rows[t][H] = W_sd h_s[t] in fp32 (plain stores).
+void launch_prefill_shared_down(int act, const void* h_s, int T, const Tables& tb, float* rows,
                                 int H, int I, hipStream_t s);
 
-// Routed down + weighted scatter: y_acc[t] += g * (W_d h[pos]) (fp32 atomics).
+// Routed down: route_rows[pos][H] = W_d h[pos] in fp32 for every sorted
+// position pos (plain stores; the gate weight is applied by the combine).
 void launch_prefill_down(int act, const int32_t* offsets, const int32_t* sorted_routes,
-                         const int32_t* tier_map, const float* topk_w, int E, int K,
-                         const void* h, const Tables& tb, float* y_acc, int H, int I,
+                         const int32_t* tier_map, int E, int K, const void* h, const Tables& tb,
+                         float* route_rows, int H, int I, hipStream_t s);
+
+// y[t] = shared_rows[t] (if any) + sum_k topk_w[t][k] * route_rows[route_pos[t][k]],
+// summed in k order in fp32, stored in y_dt.
+void launch_combine(int y_dt, const float* shared_rows, const float* route_rows,
+                    const int32_t* route_pos, const float* topk_w, int T, int K, int H, void* y,
+                    hipStream_t s);
+
+// Approximate router keys with bf16 MFMA (bf16 activations only):
+// keys_approx[t][e] = fp32 sum of x[t] * w[e] + b[e]; wnorm2[e] = |w[e]|^2 (fp32).
+void launch_router_approx(const void* x, int T, const void* w_router, const float* bias, int E,
+                          int H, float* keys_approx, float* wnorm2, hipStream_t s);
+
+// Exact top-K from approximate keys (bf16 activations): candidates within the
+// rounding bound of the K-th approximate key are rescored in float64 with the
+// arithmetic of launch_router_keys, then ranked (key desc, id asc).
+void launch_topk_recheck(const void* x, const void* w, const float* bias, const float* approx,
+                         const float* wnorm2, int T, int H, int E, int K, int32_t* ids, float* wts,
                          hipStream_t s);
-
-// y_acc (fp32) -> y in the act dtype (bf16), n elements.
-void launch_cast_out(const float* y_acc, void* y, size_t n, hipStream_t s);
-
-// Zero n floats.
-void launch_zero(float* p, size_t n, hipStream_t s);
 
 // ---- host packer (pack.cpp; no HIP calls) ----
 

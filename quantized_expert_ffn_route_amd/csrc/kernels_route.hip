@@ -38,6 +38,28 @@ __device__ __forceinline__ void load8_f64<float>(const float* p, double* v) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// Same conversion from raw registers (U4 = sizeof(A)/2 uint4 per chunk).
+template <typename A>
+__device__ __forceinline__ void cvt8_f64(const uint4* r, double* v);
+
+template <>
+__device__ __forceinline__ void cvt8_f64<bf16_t>(const uint4* r, double* v) {
+  const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    v[2 * i] = (double)bf16_lo(w[i]);
+    v[2 * i + 1] = (double)bf16_hi(w[i]);
+  }
+}
+
+template <>
+__device__ __forceinline__ void cvt8_f64<float>(const uint4* r, double* v) {
+  v[0] = __uint_as_float(r[0].x); v[1] = __uint_as_float(r[0].y);
+  v[2] = __uint_as_float(r[0].z); v[3] = __uint_as_float(r[0].w);
+  v[4] = __uint_as_float(r[1].x); v[5] = __uint_as_float(r[1].y);
+  v[6] = __uint_as_float(r[1].z); v[7] = __uint_as_float(r[1].w);
+}
+
 template <typename A>
 __global__ __launch_bounds__(256) void k_router_keys(const A* __restrict__ x, const A* __restrict__ w,
                                                      const float* __restrict__ bias,
@@ -75,8 +97,80 @@ __global__ __launch_bounds__(256) void k_router_keys(const A* __restrict__ x, co
   }
 }
 
+// Decode variant (T <= 16, tokens fit in 64 KiB of LDS): the group's tokens
+// are staged in LDS once per workgroup and every lane issues all loads of
+// its router row before the first FMA.  Same per-lane order and butterfly as
+// k_router_keys, so the keys are bit-identical.
+template <typename A, int MAXC>
+__global__ __launch_bounds__(512) void k_router_keys_dec(const A* __restrict__ x,
+                                                         const A* __restrict__ w,
+                                                         const float* __restrict__ bias,
+                                                         double* __restrict__ keys, int T, int H,
+                                                         int E) {
+  extern __shared__ uint4 s_x[];
+  const int n16 = T * H * (int)sizeof(A) / 16;
+  for (int i = threadIdx.x; i < n16; i += blockDim.x) s_x[i] = reinterpret_cast<const uint4*>(x)[i];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 8 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const int nchunk = H / 8;
+  constexpr int U4 = (int)sizeof(A) / 2;     // uint4 per 8-element chunk
+  uint4 wraw[MAXC][U4];
+  const A* wr = w + (size_t)e * H;
+#pragma unroll
+  for (int j = 0; j < MAXC; j++) {
+    const int q = lane + 64 * j;
+    if (q < nchunk)
+#pragma unroll
+      for (int u = 0; u < U4; u++) wraw[j][u] = reinterpret_cast<const uint4*>(wr + 8 * q)[u];
+  }
+  const double b = bias ? (double)bias[e] : 0.0;
+  const A* sxa = reinterpret_cast<const A*>(s_x);
+  for (int t = 0; t < T; t++) {
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < MAXC; j++) {
+      const int q = lane + 64 * j;
+      if (q < nchunk) {
+        double wv[8], xv[8];
+        uint4 xr[U4];
+#pragma unroll
+        for (int u = 0; u < U4; u++) xr[u] = reinterpret_cast<const uint4*>(sxa + (size_t)t * H + 8 * q)[u];
+        cvt8_f64<A>(wraw[j], wv);
+        cvt8_f64<A>(xr, xv);
+#pragma unroll
+        for (int k = 0; k < 8; k++) acc = __builtin_fma(xv[k], wv[k], acc);
+      }
+    }
+    const double sum = wave_sum_f64(acc);
+    if (lane == 0) keys[(size_t)t * E + e] = sum + b;
+  }
+}
+
 void launch_router_keys(int act, const void* x, const void* w, const float* b, double* keys,
                         int T, int H, int E, hipStream_t s) {
+  const size_t xbytes = (size_t)T * H * (act == MOE_BF16 ? 2 : 4);
+  if (T <= kGroup && xbytes <= 65536 && H <= 4096) {
+    dim3 grid((E + 7) / 8);
+    const int maxc = (H / 8 + 63) / 64;
+#define MOE_RK(AT, MC)                                                                          \
+  MOE_LAUNCH(MOE_K_ROUTER_KEYS, (k_router_keys_dec<AT, MC>), grid, dim3(512), xbytes, s,        \
+             (const AT*)x, (const AT*)w, b, keys, T, H, E)
+    if (act == MOE_BF16) {
+      if (maxc <= 1) MOE_RK(bf16_t, 1);
+      else if (maxc <= 2) MOE_RK(bf16_t, 2);
+      else if (maxc <= 4) MOE_RK(bf16_t, 4);
+      else MOE_RK(bf16_t, 8);
+    } else {
+      if (maxc <= 1) MOE_RK(float, 1);
+      else if (maxc <= 2) MOE_RK(float, 2);
+      else if (maxc <= 4) MOE_RK(float, 4);
+      else MOE_RK(float, 8);
+    }
+#undef MOE_RK
+    return;
+  }
   dim3 grid((E + 3) / 4, (T + kGroup - 1) / kGroup);
   if (act == MOE_BF16)
     MOE_LAUNCH(MOE_K_ROUTER_KEYS, k_router_keys<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x,
@@ -90,25 +184,20 @@ void launch_router_keys(int act, const void* x, const void* w, const float* b, d
 // A2: top-K by (key descending, id ascending), one wave per token.
 // ---------------------------------------------------------------------------
 
-// Monotone map of a key to uint64: larger key -> larger value; -0 == +0;
-// NaN maps to 0, below every number.
-__device__ __forceinline__ uint64_t order_key(double k) {
-  if (k != k) return 0ull;
-  if (k == 0.0) k = 0.0;
-  const uint64_t u = (uint64_t)__double_as_longlong(k);
-  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-}
-
-__device__ __forceinline__ bool ranks_before(uint64_t au, uint32_t aid, uint64_t bu, uint32_t bid) {
-  return au > bu || (au == bu && aid < bid);
-}
-
 // Selects the top K of `krow` (E keys) with one wave.  Lane r < K returns the
 // r-th selected id in *sel_id and its key in *sel_key.  KPL keys per lane are
-// kept in registers (E <= 64*KPL); KPL == 0 rescans memory each round.
+// kept in registers (E <= 64*KPL); KPL == 0 rescans memory each round.  Each
+// round picks the best entry ranked after the previous pick with a DPP wave
+// argmax.
 template <int KPL>
 __device__ void topk_wave(const double* __restrict__ krow, int E, int K, int lane, int* sel_id,
                           double* sel_key) {
+  if constexpr (KPL >= 1 && KPL <= 8) {
+    uint64_t su;
+    topk_sorted<KPL>(krow, E, K, lane, sel_id, &su);
+    *sel_key = lane < K ? key_of_order(su) : 0.0;
+    return;
+  }
   uint64_t uk[KPL > 0 ? KPL : 1];
   if constexpr (KPL > 0) {
 #pragma unroll
@@ -117,7 +206,7 @@ __device__ void topk_wave(const double* __restrict__ krow, int E, int K, int lan
       uk[j] = e < E ? order_key(krow[e]) : 0ull;
     }
   }
-  uint64_t last_u = 0;
+  uint64_t last_u = 0, my_u = 0;
   uint32_t last_id = 0;
   int my_id = -1;
   for (int r = 0; r < K; r++) {
@@ -140,30 +229,18 @@ __device__ void topk_wave(const double* __restrict__ krow, int E, int K, int lan
     } else {
       for (int e = lane; e < E; e += 64) consider(order_key(krow[e]), e);
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const uint64_t ou = __shfl_xor(bu, off, 64);
-      const uint32_t oid = __shfl_xor(bid, off, 64);
-      if (ranks_before(ou, oid, bu, bid)) {
-        bu = ou;
-        bid = oid;
-      }
-    }
+    wave_argmax(bu, bid);
     last_u = bu;
     last_id = bid;
-    if (lane == r) my_id = (int)bid;
+    if (lane == r) {
+      my_id = (int)bid;
+      my_u = bu;
+    }
   }
   *sel_id = my_id;
-  *sel_key = (lane < K) ? krow[my_id] : 0.0;
+  *sel_key = lane < K ? key_of_order(my_u) : 0.0;
 }
 
-// Mixing weights over the K selected keys: softmax in float64, stored fp32.
-__device__ __forceinline__ float topk_weight(double key, int lane, int K) {
-  const double k0 = __shfl(key, 0, 64);
-  const double z = lane < K ? exp(key - k0) : 0.0;
-  const double sum = wave_sum_f64(z);
-  return (float)(z / sum);
-}
 
 template <int KPL>
 __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ keys, int T, int E, int K,
@@ -197,6 +274,193 @@ void launch_topk(const double* keys, int T, int E, int K, int32_t* ids, float* w
 }
 
 // ---------------------------------------------------------------------------
+// A1-A2 for many tokens with bf16 activations: certified selection from the
+// bf16-MFMA approximate keys.
+//
+// The MFMA pass gives approx = fp32 sum of the exact bf16 products + bias.
+// With fp32 accumulation over H terms, |approx - key| <= gamma * sum|x_i w_i|
+// + (rounding of the bias add) <= delta, gamma = 1.1 (H + 64) 2^-23 (allows
+// truncating adds), sum|x_i w_i| <= |x| max_e |w_e| (Cauchy-Schwarz).  An
+// expert whose approx is below the K-th largest approx minus 2 delta is beaten
+// exactly by at least K others, so the exact top-K lies among the candidates
+// approx >= approx_K - 2 delta.  The candidates are rescored with the fp64
+// dot of k_router_keys (same per-lane order and butterfly, hence the same
+// keys as decode) and the top K taken by (key desc, id asc).
+// ---------------------------------------------------------------------------
+
+template <int KPL, int MAXC>
+__global__ __launch_bounds__(512) void k_topk_recheck(const bf16_t* __restrict__ x,
+                                                       const bf16_t* __restrict__ w,
+                                                       const float* __restrict__ bias,
+                                                       const float* __restrict__ approx,
+                                                       const float* __restrict__ wnorm2, int T,
+                                                       int H, int E, int K,
+                                                       int32_t* __restrict__ ids,
+                                                       float* __restrict__ wts) {
+  __shared__ int32_t s_cand[8][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 8 + wv;
+  if (t >= T) return;
+  const int nchunk = H / 8;
+  // token row in fp64 registers, canonical chunk order
+  double xv[MAXC][8];
+  double xx = 0.0;
+#pragma unroll
+  for (int j = 0; j < MAXC; j++) {
+    const int q = lane + 64 * j;
+    if (q < nchunk) {
+      load8_f64<bf16_t>(x + (size_t)t * H + 8 * q, xv[j]);
+#pragma unroll
+      for (int k = 0; k < 8; k++) xx = __builtin_fma(xv[j][k], xv[j][k], xx);
+    }
+  }
+  // largest router row norm and largest |approx| of this token
+  float wm = 0.0f, am = 0.0f;
+  float ap[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; j++) {
+    const int e = lane + 64 * j;
+    ap[j] = e < E ? approx[(size_t)t * E + e] : 0.0f;
+    if (e < E) {
+      wm = fmaxf(wm, wnorm2[e]);
+      am = fmaxf(am, fabsf(ap[j]));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    wm = fmaxf(wm, __shfl_xor(wm, off, 64));
+    am = fmaxf(am, __shfl_xor(am, off, 64));
+  }
+  xx = wave_sum_f64(xx);
+  const double gamma = 1.1 * (double)(H + 64) * 0x1.0p-23;
+  const double delta =
+      gamma * sqrt(xx) * sqrt((double)wm * 1.001) + 0x1.0p-21 * ((double)am + 1.0);
+  // K-th largest approximate key
+  SortedKeys<KPL> L;
+#pragma unroll
+  for (int j = 0; j < KPL; j++) {
+    const int e = lane + 64 * j;
+    L.u[j] = e < E ? order_key((double)ap[j]) : 0ull;
+    L.id[j] = e < E ? (uint32_t)e : 0xFFFFFFFFu;
+  }
+  L.sort();
+  uint64_t kth = 0;
+  for (int r = 0; r < K; r++) {
+    uint64_t bu = L.u[0];
+    uint32_t bid = L.id[0];
+    wave_argmax(bu, bid);
+    kth = bu;
+    if (L.id[0] == bid) {
+#pragma unroll
+      for (int j = 0; j + 1 < KPL; j++) {
+        L.u[j] = L.u[j + 1];
+        L.id[j] = L.id[j + 1];
+      }
+      L.u[KPL - 1] = 0ull;
+      L.id[KPL - 1] = 0xFFFFFFFFu;
+    }
+  }
+  const double theta = key_of_order(kth) - 2.0 * delta;
+  // candidates, compacted in ascending expert id
+  int nc = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; j++) {
+    const int e = lane + 64 * j;
+    const bool c = e < E && (double)ap[j] >= theta;
+    const uint64_t m = __ballot(c);
+    if (c) {
+      const int pos = nc + __popcll(m & ((1ull << lane) - 1ull));
+      if (pos < 64) s_cand[wv][pos] = e;
+    }
+    nc += __popcll(m);
+  }
+  // An oversized candidate set, or a non-finite bound (NaN / Inf inputs),
+  // rescores every expert instead.
+  const bool all = nc > 64 || nc < K || !(theta > -INFINITY) || !(delta < INFINITY);
+  const int ncand = all ? E : nc;
+  // rescored key of candidate i lives on lane i % 64, slot i / 64
+  SortedKeys<KPL> C;
+#pragma unroll
+  for (int j = 0; j < KPL; j++) {
+    C.u[j] = 0ull;
+    C.id[j] = 0xFFFFFFFFu;
+  }
+  for (int i = 0; i < ncand; i++) {
+    const int e = all ? i : s_cand[wv][i];
+    const bf16_t* wr = w + (size_t)e * H;
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < MAXC; j++) {
+      const int q = lane + 64 * j;
+      if (q < nchunk) {
+        double w8[8];
+        load8_f64<bf16_t>(wr + 8 * q, w8);
+#pragma unroll
+        for (int k = 0; k < 8; k++) acc = __builtin_fma(xv[j][k], w8[k], acc);
+      }
+    }
+    const double key = wave_sum_f64(acc) + (bias ? (double)bias[e] : 0.0);
+    if (lane == (i & 63)) {
+#pragma unroll
+      for (int j = 0; j < KPL; j++)
+        if (j == (i >> 6)) {
+          C.u[j] = order_key(key);
+          C.id[j] = (uint32_t)e;
+        }
+    }
+  }
+  C.sort();
+  int sid = -1;
+  uint64_t su = 0;
+  for (int r = 0; r < K; r++) {
+    uint64_t bu = C.u[0];
+    uint32_t bid = C.id[0];
+    wave_argmax(bu, bid);
+    if (lane == r) {
+      sid = (int)bid;
+      su = bu;
+    }
+    if (C.id[0] == bid) {
+#pragma unroll
+      for (int j = 0; j + 1 < KPL; j++) {
+        C.u[j] = C.u[j + 1];
+        C.id[j] = C.id[j + 1];
+      }
+      C.u[KPL - 1] = 0ull;
+      C.id[KPL - 1] = 0xFFFFFFFFu;
+    }
+  }
+  const float g = topk_weight(lane < K ? key_of_order(su) : 0.0, lane, K);
+  if (lane < K) {
+    ids[(size_t)t * K + lane] = sid;
+    wts[(size_t)t * K + lane] = g;
+  }
+}
+
+void launch_topk_recheck(const void* x, const void* w, const float* bias, const float* approx,
+                         const float* wnorm2, int T, int H, int E, int K, int32_t* ids, float* wts,
+                         hipStream_t s) {
+  dim3 grid((T + 7) / 8);
+  const int maxc = (H / 8 + 63) / 64;
+#define MOE_RC(KPL, MC)                                                                         \
+  MOE_LAUNCH(MOE_K_TOPK_RECHECK, (k_topk_recheck<KPL, MC>), grid, dim3(512), 0, s,              \
+             (const bf16_t*)x, (const bf16_t*)w, bias, approx, wnorm2, T, H, E, K, ids, wts)
+#define MOE_RC_KPL(MC)                                                                          \
+  do {                                                                                          \
+    if (E <= 64) MOE_RC(1, MC);                                                                 \
+    else if (E <= 128) MOE_RC(2, MC);                                                           \
+    else if (E <= 256) MOE_RC(4, MC);                                                           \
+    else MOE_RC(8, MC);                                                                         \
+  } while (0)
+  if (maxc <= 1) MOE_RC_KPL(1);
+  else if (maxc <= 2) MOE_RC_KPL(2);
+  else if (maxc <= 4) MOE_RC_KPL(4);
+  else MOE_RC_KPL(8);
+#undef MOE_RC_KPL
+#undef MOE_RC
+}
+
+// ---------------------------------------------------------------------------
 // A2 + A3 for a decode group (T <= 16): top-K per token, then the union of
 // chosen experts as work items.  One routing decision reaches every tier:
 // each item carries (tier, slot) = tier_map[expert] (P1, "step 4: three
@@ -217,6 +481,7 @@ __global__ __launch_bounds__(1024) void k_topk_items(const double* __restrict__ 
   __shared__ uint32_t bitmap[kMaxBitmapWords];
   __shared__ int32_t wordbase[kMaxBitmapWords + 1];
   __shared__ int32_t s_id[kGroup * 64];
+  __shared__ int32_t s_tm[kGroup * 64];
   __shared__ float s_w[kGroup * 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nwords = (E + 31) / 32;
@@ -225,12 +490,14 @@ __global__ __launch_bounds__(1024) void k_topk_items(const double* __restrict__ 
     int sid;
     double skey;
     topk_wave<KPL>(keys + (size_t)wv * E, E, K, lane, &sid, &skey);
+    const int tm = lane < K ? tier_map[sid] : 0;       // in flight during the softmax
     const float g = topk_weight(skey, lane, K);
     if (lane < K) {
       ids[wv * K + lane] = sid;
       w[wv * K + lane] = g;
       s_id[wv * K + lane] = sid;
       s_w[wv * K + lane] = g;
+      s_tm[wv * K + lane] = tm;
     }
   }
   __syncthreads();
@@ -258,12 +525,26 @@ __global__ __launch_bounds__(1024) void k_topk_items(const double* __restrict__ 
   }
   __syncthreads();
   const int n_union = wordbase[nwords];
-  // item headers, in ascending expert id
-  for (int e = tid; e < E; e += blockDim.x) {
+  // phase 1: clear the token slots of every item (and fill the shared one)
+  for (int i = tid; i < (n_union + 1) * kGroup; i += blockDim.x) {
+    const int u = i / kGroup, t = i % kGroup;
+    if (u < n_union) {
+      items[u].route[t] = -1;
+      items[u].gw[t] = 0.0f;
+    } else if (has_shared) {
+      items[u].route[t] = t < T ? nroutes + t : -1;
+      items[u].gw[t] = t < T ? 1.0f : 0.0f;
+    }
+  }
+  __syncthreads();
+  // phase 2: each route fills its token slot and (redundantly, same values)
+  // the header of its item; items are in ascending expert id
+  for (int i = tid; i < nroutes; i += blockDim.x) {
+    const int e = s_id[i];
     const uint32_t word = bitmap[e >> 5];
-    if (!((word >> (e & 31)) & 1u)) continue;
     const int u = wordbase[e >> 5] + __popc(word & ((1u << (e & 31)) - 1u));
-    const int tm = tier_map[e];
+    const int t = i / K;
+    const int tm = s_tm[i];
     const int tier = tm >> 16, slot = tm & 0xFFFF;
     const int ns = tier == 0 ? n_slots.x : (tier == 1 ? n_slots.y : n_slots.z);
     const bool ok = tier >= 0 && tier < 3 && slot < ns;
@@ -272,20 +553,8 @@ __global__ __launch_bounds__(1024) void k_topk_items(const double* __restrict__ 
     it.tier = ok ? tier : -1;
     it.slot = ok ? slot : 0;
     it.bits = ok ? (tier == 0 ? tier_bits.x : (tier == 1 ? tier_bits.y : tier_bits.z)) : 0;
-#pragma unroll
-    for (int t = 0; t < kGroup; t++) {
-      it.route[t] = -1;
-      it.gw[t] = 0.0f;
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < nroutes; i += blockDim.x) {
-    const int e = s_id[i];
-    const uint32_t word = bitmap[e >> 5];
-    const int u = wordbase[e >> 5] + __popc(word & ((1u << (e & 31)) - 1u));
-    const int t = i / K;
-    items[u].route[t] = i;
-    items[u].gw[t] = s_w[i];
+    it.route[t] = i;
+    it.gw[t] = s_w[i];
   }
   if (tid == 0) {
     if (has_shared) {
@@ -294,11 +563,6 @@ __global__ __launch_bounds__(1024) void k_topk_items(const double* __restrict__ 
       it.tier = kDenseTier;
       it.slot = 0;
       it.bits = 0;
-#pragma unroll
-      for (int t = 0; t < kGroup; t++) {
-        it.route[t] = t < T ? nroutes + t : -1;
-        it.gw[t] = t < T ? 1.0f : 0.0f;
-      }
     }
     *n_items = n_union + (has_shared ? 1 : 0);
   }

@@ -125,13 +125,26 @@ DecodeWs decode_ws(const moe_dims* d) {
 }
 
 struct PrefillWs {
-  size_t keys, ids, w, chunk_mask, chunk_base, offsets, sorted, route_pos, h, h_s, y_acc, total;
+  size_t keys, approx, wnorm2, ids, w, chunk_mask, chunk_base, offsets, sorted, route_pos, h, h_s,
+      route_rows, shared_rows, total;
 };
-PrefillWs prefill_ws(const moe_dims* d, int64_t T, int y_dt) {
+// The bf16 prefill router: MFMA keys + exact float64 rescoring of the
+// candidates (the recheck kernel holds up to 512 keys per token and H <= 4096
+// in registers; the MFMA pass works on 32-row groups of the router matrix).
+bool mfma_router(const moe_dims* d) {
+  return d->act == MOE_BF16 && d->n_experts <= 512 && d->n_experts % 32 == 0 &&
+         d->top_k <= 64 && d->hidden <= 4096;
+}
+
+PrefillWs prefill_ws(const moe_dims* d, int64_t T) {
   Carve c;
   PrefillWs w;
-  const int64_t K = d->top_k, E = d->n_experts, n_chunks = (T + 63) / 64;
-  w.keys = c.take((size_t)T * E * sizeof(double));
+  const int64_t K = d->top_k, E = d->n_experts, H = d->hidden, n_chunks = (T + 63) / 64;
+  const bool bf16 = mfma_router(d);
+  // float64 keys for fp32 activations; bf16 takes the MFMA keys + recheck
+  w.keys = c.take(bf16 ? 0 : (size_t)T * E * sizeof(double));
+  w.approx = c.take(bf16 ? (size_t)T * E * sizeof(float) : 0);
+  w.wnorm2 = c.take(bf16 ? (size_t)E * sizeof(float) : 0);
   w.ids = c.take((size_t)T * K * sizeof(int32_t));
   w.w = c.take((size_t)T * K * sizeof(float));
   w.chunk_mask = c.take((size_t)n_chunks * E * sizeof(uint64_t));
@@ -141,7 +154,8 @@ PrefillWs prefill_ws(const moe_dims* d, int64_t T, int y_dt) {
   w.route_pos = c.take((size_t)T * K * sizeof(int32_t));
   w.h = c.take((size_t)T * K * d->inter * act_bytes(d->act));
   w.h_s = c.take(d->has_shared ? (size_t)T * d->inter * act_bytes(d->act) : 0);
-  w.y_acc = c.take(y_dt == MOE_F32 ? 0 : (size_t)T * d->hidden * sizeof(float));
+  w.route_rows = c.take((size_t)T * K * H * sizeof(float));
+  w.shared_rows = c.take(d->has_shared ? (size_t)T * H * sizeof(float) : 0);
   w.total = c.off;
   return w;
 }
@@ -432,10 +446,17 @@ int moe_forward_decode(const moe_dims* dims, const moe_layer* layer, const void*
     int32_t* n_items = reinterpret_cast<int32_t*>(base + w.n_items);
     void* h = base + w.h;
     launch_router_keys(dims->act, xg, layer->w_router, layer->b_router, keys, nt, H, E, stream);
-    launch_topk_items(keys, nt, E, K, layer->tier_map, layer->n_slots, layer->tier_bits,
-                      dims->has_shared, ids, wts, items, n_items, stream);
-    launch_decode_gateup(dims->act, items, n_items, nt * K + dims->has_shared, xg, nt, tb, h, H,
-                         dims->inter, stream);
+    if (nt == 1 && E <= 512) {
+      // one token: the top-K is folded into the gate/up kernel
+      launch_decode1_gateup(dims->act, keys, E, K, layer->tier_map, layer->n_slots,
+                            layer->tier_bits, dims->has_shared, xg, tb, h, H, dims->inter, ids,
+                            wts, items, n_items, stream);
+    } else {
+      launch_topk_items(keys, nt, E, K, layer->tier_map, layer->n_slots, layer->tier_bits,
+                        dims->has_shared, ids, wts, items, n_items, stream);
+      launch_decode_gateup(dims->act, items, n_items, nt * K + dims->has_shared, xg, nt, tb, h,
+                           H, dims->inter, stream);
+    }
     launch_decode_down(dims->act, y_dt, items, n_items, w.max_items, h, nt, tb, yg, H,
                        dims->inter, stream);
   }
@@ -456,7 +477,7 @@ int moe_forward_prefill(const moe_dims* dims, const moe_layer* layer, const void
   if (dims->n_experts > 4096) return MOE_EUNSUPPORTED;
   if (T < 0 || (int64_t)T * dims->top_k > INT32_MAX) return MOE_EINVAL;
   if (y_dt != MOE_F32 && y_dt != dims->act) return MOE_EINVAL;
-  const PrefillWs w = prefill_ws(dims, T, y_dt);
+  const PrefillWs w = prefill_ws(dims, T);
   bool size_only;
   if ((rc = check_ws(ws, ws_bytes, w.total, &size_only)) || size_only) return rc;
   if (T == 0) return MOE_OK;
@@ -465,7 +486,6 @@ int moe_forward_prefill(const moe_dims* dims, const moe_layer* layer, const void
   char* base = static_cast<char*>(ws);
   const int H = dims->hidden, I = dims->inter, K = dims->top_k, E = dims->n_experts;
   const Tables tb = make_tables(dims, layer);
-  double* keys = reinterpret_cast<double*>(base + w.keys);
   int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(base + w.ids);
   float* wts = topk_w ? topk_w : reinterpret_cast<float*>(base + w.w);
   int32_t* offsets = expert_offsets ? expert_offsets : reinterpret_cast<int32_t*>(base + w.offsets);
@@ -473,23 +493,31 @@ int moe_forward_prefill(const moe_dims* dims, const moe_layer* layer, const void
   int32_t* route_pos = reinterpret_cast<int32_t*>(base + w.route_pos);
   void* h = base + w.h;
   void* h_s = base + w.h_s;
-  float* y_acc = y_dt == MOE_F32 ? static_cast<float*>(y) : reinterpret_cast<float*>(base + w.y_acc);
+  float* route_rows = reinterpret_cast<float*>(base + w.route_rows);
+  float* shared_rows = dims->has_shared ? reinterpret_cast<float*>(base + w.shared_rows) : nullptr;
 
-  launch_router_keys(dims->act, x, layer->w_router, layer->b_router, keys, T, H, E, stream);
-  launch_topk(keys, T, E, K, ids, wts, stream);
+  if (mfma_router(dims)) {
+    float* approx = reinterpret_cast<float*>(base + w.approx);
+    float* wnorm2 = reinterpret_cast<float*>(base + w.wnorm2);
+    launch_router_approx(x, T, layer->w_router, layer->b_router, E, H, approx, wnorm2, stream);
+    launch_topk_recheck(x, layer->w_router, layer->b_router, approx, wnorm2, T, H, E, K, ids, wts,
+                        stream);
+  } else {
+    double* keys = reinterpret_cast<double*>(base + w.keys);
+    launch_router_keys(dims->act, x, layer->w_router, layer->b_router, keys, T, H, E, stream);
+    launch_topk(keys, T, E, K, ids, wts, stream);
+  }
   launch_sort_routes(ids, T, K, E, reinterpret_cast<uint64_t*>(base + w.chunk_mask),
                      reinterpret_cast<int32_t*>(base + w.chunk_base), offsets, sorted, route_pos,
                      stream);
   launch_prefill_gateup(dims->act, offsets, sorted, layer->tier_map, E, K, x, tb, h, H, I, stream);
   if (dims->has_shared) {
     launch_prefill_shared_gateup(dims->act, x, T, tb, h_s, H, I, stream);
-    launch_prefill_shared_down(dims->act, h_s, T, tb, y_acc, H, I, stream);
-  } else {
-    launch_zero(y_acc, (size_t)T * H, stream);
+    launch_prefill_shared_down(dims->act, h_s, T, tb, shared_rows, H, I, stream);
   }
-  launch_prefill_down(dims->act, offsets, sorted, layer->tier_map, wts, E, K, h, tb, y_acc, H, I,
+  launch_prefill_down(dims->act, offsets, sorted, layer->tier_map, E, K, h, tb, route_rows, H, I,
                       stream);
-  if (y_dt != MOE_F32) launch_cast_out(y_acc, y, (size_t)T * H, stream);
+  launch_combine(y_dt, shared_rows, route_rows, route_pos, wts, T, K, H, y, stream);
   return hip_status();
 }
 

@@ -151,7 +151,18 @@ def test_decode_tiny(tiny):
     check_y(y, ref["y"], "f32", "decode tiny T=8")
 
 
-@pytest.mark.parametrize("T", [1, 5, 16, 21, 40])
+def test_decode_tiny_single_token(tiny):
+    # one token takes the fused top-K + gate/up path
+    for seed in (30, 31, 32):
+        x = synth.tokens(tiny.spec, 1, seed)
+        y, ids, w = run_decode(tiny, x)
+        ref = O.moe_layer(act_f64(x, "f32"), tiny.ol)
+        np.testing.assert_array_equal(ids, ref["ids"])
+        assert np.max(np.abs(w - ref["g"])) <= 1e-6
+        check_y(y, ref["y"], "f32", f"decode tiny T=1 seed {seed}")
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 21, 40])
 def test_decode_mid_ragged(mid, T):
     x = synth.tokens(mid.spec, T, 14 + T)
     y, ids, w = run_decode(mid, x)
@@ -266,6 +277,72 @@ def test_prefill_full_4096_sampled(full):
     sample = [0, 1, 777, 2048, 3000, 4095]
     ref = O.moe_layer(xs, full.ol, tokens=sample, routing=(keys, oids, g))
     check_y(y[sample], O.output_cast(ref["y"], "bf16"), "bf16", "prefill full T=4096 (sampled rows)")
+
+
+def test_prefill_router_ties_take_lower_id():
+    # bf16 prefill ranks from approximate MFMA keys, then rescores the
+    # candidates exactly: duplicated router rows must still tie-break by id
+    def dup(w_r, b):
+        w_r = w_r.copy()
+        b = b.copy()
+        for src, dst in ((3, 17), (3, 29), (8, 9)):
+            w_r[dst] = w_r[src]
+            b[dst] = b[src]
+        b[[3, 17, 29]] += 3.0
+        return w_r, b
+    tl = make_layer(MID, seed=6, router_override=dup)
+    x = synth.tokens(MID, 200, 31)
+    y, ids, w, _, _ = run_prefill(tl, x)
+    ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+    _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, MID.top_k, exact=True)
+    np.testing.assert_array_equal(ids, oids)
+    assert np.all(ids[:, :3] == [3, 17, 29])
+    assert np.max(np.abs(w - g)) <= 1e-6
+    check_y(y, ref["y"], "bf16", "prefill with tied router rows")
+
+
+def test_prefill_router_one_ulp_apart():
+    # router rows that differ in a single element by one bf16 ulp: the fp32
+    # MFMA keys cannot order them reliably, the exact rescoring must
+    def near(w_r, b):
+        w_r = w_r.copy()
+        b = b.copy()
+        for src, dst in ((5, 6), (5, 20), (11, 2)):
+            w_r[dst] = w_r[src]
+            b[dst] = b[src]
+            w_r[dst, dst] = np.uint16(int(w_r[dst, dst]) + 1)   # bf16 bit pattern
+        b[[5, 6, 20]] += 3.0
+        return w_r, b
+    tl = make_layer(MID, seed=7, router_override=near)
+    x = synth.tokens(MID, 256, 32)
+    _, ids, w, _, _ = run_prefill(tl, x)
+    _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, MID.top_k, exact=True)
+    np.testing.assert_array_equal(ids, oids)
+    assert np.max(np.abs(w - g)) <= 1e-6
+
+
+WIDE = synth.LayerSpec(hidden=256, inter=128, n_experts=128, top_k=8, has_shared=False,
+                       act="bf16", n_slots=(32, 64, 32))
+
+
+def test_prefill_router_many_candidates():
+    # 100 identical router rows: more near-K candidates than one wave holds,
+    # which takes the exact rescoring of every expert
+    def many(w_r, b):
+        w_r = w_r.copy()
+        b = b.copy()
+        w_r[:100] = w_r[0]
+        b[:100] = b[0] + 4.0
+        return w_r, b
+    tl = make_layer(WIDE, seed=8, router_override=many)
+    x = synth.tokens(WIDE, 96, 33)
+    y, ids, w, _, _ = run_prefill(tl, x)
+    _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, WIDE.top_k, exact=True)
+    np.testing.assert_array_equal(ids, oids)
+    assert np.all(ids == np.arange(WIDE.top_k))
+    assert np.max(np.abs(w - g)) <= 1e-6
+    ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+    check_y(y, ref["y"], "bf16", "prefill, 100 tied router rows")
 
 
 def test_decode_equals_prefill(mid, full):
