@@ -62,7 +62,8 @@ enum { MOE_CODES = 0, MOE_DM = 1 };
 enum { MOE_SRC_F32 = 0, MOE_SRC_CODES = 1 };
 
 /* Shape of one layer.
- *   hidden (H), inter (I): multiples of 128.  E in [1, 65535].
+ *   hidden (H), inter (I): multiples of 128, H <= 8192 (MOE_EUNSUPPORTED
+ *   otherwise).  E in [1, 65535].
  *   top_k (K) in [1, min(E, 64)].  has_shared: 0 or 1.
  *   act: moe_dtype of the activations x, the router weights, the shared
  *   expert's weights and the intermediate h (bf16 for the full-size layer,

@@ -305,10 +305,17 @@ __device__ __forceinline__ void topk_sorted(const double* __restrict__ krow, int
                                             int lane, int* sel_id, uint64_t* sel_u) {
   static_assert(KPL == 1 || KPL == 2 || KPL == 4 || KPL == 8, "KPL");
   SortedKeys<KPL> L;
+  // unconditional loads (clamped index), so all KPL are in flight at once
+  double kv[KPL];
 #pragma unroll
   for (int j = 0; j < KPL; j++) {
     const int e = lane + 64 * j;
-    L.u[j] = e < E ? order_key(krow[e]) : 0ull;
+    kv[j] = krow[e < E ? e : E - 1];
+  }
+#pragma unroll
+  for (int j = 0; j < KPL; j++) {
+    const int e = lane + 64 * j;
+    L.u[j] = e < E ? order_key(kv[j]) : 0ull;
     L.id[j] = e < E ? (uint32_t)e : 0xFFFFFFFFu;
   }
   L.sort();
@@ -334,6 +341,163 @@ __device__ __forceinline__ void topk_sorted(const double* __restrict__ krow, int
   }
   *sel_id = my_id;
   *sel_u = my_u;
+}
+
+
+// Helpers of the threshold top-K below.
+template <int CTRL>
+__device__ __forceinline__ double dpp_max_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)b), hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
+  return fmax(v, __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Wave-wide maximum of a and of b (all 64 lanes active), the two chains
+// interleaved: quads, rows of 16, then the four rows.
+__device__ __forceinline__ void wave_max2_f64(double& a, double& b) {
+  a = dpp_max_f64<0xB1>(a);  b = dpp_max_f64<0xB1>(b);    // quad_perm [1,0,3,2]
+  a = dpp_max_f64<0x4E>(a);  b = dpp_max_f64<0x4E>(b);    // quad_perm [2,3,0,1]
+  a = dpp_max_f64<0x124>(a); b = dpp_max_f64<0x124>(b);   // row_ror:4
+  a = dpp_max_f64<0x128>(a); b = dpp_max_f64<0x128>(b);   // row_ror:8
+  a = fmax(fmax(readlane_f64(a, 0), readlane_f64(a, 16)), fmax(readlane_f64(a, 32), readlane_f64(a, 48)));
+  b = fmax(fmax(readlane_f64(b, 0), readlane_f64(b, 16)), fmax(readlane_f64(b, 32), readlane_f64(b, 48)));
+}
+
+// Number of keys >= th over the wave (empty slots hold -inf), wave-uniform.
+template <int KPL>
+__device__ __forceinline__ int count_ge(const double (&kv)[KPL], double th) {
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; j++) c += __popcll(__ballot(kv[j] >= th));
+  return c;
+}
+
+// ---------------------------------------------------------------------------
+// Threshold top-K of one wave (E <= 64 * KPL keys, lane l holding ids
+// l + 64 j).  A value threshold is bisected between the smallest and the
+// largest key with ballot counts until between `rounds` and rounds + 8 keys
+// (at most 64) reach it; those candidates are compacted one per lane and each
+// is ranked exactly by (key desc, id asc) against the others, read from the
+// other lanes' registers.  The result equals the sorted-list selection above,
+// which remains the fallback when the field cannot be narrowed to 64 keys
+// (many equal keys) or holds NaN or infinite keys.  `scratch` is 64 slots of
+// LDS owned by this wave.  Lanes r < rounds end with the r-th best id and its
+// order key; the other lanes with -1 and 0.
+// ---------------------------------------------------------------------------
+
+struct TopkSlot {
+  uint64_t u;
+  uint32_t id;
+  uint32_t pad;
+};
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int KPL>
+__device__ __forceinline__ void topk_threshold(const double* __restrict__ krow, int E, int rounds,
+                                               int lane, TopkSlot* __restrict__ scratch,
+                                               int* sel_id, uint64_t* sel_u) {
+  static_assert(KPL == 1 || KPL == 2 || KPL == 4 || KPL == 8, "KPL");
+  double kv[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; j++) {
+    const int e = lane + 64 * j;
+    kv[j] = krow[e < E ? e : E - 1];
+  }
+  double mx = -INFINITY, nmn = -INFINITY;   // max and -min over the valid keys
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < KPL; j++) {
+    const bool ok = lane + 64 * j < E;
+    bad |= ok && !(fabs(kv[j]) < INFINITY);   // NaN or infinite
+    if (!ok) kv[j] = -INFINITY;
+    if (ok) {
+      mx = fmax(mx, kv[j]);
+      nmn = fmax(nmn, -kv[j]);
+    }
+  }
+  bad = __ballot(bad) != 0;
+  const int want = rounds + 8 < 64 ? rounds + 8 : 64;
+  bool found = false;
+  double th = 0.0;
+  if (!bad) {
+    wave_max2_f64(mx, nmn);
+    double lo = -nmn, hi = mx;               // count(>= lo) = E >= rounds
+    if (E <= want) {
+      th = lo;
+      found = true;
+    } else {
+      for (int it = 0; it < 64 && !found; it++) {
+        const double mid = lo + (hi - lo) * 0.5;
+        if (!(mid > lo && mid < hi)) break;   // no room left: equal keys
+        const int c = count_ge<KPL>(kv, mid);
+        if (c < rounds) hi = mid;
+        else if (c > want) lo = mid;
+        else { th = mid; found = true; }
+      }
+      if (!found && count_ge<KPL>(kv, lo) <= 64) {   // ties: take the wider set
+        th = lo;
+        found = true;
+      }
+    }
+  }
+  if (!found) {
+    topk_sorted<KPL>(krow, E, rounds, lane, sel_id, sel_u);
+    return;
+  }
+  // compact the candidates: candidate i goes to lane i
+  int nc = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; j++) {
+    const bool c = kv[j] >= th;
+    const uint64_t m = __ballot(c);
+    if (c) {
+      const int pos = nc + __popcll(m & ((1ull << lane) - 1ull));
+      scratch[pos].u = order_key(kv[j]);
+      scratch[pos].id = (uint32_t)(lane + 64 * j);
+    }
+    nc += __popcll(m);
+  }
+  wave_sync_lds();
+  uint64_t mu = 0;
+  uint32_t mid_ = 0xFFFFFFFFu;
+  if (lane < nc) {
+    mu = scratch[lane].u;
+    mid_ = scratch[lane].id;
+  }
+  // exact rank among the candidates, the others read through readlane
+  int rank = 0;
+  for (int i = 0; i < nc; i++) {
+    const uint32_t ulo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mu, i);
+    const uint32_t uhi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mu >> 32), i);
+    const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)mid_, i);
+    rank += ranks_before(((uint64_t)uhi << 32) | ulo, id, mu, mid_) ? 1 : 0;
+  }
+  wave_sync_lds();
+  if (lane < nc && rank < rounds) {
+    scratch[rank].u = mu;
+    scratch[rank].id = mid_;
+  }
+  wave_sync_lds();
+  if (lane < rounds) {
+    *sel_u = scratch[lane].u;
+    *sel_id = (int)scratch[lane].id;
+  } else {
+    *sel_u = 0;
+    *sel_id = -1;
+  }
+  wave_sync_lds();
 }
 
 }  // namespace moe

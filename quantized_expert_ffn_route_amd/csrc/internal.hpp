@@ -83,9 +83,10 @@ void launch_decode1_gateup(int act, const double* keys, int E, int K, const int3
                            float* w, Item* items, int32_t* n_items, hipStream_t s);
 
 // Decode down + combine: y[t][H] = sum over items of gw * (W_d h).
+// h holds rows [0, h_rows) of the group (staged in LDS when they fit).
 void launch_decode_down(int act, int y_dt, const Item* items, const int32_t* n_items,
-                        int max_items, const void* h, int T, const Tables& tb, void* y,
-                        int H, int I, hipStream_t s);
+                        int max_items, const void* h, int h_rows, int T, const Tables& tb,
+                        void* y, int H, int I, hipStream_t s);
 
 // ---- prefill ----
 

@@ -146,13 +146,18 @@ __device__ __forceinline__ void to_frag(Frag<A>& f, const Raw<A>& r) {
 
 // ---- A5: gate + up + SwiGLU --------------------------------------------------
 //
-// Workgroup = (work item, 16 rows of gate and up); wave w takes the 128-wide
-// super-steps c = w, w + NW, ... (NC of them) of the contraction.  Every load
-// of the wave -- both matrices and the tokens -- is issued before the first
-// dequantisation, so the whole kernel's traffic is in flight at once.
+// Workgroup = (work item, 16-row group of gate and of up).  Wave w takes the
+// 128-wide super-steps c = w, w + NW, ... (NC of them) of the contraction;
+// every load of the wave is issued before the first dequantisation.  The
+// grid of one decode step must be resident in a single round (the work is
+// one round of loads per wave), which fixes the workgroup shape below.
+
+// Waves per gate/up workgroup: with two super-steps per wave two workgroups
+// stay resident per CU, enough for one token's 11 x I/16 workgroups.
+constexpr int kGateUpWaves = 8;
 
 template <typename A, int BITS, int NC>
-__device__ __forceinline__ void gateup_wave(const A* __restrict__ x, int T, int H, int I, int rg,
+__device__ __forceinline__ void gateup_tile(const A* __restrict__ x, int T, int H, int I, int rg,
                                             int tier, int slot, const Tables& tb, int wave, int NW,
                                             int lane, f32x4_t& accg, f32x4_t& accu) {
   const int lm = lane & 15, lg = lane >> 4;
@@ -201,12 +206,78 @@ __device__ __forceinline__ void gateup_wave(const A* __restrict__ x, int T, int 
   }
 }
 
+// Sum the waves' 16x16 gate and up tiles (in wave order) and store
+// act(silu(gate) * up) for the tokens of this workgroup's rows: element i of
+// lane l is token 4 * (l / 16) + i, weight row l % 16; route[i] names the h
+// row of token 4 * (l / 16) + i (-1: token not routed here).
+template <typename A>
+__device__ __forceinline__ void gateup_store(float (*red)[8][64], const f32x4_t& accg,
+                                             const f32x4_t& accu, int wave, int NW, int lane,
+                                             const int rt[4], int T, A* __restrict__ h, int I,
+                                             int rg) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    red[wave][i][lane] = accg[i];
+    red[wave][4 + i][lane] = accu[i];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int lm = lane & 15, lg = lane >> 4;
+  // all partials read first (one LDS round trip), then summed in wave order
+  float pg[kGateUpWaves][4], pu[kGateUpWaves][4];
+#pragma unroll
+  for (int w = 0; w < kGateUpWaves; w++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      pg[w][i] = w < NW ? red[w][i][lane] : 0.f;
+      pu[w][i] = w < NW ? red[w][4 + i][lane] : 0.f;
+    }
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int t = 4 * lg + i;
+    if (t < T && rt[i] >= 0) {
+      float g = 0.f, u = 0.f;
+#pragma unroll
+      for (int w = 0; w < kGateUpWaves; w++) {
+        g += pg[w][i];
+        u += pu[w][i];
+      }
+      store_act<A>(h + (size_t)rt[i] * I + rg * 16 + lm, silu_f32(g) * u);
+    }
+  }
+}
+
+template <typename A, int BITS, int NC>
+__device__ __forceinline__ void gateup_item(float (*red)[8][64], const A* __restrict__ x, int T,
+                                            int H, int I, int rg, int tier, int slot,
+                                            const Tables& tb, int wave, int NW, int lane,
+                                            const int rt[4], A* __restrict__ h) {
+  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  gateup_tile<A, BITS, NC>(x, T, H, I, rg, tier, slot, tb, wave, NW, lane, accg, accu);
+  gateup_store<A>(red, accg, accu, wave, NW, lane, rt, T, h, I, rg);
+}
+
 template <typename A, int NC>
-__global__ __launch_bounds__(1024) void k_decode_gateup(const Item* __restrict__ items,
+__device__ __forceinline__ void gateup_dispatch(float (*red)[8][64], const A* __restrict__ x,
+                                                int T, int H, int I, int rg, int tier, int slot,
+                                                int bits, const Tables& tb, int wave, int NW,
+                                                int lane, const int rt[4], A* __restrict__ h) {
+  if (tier == kDenseTier)
+    gateup_item<A, 0, NC>(red, x, T, H, I, rg, 0, 0, tb, wave, NW, lane, rt, h);
+  else if (bits == 4)
+    gateup_item<A, 4, NC>(red, x, T, H, I, rg, tier, slot, tb, wave, NW, lane, rt, h);
+  else if (bits == 3)
+    gateup_item<A, 3, NC>(red, x, T, H, I, rg, tier, slot, tb, wave, NW, lane, rt, h);
+  else
+    gateup_item<A, 2, NC>(red, x, T, H, I, rg, tier, slot, tb, wave, NW, lane, rt, h);
+}
+
+template <typename A, int NC>
+__global__ __launch_bounds__(64 * kGateUpWaves) void k_decode_gateup(const Item* __restrict__ items,
                                                         const int32_t* __restrict__ n_items,
                                                         const A* __restrict__ x, int T, Tables tb,
                                                         A* __restrict__ h, int H, int I) {
-  __shared__ float red[16][8][64];
+  __shared__ float red[kGateUpWaves][8][64];
   const int nrg = I / 16;
   const int u = blockIdx.x / nrg, rg = blockIdx.x % nrg;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, NW = blockDim.x >> 6;
@@ -216,49 +287,21 @@ __global__ __launch_bounds__(1024) void k_decode_gateup(const Item* __restrict__
   const int slot = items[u].slot, bits = items[u].bits;
   const int4 routes = *reinterpret_cast<const int4*>(&items[u].route[4 * (lane >> 4)]);
   if (u >= n || tier < 0) return;
-  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  if (tier == kDenseTier)
-    gateup_wave<A, 0, NC>(x, T, H, I, rg, 0, 0, tb, wave, NW, lane, accg, accu);
-  else if (bits == 4)
-    gateup_wave<A, 4, NC>(x, T, H, I, rg, tier, slot, tb, wave, NW, lane, accg, accu);
-  else if (bits == 3)
-    gateup_wave<A, 3, NC>(x, T, H, I, rg, tier, slot, tb, wave, NW, lane, accg, accu);
-  else
-    gateup_wave<A, 2, NC>(x, T, H, I, rg, tier, slot, tb, wave, NW, lane, accg, accu);
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    red[wave][i][lane] = accg[i];
-    red[wave][4 + i][lane] = accu[i];
-  }
-  __syncthreads();
-  for (int v = wave; v < 8; v += NW) {  // slot v summed over the waves, in wave order
-    float sum = 0.f;
-    for (int w = 0; w < NW; w++) sum += red[w][v][lane];
-    red[0][v][lane] = sum;
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  const int lm = lane & 15, lg = lane >> 4;
   const int rt[4] = {routes.x, routes.y, routes.z, routes.w};
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int t = 4 * lg + i;
-    if (t < T && rt[i] >= 0)
-      store_act<A>(h + (size_t)rt[i] * I + rg * 16 + lm, silu_f32(red[0][i][lane]) * red[0][4 + i][lane]);
-  }
+  gateup_dispatch<A, NC>(red, x, T, H, I, rg, tier, slot, bits, tb, wave, NW, lane, rt, h);
 }
 
 // ---- A2 + A3 + A5 for one token ----------------------------------------------
 //
 // Batch-1 decode.  Work item u < K is the token's rank-u expert, item K the
 // shared expert, so workgroup (u, rg) needs only the first u + 1 ranks of the
-// top-K: wave 0 runs those rounds on the keys while the other waves prefetch
-// the tier map into LDS, and the shared-expert workgroups skip routing.  The
-// workgroup (K - 1, 0) runs all K rounds and publishes ids, weights and the
-// work items for the down kernel.
+// top-K: wave 0 selects them from the keys while the other waves prefetch the
+// tier map into LDS, and the shared-expert workgroups skip routing.
+// Workgroup (K - 1, 0) selects all K and publishes ids, weights and the work
+// items for the down kernel.
 
 template <typename A, int NC, int KPL>
-__global__ __launch_bounds__(1024) void k_decode1_gateup(const double* __restrict__ keys, int E, int K,
+__global__ __launch_bounds__(64 * kGateUpWaves) void k_decode1_gateup(const double* __restrict__ keys, int E, int K,
                                                          const int32_t* __restrict__ tier_map,
                                                          int3 n_slots, int3 tier_bits, int has_shared,
                                                          const A* __restrict__ x, Tables tb,
@@ -267,9 +310,10 @@ __global__ __launch_bounds__(1024) void k_decode1_gateup(const double* __restric
                                                          float* __restrict__ wts,
                                                          Item* __restrict__ items,
                                                          int32_t* __restrict__ n_items) {
-  __shared__ float red[16][8][64];
+  __shared__ float red[kGateUpWaves][8][64];
   __shared__ int32_t s_tm[4096];
   __shared__ int32_t s_sel;
+  __shared__ TopkSlot s_scr[64];
   const int nrg = I / 16;
   const int u = blockIdx.x / nrg, rg = blockIdx.x % nrg;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, NW = blockDim.x >> 6;
@@ -279,7 +323,7 @@ __global__ __launch_bounds__(1024) void k_decode1_gateup(const double* __restric
     if (wave == 0) {
       int sid;
       uint64_t su;
-      topk_sorted<KPL>(keys, E, writer ? K : u + 1, lane, &sid, &su);
+      topk_threshold<KPL>(keys, E, writer ? K : u + 1, lane, s_scr, &sid, &su);
       if (lane == u) s_sel = sid;
       if (writer) {
         const double key = lane < K ? key_of_order(su) : 0.0;
@@ -323,7 +367,19 @@ __global__ __launch_bounds__(1024) void k_decode1_gateup(const double* __restric
         }
       }
     } else {
-      for (int e = threadIdx.x - 64; e < E; e += blockDim.x - 64) s_tm[e] = tier_map[e];
+      // tier map into LDS; four clamped loads in flight per thread per pass
+      const int nt = blockDim.x - 64;
+      for (int e0 = threadIdx.x - 64; e0 < E; e0 += 4 * nt) {
+        int v[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int e = e0 + j * nt;
+          v[j] = tier_map[e < E ? e : E - 1];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          if (e0 + j * nt < E) s_tm[e0 + j * nt] = v[j];
+      }
     }
     __syncthreads();
     const int tm = s_tm[s_sel];
@@ -336,122 +392,131 @@ __global__ __launch_bounds__(1024) void k_decode1_gateup(const double* __restric
   } else if (!has_shared) {
     return;
   }
-  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  if (tier == kDenseTier)
-    gateup_wave<A, 0, NC>(x, 1, H, I, rg, 0, 0, tb, wave, NW, lane, accg, accu);
-  else if (bits == 4)
-    gateup_wave<A, 4, NC>(x, 1, H, I, rg, tier, slot, tb, wave, NW, lane, accg, accu);
-  else if (bits == 3)
-    gateup_wave<A, 3, NC>(x, 1, H, I, rg, tier, slot, tb, wave, NW, lane, accg, accu);
-  else
-    gateup_wave<A, 2, NC>(x, 1, H, I, rg, tier, slot, tb, wave, NW, lane, accg, accu);
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    red[wave][i][lane] = accg[i];
-    red[wave][4 + i][lane] = accu[i];
-  }
-  __syncthreads();
-  for (int v = wave; v < 8; v += NW) {
-    float sum = 0.f;
-    for (int w = 0; w < NW; w++) sum += red[w][v][lane];
-    red[0][v][lane] = sum;
-  }
-  __syncthreads();
   // token 0 sits in accumulator element 0 of lanes 0..15; its h row is u
-  if (threadIdx.x < 16)
-    store_act<A>(h + (size_t)u * I + rg * 16 + lane, silu_f32(red[0][0][lane]) * red[0][4][lane]);
+  const int rt[4] = {lane < 16 ? u : -1, -1, -1, -1};
+  gateup_dispatch<A, NC>(red, x, 1, H, I, rg, tier, slot, bits, tb, wave, NW, lane, rt, h);
 }
 
 // ---- A6: down + weighted combine --------------------------------------------
 //
-// Workgroup = 16 output rows; its (item, super-step) pairs are dealt to the
-// waves round-robin and processed in batches of kBatch, all loads of a batch
-// issued first.  Each pair's 16x16 partial is scaled by the tokens' weights
-// and added in a fixed order, then the waves are summed in wave order: the
-// result is deterministic (no atomics).
+// Workgroup = (16 output rows, row half): the MFMA tile spans 16 weight
+// rows, and the lanes of the other half's rows carry zero weights, which gives
+// H / 8 workgroups -- one per CU at H = 2048, so every CU streams the same
+// share.  The (item, super-step) pairs are dealt to the waves round-robin and
+// processed in batches of PB, all loads of a batch issued first (for one
+// token's 11 items a single batch).  Each pair's 16x16 partial is scaled by
+// the tokens' weights and added in a fixed order, then the waves are summed in
+// wave order: the result is deterministic (no atomics).
 
-constexpr int kBatch = 2;
+template <typename A, int BITS>
+__device__ __forceinline__ void load_down(Raw<A>& r, const Tables& tb, int t, size_t idx,
+                                          const A* dense) {
+  if constexpr (BITS == 0) load_raw_dense<A>(r, dense);
+  else load_raw<A, BITS>(r, tb.codes[t][MOE_DOWN], tb.dm[t][MOE_DOWN], idx);
+}
 
-template <typename A, typename Y>
+// The work items (and, when they fit, the group's h rows: STAGE) are first
+// copied into LDS in one round trip; each wave then issues the weight loads
+// of its pairs straight from the LDS headers, so only the raw weight words
+// are live in registers while they are in flight.  Without STAGE the A
+// operands are loaded from global memory together with the weights.
+template <typename A, typename Y, int PB, bool STAGE>
 __global__ __launch_bounds__(1024) void k_decode_down(const Item* __restrict__ items,
                                                       const int32_t* __restrict__ n_items,
-                                                      int max_pairs, const A* __restrict__ h, int T,
-                                                      Tables tb, Y* __restrict__ y, int H, int I) {
+                                                      int max_items, const A* __restrict__ h,
+                                                      int h_rows, int T, Tables tb,
+                                                      Y* __restrict__ y, int H, int I) {
   __shared__ float red[16][4][64];
-  const int rg = blockIdx.x;
+  extern __shared__ uint4 s_dyn[];
+  Item* s_items = reinterpret_cast<Item*>(s_dyn);
+  const A* s_h = reinterpret_cast<const A*>(s_dyn + (size_t)max_items * (sizeof(Item) / 16));
+  const int rg = blockIdx.x >> 1, half = blockIdx.x & 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, NW = blockDim.x >> 6;
   const int lm = lane & 15, lg = lane >> 4;
+  const bool mine = (lm >> 3) == half;
   const int nbg = I / 128, nrg = H / 16;
+  {
+    const int nh = max_items * (int)(sizeof(Item) / 16);
+    const int n16 = STAGE ? h_rows * I * (int)sizeof(A) / 16 : 0;
+    const uint4* si = reinterpret_cast<const uint4*>(items);
+    const uint4* sh = reinterpret_cast<const uint4*>(h);
+    for (int i = threadIdx.x; i < nh + n16; i += blockDim.x)
+      s_dyn[i] = i < nh ? si[i] : sh[i - nh];
+  }
   const int npairs = *n_items * nbg;
+  __syncthreads();
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  // the first batch's headers are read in the same trip as the count (the
-  // items array always holds max_items entries)
-  for (int p0 = wave; p0 < max_pairs; p0 += NW * kBatch) {
-    if (p0 >= npairs) break;
-    int tier[kBatch], bits[kBatch], route[kBatch], cc[kBatch];
-    size_t idx[kBatch];
-    float4 gw[kBatch];
-    Raw<A> raw[kBatch];
-    Frag<A> ha[kBatch];
+  for (int p0 = wave; p0 < npairs; p0 += NW * PB) {
+    Raw<A> raw[PB];
+    Frag<A> ha[STAGE ? 1 : PB];
 #pragma unroll
-    for (int j = 0; j < kBatch; j++) {
+    for (int j = 0; j < PB; j++) {
       const int p = p0 + NW * j;
-      tier[j] = -1;
-      if (p < max_pairs) {
-        const int u = p / nbg;
-        cc[j] = p % nbg;
-        const Item& it = items[u];
-        tier[j] = it.tier;
-        bits[j] = it.bits;
-        route[j] = lm < T ? it.route[lm] : -1;
-        gw[j] = *reinterpret_cast<const float4*>(&it.gw[4 * lg]);
-        idx[j] = (((size_t)it.slot * nrg + rg) * nbg + cc[j]) * 64 + lane;
-        if (p >= npairs) tier[j] = -1;
+      if (p >= npairs) continue;
+      const Item& it = s_items[p / nbg];
+      const int c = p % nbg, t = it.tier;
+#pragma unroll
+      for (int i = 0; i < (int)(16 * sizeof(A) / 2); i++) raw[j].v[i] = 0u;
+      if (mine && t >= 0) {
+        const size_t idx = (((size_t)it.slot * nrg + rg) * nbg + c) * 64 + lane;
+        const A* dense = reinterpret_cast<const A*>(tb.dense[MOE_DOWN]) +
+                         (size_t)(rg * 16 + lm) * I + 128 * c + 32 * lg;
+        if (t == kDenseTier) load_down<A, 0>(raw[j], tb, t, idx, dense);
+        else if (it.bits == 4) load_down<A, 4>(raw[j], tb, t, idx, dense);
+        else if (it.bits == 3) load_down<A, 3>(raw[j], tb, t, idx, dense);
+        else load_down<A, 2>(raw[j], tb, t, idx, dense);
+      }
+      if constexpr (!STAGE) {
+        const int r = lm < T ? it.route[lm] : -1;
+        ha[j].load_act(h + (size_t)(r < 0 ? 0 : r) * I + 128 * c + 32 * lg, r >= 0);
       }
     }
 #pragma unroll
-    for (int j = 0; j < kBatch; j++) {
-      const int t = tier[j];
+    for (int j = 0; j < PB; j++) {
+      const int p = p0 + NW * j;
+      if (p >= npairs) continue;
+      const Item& it = s_items[p / nbg];
+      const int c = p % nbg, t = it.tier;
       if (t < 0) continue;
-      if (t == kDenseTier)
-        load_raw_dense<A>(raw[j], reinterpret_cast<const A*>(tb.dense[MOE_DOWN]) +
-                                      (size_t)(rg * 16 + lm) * I + 128 * cc[j] + 32 * lg);
-      else if (bits[j] == 4)
-        load_raw<A, 4>(raw[j], tb.codes[t][MOE_DOWN], tb.dm[t][MOE_DOWN], idx[j]);
-      else if (bits[j] == 3)
-        load_raw<A, 3>(raw[j], tb.codes[t][MOE_DOWN], tb.dm[t][MOE_DOWN], idx[j]);
-      else
-        load_raw<A, 2>(raw[j], tb.codes[t][MOE_DOWN], tb.dm[t][MOE_DOWN], idx[j]);
-      const int r = route[j];
-      ha[j].load_act(h + (size_t)(r < 0 ? 0 : r) * I + 128 * cc[j] + 32 * lg, r >= 0);
-    }
-#pragma unroll
-    for (int j = 0; j < kBatch; j++) {
-      const int t = tier[j];
-      if (t < 0) continue;
+      Frag<A>* hf;
+      if constexpr (STAGE) {
+        const int r = lm < T ? it.route[lm] : -1;
+        ha[0].load_act(s_h + (size_t)(r < 0 ? 0 : r) * I + 128 * c + 32 * lg, r >= 0);
+        hf = &ha[0];
+      } else {
+        hf = &ha[j];
+      }
       Frag<A> b;
       if (t == kDenseTier) to_frag<A, 0>(b, raw[j]);
-      else if (bits[j] == 4) to_frag<A, 4>(b, raw[j]);
-      else if (bits[j] == 3) to_frag<A, 3>(b, raw[j]);
+      else if (it.bits == 4) to_frag<A, 4>(b, raw[j]);
+      else if (it.bits == 3) to_frag<A, 3>(b, raw[j]);
       else to_frag<A, 2>(b, raw[j]);
       const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-      const f32x4_t part = mma_step(ha[j], b, z);
-      acc[0] += gw[j].x * part[0];
-      acc[1] += gw[j].y * part[1];
-      acc[2] += gw[j].z * part[2];
-      acc[3] += gw[j].w * part[3];
+      const f32x4_t part = mma_step(*hf, b, z);
+      const float4 gw = *reinterpret_cast<const float4*>(&it.gw[4 * lg]);
+      acc[0] += gw.x * part[0];
+      acc[1] += gw.y * part[1];
+      acc[2] += gw.z * part[2];
+      acc[3] += gw.w * part[3];
     }
   }
 #pragma unroll
   for (int i = 0; i < 4; i++) red[wave][i][lane] = acc[i];
   __syncthreads();
-  if (wave != 0) return;
+  if (wave != 0 || !mine) return;
+  // all partials read first (one LDS round trip), then summed in wave order
+  float pr[16][4];
+#pragma unroll
+  for (int w = 0; w < 16; w++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) pr[w][i] = w < NW ? red[w][i][lane] : 0.f;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    float sum = 0.f;
-    for (int w = 0; w < NW; w++) sum += red[w][i][lane];
     const int t = 4 * lg + i;
     if (t < T) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 16; w++) sum += pr[w][i];
       Y* out = y + (size_t)t * H + rg * 16 + lm;
       if constexpr (sizeof(Y) == 4) *out = sum; else *out = to_bf16(sum);
     }
@@ -465,8 +530,8 @@ void launch_decode_gateup(int act, const Item* items, const int32_t* n_items, in
                           hipStream_t s) {
   dim3 grid(max_items * (I / 16));
   const int nbg = H / 128;
-  const int nw = nbg < 16 ? nbg : 16;
-  const int nc = (nbg + 15) / 16;
+  const int nw = nbg < kGateUpWaves ? nbg : kGateUpWaves;
+  const int nc = (nbg + kGateUpWaves - 1) / kGateUpWaves;
   dim3 block(64 * nw);
 #define MOE_GU(AT, NC)                                                                       \
   MOE_LAUNCH(MOE_K_DECODE_GATEUP, (k_decode_gateup<AT, NC>), grid, block, 0, s, items, n_items, \
@@ -474,11 +539,13 @@ void launch_decode_gateup(int act, const Item* items, const int32_t* n_items, in
   if (act == MOE_BF16) {
     if (nc <= 1) MOE_GU(bf16_t, 1);
     else if (nc <= 2) MOE_GU(bf16_t, 2);
-    else MOE_GU(bf16_t, 4);
+    else if (nc <= 4) MOE_GU(bf16_t, 4);
+    else MOE_GU(bf16_t, 8);
   } else {
     if (nc <= 1) MOE_GU(float, 1);
     else if (nc <= 2) MOE_GU(float, 2);
-    else MOE_GU(float, 4);
+    else if (nc <= 4) MOE_GU(float, 4);
+    else MOE_GU(float, 8);
   }
 #undef MOE_GU
 }
@@ -489,8 +556,8 @@ void launch_decode1_gateup(int act, const double* keys, int E, int K, const int3
                            float* w, Item* items, int32_t* n_items, hipStream_t s) {
   dim3 grid((K + 1) * (I / 16));
   const int nbg = H / 128;
-  const int nw = nbg < 16 ? nbg : 16;
-  const int nc = (nbg + 15) / 16;
+  const int nw = nbg < kGateUpWaves ? nbg : kGateUpWaves;
+  const int nc = (nbg + kGateUpWaves - 1) / kGateUpWaves;
   dim3 block(64 * (nw < 2 ? 2 : nw));   // wave 0 routes, the others prefetch the tier map
   const int3 ns = make_int3(n_slots[0], n_slots[1], n_slots[2]);
   const int3 tbits = make_int3(tier_bits[0], tier_bits[1], tier_bits[2]);
@@ -508,34 +575,51 @@ void launch_decode1_gateup(int act, const double* keys, int E, int K, const int3
   if (act == MOE_BF16) {
     if (nc <= 1) MOE_G1_KPL(bf16_t, 1);
     else if (nc <= 2) MOE_G1_KPL(bf16_t, 2);
-    else MOE_G1_KPL(bf16_t, 4);
+    else if (nc <= 4) MOE_G1_KPL(bf16_t, 4);
+    else MOE_G1_KPL(bf16_t, 8);
   } else {
     if (nc <= 1) MOE_G1_KPL(float, 1);
     else if (nc <= 2) MOE_G1_KPL(float, 2);
-    else MOE_G1_KPL(float, 4);
+    else if (nc <= 4) MOE_G1_KPL(float, 4);
+    else MOE_G1_KPL(float, 8);
   }
 #undef MOE_G1_KPL
 #undef MOE_G1
 }
 
 void launch_decode_down(int act, int y_dt, const Item* items, const int32_t* n_items,
-                        int max_items, const void* h, int T, const Tables& tb, void* y, int H,
-                        int I, hipStream_t s) {
-  dim3 grid(H / 16);
+                        int max_items, const void* h, int h_rows, int T, const Tables& tb, void* y,
+                        int H, int I, hipStream_t s) {
+  dim3 grid(H / 16 * 2);
   const int pairs = max_items * (I / 128);
   const int nw = pairs < 16 ? pairs : 16;
+  const int per_wave = (pairs + nw - 1) / nw;
   dim3 block(64 * nw);
+  const size_t item_bytes = (size_t)max_items * sizeof(Item);
+  const size_t stage_bytes = (size_t)h_rows * I * (act == MOE_BF16 ? 2 : 4);
+  const bool stage = act == MOE_BF16 && item_bytes + stage_bytes <= 48 * 1024;
+  const size_t lds = item_bytes + (stage ? stage_bytes : 0);
+#define MOE_DN(AT, YT, PB, ST)                                                                 \
+  MOE_LAUNCH(MOE_K_DECODE_DOWN, (k_decode_down<AT, YT, PB, ST>), grid, block, lds, s, items,   \
+             n_items, max_items, (const AT*)h, h_rows, T, tb, (YT*)y, H, I)
+#define MOE_DN_PB(YT, ST)                                                                      \
+  do {                                                                                         \
+    if (per_wave <= 1) MOE_DN(bf16_t, YT, 1, ST);                                              \
+    else if (per_wave <= 2) MOE_DN(bf16_t, YT, 2, ST);                                         \
+    else if (per_wave <= 3 || !ST) MOE_DN(bf16_t, YT, 3, ST);                                  \
+    else MOE_DN(bf16_t, YT, 4, ST);                                                            \
+  } while (0)
   if (act == MOE_BF16) {
-    if (y_dt == MOE_BF16)
-      MOE_LAUNCH(MOE_K_DECODE_DOWN, (k_decode_down<bf16_t, bf16_t>), grid, block, 0, s, items,
-                 n_items, pairs, (const bf16_t*)h, T, tb, (bf16_t*)y, H, I);
-    else
-      MOE_LAUNCH(MOE_K_DECODE_DOWN, (k_decode_down<bf16_t, float>), grid, block, 0, s, items,
-                 n_items, pairs, (const bf16_t*)h, T, tb, (float*)y, H, I);
+    if (y_dt == MOE_BF16) {
+      if (stage) MOE_DN_PB(bf16_t, true); else MOE_DN_PB(bf16_t, false);
+    } else {
+      if (stage) MOE_DN_PB(float, true); else MOE_DN_PB(float, false);
+    }
   } else {
-    MOE_LAUNCH(MOE_K_DECODE_DOWN, (k_decode_down<float, float>), grid, block, 0, s, items,
-               n_items, pairs, (const float*)h, T, tb, (float*)y, H, I);
+    MOE_DN(float, float, 1, false);
   }
+#undef MOE_DN_PB
+#undef MOE_DN
 }
 
 }  // namespace moe

@@ -191,19 +191,25 @@ void launch_router_keys(int act, const void* x, const void* w, const float* b, d
 // argmax.
 template <int KPL>
 __device__ void topk_wave(const double* __restrict__ krow, int E, int K, int lane, int* sel_id,
-                          double* sel_key) {
+                          double* sel_key, TopkSlot* __restrict__ scratch) {
   if constexpr (KPL >= 1 && KPL <= 8) {
     uint64_t su;
-    topk_sorted<KPL>(krow, E, K, lane, sel_id, &su);
+    topk_threshold<KPL>(krow, E, K, lane, scratch, sel_id, &su);
     *sel_key = lane < K ? key_of_order(su) : 0.0;
     return;
   }
   uint64_t uk[KPL > 0 ? KPL : 1];
   if constexpr (KPL > 0) {
+    double kv[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; j++) {   // unconditional loads: all in flight at once
+      const int e = lane + 64 * j;
+      kv[j] = krow[e < E ? e : E - 1];
+    }
 #pragma unroll
     for (int j = 0; j < KPL; j++) {
       const int e = lane + 64 * j;
-      uk[j] = e < E ? order_key(krow[e]) : 0ull;
+      uk[j] = e < E ? order_key(kv[j]) : 0ull;
     }
   }
   uint64_t last_u = 0, my_u = 0;
@@ -245,12 +251,13 @@ __device__ void topk_wave(const double* __restrict__ krow, int E, int K, int lan
 template <int KPL>
 __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ keys, int T, int E, int K,
                                                int32_t* __restrict__ ids, float* __restrict__ w) {
+  __shared__ TopkSlot s_scr[16][64];
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 16 + (threadIdx.x >> 6);
   if (t >= T) return;
   int sid;
   double skey;
-  topk_wave<KPL>(keys + (size_t)t * E, E, K, lane, &sid, &skey);
+  topk_wave<KPL>(keys + (size_t)t * E, E, K, lane, &sid, &skey, s_scr[threadIdx.x >> 6]);
   const float g = topk_weight(skey, lane, K);
   if (lane < K) {
     ids[(size_t)t * K + lane] = sid;
@@ -317,12 +324,19 @@ __global__ __launch_bounds__(512) void k_topk_recheck(const bf16_t* __restrict__
   // largest router row norm and largest |approx| of this token
   float wm = 0.0f, am = 0.0f;
   float ap[KPL];
+  float wn[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; j++) {   // unconditional loads: all in flight at once
+    const int e = lane + 64 * j, ec = e < E ? e : E - 1;
+    ap[j] = approx[(size_t)t * E + ec];
+    wn[j] = wnorm2[ec];
+  }
 #pragma unroll
   for (int j = 0; j < KPL; j++) {
     const int e = lane + 64 * j;
-    ap[j] = e < E ? approx[(size_t)t * E + e] : 0.0f;
+    if (e >= E) ap[j] = 0.0f;
     if (e < E) {
-      wm = fmaxf(wm, wnorm2[e]);
+      wm = fmaxf(wm, wn[j]);
       am = fmaxf(am, fabsf(ap[j]));
     }
   }
@@ -483,13 +497,14 @@ __global__ __launch_bounds__(1024) void k_topk_items(const double* __restrict__ 
   __shared__ int32_t s_id[kGroup * 64];
   __shared__ int32_t s_tm[kGroup * 64];
   __shared__ float s_w[kGroup * 64];
+  __shared__ TopkSlot s_scr[kGroup][64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nwords = (E + 31) / 32;
   for (int i = tid; i < nwords; i += blockDim.x) bitmap[i] = 0u;
   if (wv < T) {
     int sid;
     double skey;
-    topk_wave<KPL>(keys + (size_t)wv * E, E, K, lane, &sid, &skey);
+    topk_wave<KPL>(keys + (size_t)wv * E, E, K, lane, &sid, &skey, s_scr[wv]);
     const int tm = lane < K ? tier_map[sid] : 0;       // in flight during the softmax
     const float g = topk_weight(skey, lane, K);
     if (lane < K) {

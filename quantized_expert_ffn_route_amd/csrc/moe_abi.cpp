@@ -36,7 +36,7 @@ int check_dims(const moe_dims* d) {
   if (d->top_k > d->n_experts || d->top_k > 64) return MOE_EINVAL;
   if (d->has_shared != 0 && d->has_shared != 1) return MOE_EINVAL;
   if (d->act != MOE_F32 && d->act != MOE_BF16) return MOE_EINVAL;
-  if (d->hidden % 128 || d->inter % 128) return MOE_EUNSUPPORTED;
+  if (d->hidden % 128 || d->inter % 128 || d->hidden > 8192) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -457,8 +457,8 @@ int moe_forward_decode(const moe_dims* dims, const moe_layer* layer, const void*
       launch_decode_gateup(dims->act, items, n_items, nt * K + dims->has_shared, xg, nt, tb, h,
                            H, dims->inter, stream);
     }
-    launch_decode_down(dims->act, y_dt, items, n_items, w.max_items, h, nt, tb, yg, H,
-                       dims->inter, stream);
+    launch_decode_down(dims->act, y_dt, items, n_items, nt * K + dims->has_shared, h,
+                       nt * (K + dims->has_shared), nt, tb, yg, H, dims->inter, stream);
   }
   return hip_status();
 }

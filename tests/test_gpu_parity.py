@@ -345,6 +345,27 @@ def test_prefill_router_many_candidates():
     check_y(y, ref["y"], "bf16", "prefill, 100 tied router rows")
 
 
+def test_decode_router_many_ties():
+    # 100 identical router rows: the threshold top-K cannot narrow the field
+    # below 64 candidates and takes the sorted-list path; ids stay exact
+    def many(w_r, b):
+        w_r = w_r.copy()
+        b = b.copy()
+        w_r[:100] = w_r[0]
+        b[:100] = b[0] + 4.0
+        return w_r, b
+    tl = make_layer(WIDE, seed=8, router_override=many)
+    for T in (1, 3):
+        x = synth.tokens(WIDE, T, 40 + T)
+        y, ids, w = run_decode(tl, x)
+        _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, WIDE.top_k, exact=True)
+        np.testing.assert_array_equal(ids, oids)
+        assert np.all(ids == np.arange(WIDE.top_k))
+        assert np.max(np.abs(w - g)) <= 1e-6
+        ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+        check_y(y, ref["y"], "bf16", f"decode T={T}, 100 tied router rows")
+
+
 def test_decode_equals_prefill(mid, full):
     for tl, T in ((mid, 16), (full, 8)):
         x = synth.tokens(tl.spec, T, 22)
