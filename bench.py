@@ -55,6 +55,11 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
     ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run an elementwise copy of 256 MiB (fp32 -> fp32) three times, the "
+                         "known-size reference for HBM byte counters")
+    ap.add_argument("--prof-summary", nargs=3, metavar=("DIR", "COMMAND", "TITLE"),
+                    help="print a markdown summary of a rocprofv3 output directory and exit")
     return ap.parse_args()
 
 
@@ -120,6 +125,33 @@ def make_stack(M, torch, spec, n_layers, seed):
             log(f"built layers 0..{l}")
     torch.cuda.synchronize()
     return d, layers
+
+
+def sources_sha256():
+    """Hash of the library's kernel sources (every file under csrc/)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "quantized_expert_ffn_route_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter record
+    (profiles/hbm_traffic.json), or None when the record is missing or was
+    taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("sources_sha256") != sources_sha256():
+        return None
+    b = rec.get("per_launch_bytes", {}).get(kernel)
+    return None if b is None else int(b["read"] + b["write"])
 
 
 def table_bytes(spec, bits, mat):
@@ -191,8 +223,91 @@ def cpu_baseline(n_tokens, seed):
 
 # ---------------------------------------------------------------------------
 
+def prof_summary(out_dir, command, title):
+    """Markdown summary of rocprofv3 output under out_dir: per-kernel durations
+    (kernel_stats / kernel_trace csv) and, when present, per-dispatch averages
+    of the collected counters (counter_collection csv)."""
+    import csv
+    import glob
+
+    def rows(pattern):
+        out = []
+        for f in sorted(glob.glob(os.path.join(out_dir, "**", pattern), recursive=True)):
+            with open(f, newline="") as fh:
+                out.extend(csv.DictReader(fh))
+        return out
+
+    def short(name):
+        name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+        return name.split("(")[0]
+
+    print(f"# {title}\n")
+    print("Command (repository root in `$R`, run from /tmp with TMPDIR=/tmp):\n")
+    print(f"```\n{command}\n```\n")
+    trace = rows("*kernel_trace.csv")
+    if trace:
+        agg = {}
+        for r in trace:
+            n = r.get("Kernel_Name", "")
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            a = agg.setdefault(short(n), [0, 0.0, 1e30, 0.0, r.get("Grid_Size_X", ""),
+                                          r.get("Workgroup_Size_X", ""), r.get("VGPR_Count", ""),
+                                          r.get("LDS_Block_Size", "")])
+            a[0] += 1
+            a[1] += d
+            a[2] = min(a[2], d)
+            a[3] = max(a[3], d)
+        print("Per-kernel durations (`--kernel-trace`), library kernels:\n")
+        print("| kernel | launches | avg us | min us | max us | grid | wg | vgpr | lds |")
+        print("|---|---|---|---|---|---|---|---|---|")
+        for n, a in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+            if "moe::" not in n:
+                continue
+            print(f"| `{n}` | {a[0]} | {a[1] / a[0]:.2f} | {a[2]:.2f} | {a[3]:.2f} | {a[4]} | {a[5]} "
+                  f"| {a[6]} | {a[7]} |")
+        print()
+    ctr = rows("*counter_collection.csv")
+    if ctr:
+        agg = {}
+        r_name_of = {}
+        for r in ctr:
+            n = short(r.get("Kernel_Name", ""))
+            r_name_of[n] = r.get("Kernel_Name", "")
+            key = (n, r.get("Counter_Name", ""))
+            a = agg.setdefault(key, [0, 0.0])
+            a[0] += 1
+            a[1] += float(r.get("Counter_Value", 0.0))
+        # calibration: the largest elementwise negation (bench --calib-copy, 256 MiB each way)
+        calib = {}
+        for r in ctr:
+            if "neg_kernel" in r.get("Kernel_Name", ""):
+                g = int(r.get("Grid_Size", 0))
+                c = r.get("Counter_Name", "")
+                if g >= calib.get(c, (0, 0.0))[0]:
+                    calib[c] = (g, float(r.get("Counter_Value", 0.0)))
+        factor = {c: (256 * 1024) / v for c, (g, v) in calib.items() if v > 0}
+        print("Counters, average per dispatch (`--pmc`), in KiB as reported; the scaled column "
+              "multiplies by the factor that maps the 256 MiB reference copy (read once, "
+              "written once) onto its true size:\n")
+        for c, f in sorted(factor.items()):
+            print(f"- {c}: reference copy counted {calib[c][1]:.0f} KiB -> factor {f:.4f}")
+        print()
+        print("| kernel | counter | dispatches | avg KiB | scaled bytes per dispatch |")
+        print("|---|---|---|---|---|")
+        for (n, c), a in sorted(agg.items()):
+            if "moe::" not in n:
+                continue
+            v = a[1] / a[0]
+            scaled = f"{v * 1024 * factor[c]:.0f}" if c in factor else "-"
+            print(f"| `{n}` | {c} | {a[0]} | {v:.1f} | {scaled} |")
+        print()
+
+
 def main():
     args = parse()
+    if args.prof_summary:
+        prof_summary(*args.prof_summary)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "single-GPU build: this benchmark runs on exactly one GPU "
                           "(--gpus 1); multi-GPU sharding is not implemented"}))
@@ -267,9 +382,12 @@ def main():
     durs = trace.durations_ms(0)
     ids_host = IDS.cpu().numpy()
     per_kernel = {}
-    for i, (name, ms) in enumerate(durs):
-        g, rem = divmod(i, per_graph)
-        l = rem // 4
+    l = g = -1
+    for name, ms in durs:
+        if name == "router_keys":           # first kernel of every layer call
+            l += 1
+            if l % N_LAYERS == 0:
+                l, g = 0, g + 1
         nbytes = decode_kernel_bytes(spec, layers[l], ids_host[g, l, 0])[name]
         pk = per_kernel.setdefault(name, {"n": 0, "ms": 0.0, "bytes": 0})
         pk["n"] += 1
@@ -285,7 +403,8 @@ def main():
     roofline = None
     if dom:
         roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic("decode_gateup"),
                     "kernel": "k_decode_gateup", "bytes_per_launch": dom["bytes"],
                     "avg_us": dom["avg_us"]}
     layer_bytes = sum(k["bytes"] for k in kernels.values()) if kernels else None
@@ -325,9 +444,18 @@ def main():
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(routed_gu_flops / (gu_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
                          "flops_per_launch": routed_gu_flops, "avg_us": round(gu_us, 2),
-                         "traffic": None},
+                         "traffic": measured_traffic("prefill_gateup")},
         }
         log(f"prefill: {prefill['tokens_per_s']:.0f} tokens/s")
+
+    if args.calib_copy:
+        # known-size reference for the HBM byte counters: 256 MiB read + 256 MiB written
+        src = torch.randn(64 << 20, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
