@@ -404,6 +404,35 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Exact top-`rounds` of nc <= 64 candidates held one per lane (lane i < nc:
+// order key mu, id mid_): each candidate's rank (key desc, id asc) is counted
+// against the others, read from their registers; lane r < rounds ends with
+// the r-th best.  `scratch`: 64 slots of LDS owned by this wave.
+__device__ __forceinline__ void rank_select(uint64_t mu, uint32_t mid_, int nc, int rounds,
+                                            int lane, TopkSlot* __restrict__ scratch,
+                                            int* sel_id, uint64_t* sel_u) {
+  int rank = 0;
+  for (int i = 0; i < nc; i++) {
+    const uint32_t ulo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mu, i);
+    const uint32_t uhi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mu >> 32), i);
+    const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)mid_, i);
+    rank += ranks_before(((uint64_t)uhi << 32) | ulo, id, mu, mid_) ? 1 : 0;
+  }
+  if (lane < nc && rank < rounds) {
+    scratch[rank].u = mu;
+    scratch[rank].id = mid_;
+  }
+  wave_sync_lds();
+  if (lane < rounds) {
+    *sel_u = scratch[lane].u;
+    *sel_id = (int)scratch[lane].id;
+  } else {
+    *sel_u = 0;
+    *sel_id = -1;
+  }
+  wave_sync_lds();
+}
+
 template <int KPL>
 __device__ __forceinline__ void topk_threshold(const double* __restrict__ krow, int E, int rounds,
                                                int lane, TopkSlot* __restrict__ scratch,
@@ -476,28 +505,8 @@ __device__ __forceinline__ void topk_threshold(const double* __restrict__ krow, 
     mu = scratch[lane].u;
     mid_ = scratch[lane].id;
   }
-  // exact rank among the candidates, the others read through readlane
-  int rank = 0;
-  for (int i = 0; i < nc; i++) {
-    const uint32_t ulo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mu, i);
-    const uint32_t uhi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mu >> 32), i);
-    const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)mid_, i);
-    rank += ranks_before(((uint64_t)uhi << 32) | ulo, id, mu, mid_) ? 1 : 0;
-  }
   wave_sync_lds();
-  if (lane < nc && rank < rounds) {
-    scratch[rank].u = mu;
-    scratch[rank].id = mid_;
-  }
-  wave_sync_lds();
-  if (lane < rounds) {
-    *sel_u = scratch[lane].u;
-    *sel_id = (int)scratch[lane].id;
-  } else {
-    *sel_u = 0;
-    *sel_id = -1;
-  }
-  wave_sync_lds();
+  rank_select(mu, mid_, nc, rounds, lane, scratch, sel_id, sel_u);
 }
 
 }  // namespace moe

@@ -92,13 +92,18 @@ void launch_decode_down(int act, int y_dt, const Item* items, const int32_t* n_i
 
 // Stable counting sort of the routes by expert.
 //   chunk_mask: [n_chunks][E] uint64, chunk_base: [n_chunks][E] int32.
+// Also lists the grouped-GEMM tiles: bucket e splits into ceil(n_e /
+// tile_rows) tiles (e, first row inside the bucket), *n_tiles of them
+// (at most E + T * K / tile_rows).
 void launch_sort_routes(const int32_t* ids, int T, int K, int E, uint64_t* chunk_mask,
                         int32_t* chunk_base, int32_t* offsets, int32_t* sorted_routes,
-                        int32_t* route_pos, hipStream_t s);
+                        int32_t* route_pos, int tile_rows, int2* tiles, int32_t* n_tiles,
+                        hipStream_t s);
 
 // Routed gate/up grouped GEMM: for every expert bucket, h[pos][I] for the
 // sorted positions pos of that bucket.
 void launch_prefill_gateup(int act, const int32_t* offsets, const int32_t* sorted_routes,
+                           const int2* tiles, const int32_t* n_tiles, int max_tiles,
                            const int32_t* tier_map, int E, int K, const void* x, const Tables& tb,
                            void* h, int H, int I, hipStream_t s);
 
@@ -113,8 +118,12 @@ void launch_prefill_shared_down(int act, const void* h_s, int T, const Tables& t
 // Routed down: route_rows[pos][H] = W_d h[pos] in fp32 for every sorted
 // position pos (plain stores; the gate weight is applied by the combine).
 void launch_prefill_down(int act, const int32_t* offsets, const int32_t* sorted_routes,
+                         const int2* tiles, const int32_t* n_tiles, int max_tiles,
                          const int32_t* tier_map, int E, int K, const void* h, const Tables& tb,
                          float* route_rows, int H, int I, hipStream_t s);
+
+// Token rows per routed GEMM tile for the activation dtype.
+int prefill_tile_rows(int act);
 
 // y[t] = shared_rows[t] (if any) + sum_k topk_w[t][k] * route_rows[route_pos[t][k]],
 // summed in k order in fp32, stored in y_dt.

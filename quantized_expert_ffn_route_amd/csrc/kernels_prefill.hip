@@ -32,6 +32,8 @@ enum Mode {
 
 struct PArgs {
   const int32_t* offsets;
+  const int2* tiles;         // routed modes: (expert, first row inside its bucket)
+  const int32_t* n_tiles;
   const int32_t* sorted;
   const int32_t* tier_map;
   int E, K, T, H, I;
@@ -48,12 +50,20 @@ constexpr int kThreads = 64 * kWaves;
 
 template <typename A> struct PT;
 template <> struct PT<bf16_t> {
-  static constexpr int ROWS = 128;        // token rows per pass
+  static constexpr int ROWS = 64;         // token rows per pass
   static constexpr int RU = 64 + 4;       // LDS row stride in u32 (128 bf16 + pad)
 };
 template <> struct PT<float> {
   static constexpr int ROWS = 64;
   static constexpr int RU = 128 + 4;
+};
+
+// Token rows per workgroup: 64 keeps a routed workgroup within 128 VGPRs
+// (two resident per CU) and gives the dense modes (router, shared expert)
+// 64 token tiles, enough to fill 256 CUs at a 4096-token prefill.
+template <typename A, int MODE> struct PR {
+  static constexpr int ROWS = (MODE == 0 || MODE == 2 || sizeof(A) == 2) ? PT<A>::ROWS
+                                                                        : PT<A>::ROWS / 2;
 };
 
 template <int MODE> struct MC {
@@ -64,10 +74,11 @@ template <int MODE> struct MC {
   static constexpr int NWG = kWaves * RGW * 16;       // weight rows per workgroup
 };
 
-// Raw weight data of one lane for one super-step (loaded one step ahead).
-template <typename A>
+// Raw weight data of one lane for one super-step (loaded one step ahead):
+// dense, 32 act values; quantised, the code field w[0..3] and dm in v[4].
+template <typename A, int BITS>
 struct BRaw {
-  uint32_t v[16 * sizeof(A) / 2];   // dense: 32 act values; quantised: w[0..3], dm in v[4]
+  uint32_t v[BITS == 0 ? 16 * sizeof(A) / 2 : 5];
 };
 
 // MFMA operand fragment of the weights.
@@ -76,7 +87,7 @@ template <> struct BFrag<bf16_t> { uint32_t v[16]; };
 template <> struct BFrag<float> { float v[32]; };
 
 template <typename A, int BITS>
-__device__ __forceinline__ void load_braw(BRaw<A>& r, const Tables& tb, int tier, int mat, int slot,
+__device__ __forceinline__ void load_braw(BRaw<A, BITS>& r, const Tables& tb, int tier, int mat, int slot,
                                           int R, int C, int rg, int c, int lane, const void* dense) {
   const int lm = lane & 15, lg = lane >> 4;
   if constexpr (BITS == 0) {
@@ -95,7 +106,7 @@ __device__ __forceinline__ void load_braw(BRaw<A>& r, const Tables& tb, int tier
 }
 
 template <typename A, int BITS>
-__device__ __forceinline__ void to_bfrag(BFrag<A>& f, const BRaw<A>& r) {
+__device__ __forceinline__ void to_bfrag(BFrag<A>& f, const BRaw<A, BITS>& r) {
   if constexpr (BITS == 0) {
 #pragma unroll
     for (int i = 0; i < (int)(16 * sizeof(A) / 2); i++) {
@@ -121,7 +132,7 @@ __device__ __forceinline__ void prefill_body(const PArgs& a, int grp, int row0, 
                                              int slot, int nt, uint32_t* __restrict__ sA) {
   using C = MC<MODE>;
   constexpr int NMAT = C::NMAT, RGW = C::RGW;
-  constexpr int ROWS = PT<A>::ROWS, RU = PT<A>::RU;
+  constexpr int ROWS = PR<A, MODE>::ROWS, RU = PT<A>::RU;
   constexpr int MT = ROWS / 16;
   constexpr int PARTS = kThreads / ROWS;                 // threads staging one row
   constexpr int U4 = 128 * (int)sizeof(A) / 16 / PARTS;  // uint4 per staging thread
@@ -139,7 +150,7 @@ __device__ __forceinline__ void prefill_body(const PArgs& a, int grp, int row0, 
     if constexpr (MODE == kRouterApprox) return a.wdense;
     else return a.tb.dense[C::GATEUP ? m : MOE_DOWN];
   };
-  auto load_b = [&](BRaw<A> (&r)[RGW][NMAT], int c) {
+  auto load_b = [&](BRaw<A, BITS> (&r)[RGW][NMAT], int c) {
     if (!active) return;
 #pragma unroll
     for (int q = 0; q < RGW; q++)
@@ -184,14 +195,14 @@ __device__ __forceinline__ void prefill_body(const PArgs& a, int grp, int row0, 
     float wsq[RGW] = {};
 
     uint4 ra[U4];
-    BRaw<A> rb[RGW][NMAT];
+    BRaw<A, BITS> rb[RGW][NMAT];
     __syncthreads();                 // previous pass done with the LDS buffers
     load_a(ra, 0);
     load_b(rb, 0);
     store_a(ra, 0);
     __syncthreads();
     for (int c = 0; c < nbg; c++) {
-      BRaw<A> nb[RGW][NMAT];
+      BRaw<A, BITS> nb[RGW][NMAT];
       const bool more = c + 1 < nbg;
       if (more) {
         load_a(ra, c + 1);
@@ -295,9 +306,9 @@ __device__ __forceinline__ void prefill_body(const PArgs& a, int grp, int row0, 
 }
 
 template <typename A, int MODE>
-__global__ __launch_bounds__(kThreads) void k_prefill(PArgs a) {
+__device__ __forceinline__ void prefill_wg(const PArgs& a) {
   using C = MC<MODE>;
-  constexpr int ROWS = PT<A>::ROWS, RU = PT<A>::RU;
+  constexpr int ROWS = PR<A, MODE>::ROWS, RU = PT<A>::RU;
   __shared__ uint32_t sA[2 * ROWS * RU];
   const int Nr = C::GATEUP ? a.I : (MODE == kRouterApprox ? a.E : a.H);
   const int NT = (Nr + C::NWG - 1) / C::NWG;
@@ -306,11 +317,13 @@ __global__ __launch_bounds__(kThreads) void k_prefill(PArgs a) {
   const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
   const int grp = (j / NT) * 8 + xcd, nt = j % NT;
   if constexpr (C::ROUTED) {
-    if (grp >= a.E) return;
-    const int row0 = a.offsets[grp];
-    const int nrows = a.offsets[grp + 1] - row0;
-    if (nrows == 0) return;
-    const int tm = a.tier_map[grp];
+    if (grp >= *a.n_tiles) return;
+    const int2 tile = a.tiles[grp];
+    const int e = tile.x;
+    const int row0 = a.offsets[e] + tile.y;
+    const int nrows = min(ROWS, a.offsets[e + 1] - row0);
+    if (nrows <= 0) return;
+    const int tm = a.tier_map[e];
     const int tier = tm >> 16, slot = tm & 0xFFFF;
     if (tier < 0 || tier > 2 || slot >= a.tb.n_slots[tier]) return;
     // the tier's code width is uniform over the workgroup
@@ -326,6 +339,17 @@ __global__ __launch_bounds__(kThreads) void k_prefill(PArgs a) {
   }
 }
 
+// bf16: four waves per SIMD (two workgroups per CU); the fp32 variants keep
+// their registers (no spills) at lower occupancy.
+template <int MODE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_prefill_bf16(PArgs a) {
+  prefill_wg<bf16_t, MODE>(a);
+}
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void k_prefill_f32(PArgs a) {
+  prefill_wg<float, MODE>(a);
+}
+
 template <typename A, int MODE>
 void launch_mode(const PArgs& a, int n_groups, hipStream_t s) {
   using C = MC<MODE>;
@@ -337,13 +361,16 @@ void launch_mode(const PArgs& a, int n_groups, hipStream_t s) {
                       : MODE == kSharedDown   ? MOE_K_PREFILL_SHARED_DOWN
                       : MODE == kRoutedDown   ? MOE_K_PREFILL_DOWN
                                               : MOE_K_ROUTER_APPROX;
-  MOE_LAUNCH(kid, (k_prefill<A, MODE>), grid, dim3(kThreads), 0, s, a);
+  if constexpr (sizeof(A) == 2) MOE_LAUNCH(kid, (k_prefill_bf16<MODE>), grid, dim3(kThreads), 0, s, a);
+  else MOE_LAUNCH(kid, (k_prefill_f32<MODE>), grid, dim3(kThreads), 0, s, a);
 }
 
 PArgs make_args(const int32_t* offsets, const int32_t* sorted, const int32_t* tier_map, int E,
                 int K, int T, int H, int I, const void* src, void* dst, const Tables& tb) {
   PArgs a;
   a.offsets = offsets;
+  a.tiles = nullptr;
+  a.n_tiles = nullptr;
   a.sorted = sorted;
   a.tier_map = tier_map;
   a.E = E;
@@ -399,37 +426,50 @@ void launch_router_approx(const void* x, int T, const void* w_router, const floa
   a.wdense = w_router;
   a.bias = bias;
   a.wnorm2 = wnorm2;
-  launch_mode<bf16_t, kRouterApprox>(a, (T + PT<bf16_t>::ROWS - 1) / PT<bf16_t>::ROWS, s);
+  constexpr int R = PR<bf16_t, kRouterApprox>::ROWS;
+  launch_mode<bf16_t, kRouterApprox>(a, (T + R - 1) / R, s);
+}
+
+int prefill_tile_rows(int act) {
+  return act == MOE_BF16 ? PR<bf16_t, kRoutedGateUp>::ROWS : PR<float, kRoutedGateUp>::ROWS;
 }
 
 void launch_prefill_gateup(int act, const int32_t* offsets, const int32_t* sorted_routes,
+                           const int2* tiles, const int32_t* n_tiles, int max_tiles,
                            const int32_t* tier_map, int E, int K, const void* x, const Tables& tb,
                            void* h, int H, int I, hipStream_t s) {
-  const PArgs a = make_args(offsets, sorted_routes, tier_map, E, K, 0, H, I, x, h, tb);
-  if (act == MOE_BF16) launch_mode<bf16_t, kRoutedGateUp>(a, E, s);
-  else launch_mode<float, kRoutedGateUp>(a, E, s);
+  PArgs a = make_args(offsets, sorted_routes, tier_map, E, K, 0, H, I, x, h, tb);
+  a.tiles = tiles;
+  a.n_tiles = n_tiles;
+  if (act == MOE_BF16) launch_mode<bf16_t, kRoutedGateUp>(a, max_tiles, s);
+  else launch_mode<float, kRoutedGateUp>(a, max_tiles, s);
 }
 
 void launch_prefill_shared_gateup(int act, const void* x, int T, const Tables& tb, void* h_s,
                                   int H, int I, hipStream_t s) {
   const PArgs a = make_args(nullptr, nullptr, nullptr, 0, 0, T, H, I, x, h_s, tb);
-  if (act == MOE_BF16) launch_mode<bf16_t, kSharedGateUp>(a, (T + 127) / 128, s);
-  else launch_mode<float, kSharedGateUp>(a, (T + 63) / 64, s);
+  constexpr int RB = PR<bf16_t, kSharedGateUp>::ROWS, RF = PR<float, kSharedGateUp>::ROWS;
+  if (act == MOE_BF16) launch_mode<bf16_t, kSharedGateUp>(a, (T + RB - 1) / RB, s);
+  else launch_mode<float, kSharedGateUp>(a, (T + RF - 1) / RF, s);
 }
 
 void launch_prefill_shared_down(int act, const void* h_s, int T, const Tables& tb, float* rows,
                                 int H, int I, hipStream_t s) {
   const PArgs a = make_args(nullptr, nullptr, nullptr, 0, 0, T, H, I, h_s, rows, tb);
-  if (act == MOE_BF16) launch_mode<bf16_t, kSharedDown>(a, (T + 127) / 128, s);
-  else launch_mode<float, kSharedDown>(a, (T + 63) / 64, s);
+  if (act == MOE_BF16) launch_mode<bf16_t, kSharedDown>(a, (T + PR<bf16_t, kSharedDown>::ROWS - 1) / PR<bf16_t, kSharedDown>::ROWS, s);
+  else launch_mode<float, kSharedDown>(a, (T + PR<float, kSharedDown>::ROWS - 1) / PR<float, kSharedDown>::ROWS, s);
 }
 
+
 void launch_prefill_down(int act, const int32_t* offsets, const int32_t* sorted_routes,
+                         const int2* tiles, const int32_t* n_tiles, int max_tiles,
                          const int32_t* tier_map, int E, int K, const void* h, const Tables& tb,
                          float* route_rows, int H, int I, hipStream_t s) {
-  const PArgs a = make_args(offsets, sorted_routes, tier_map, E, K, 0, H, I, h, route_rows, tb);
-  if (act == MOE_BF16) launch_mode<bf16_t, kRoutedDown>(a, E, s);
-  else launch_mode<float, kRoutedDown>(a, E, s);
+  PArgs a = make_args(offsets, sorted_routes, tier_map, E, K, 0, H, I, h, route_rows, tb);
+  a.tiles = tiles;
+  a.n_tiles = n_tiles;
+  if (act == MOE_BF16) launch_mode<bf16_t, kRoutedDown>(a, max_tiles, s);
+  else launch_mode<float, kRoutedDown>(a, max_tiles, s);
 }
 
 void launch_combine(int y_dt, const float* shared_rows, const float* route_rows,

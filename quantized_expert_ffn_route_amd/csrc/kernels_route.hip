@@ -295,6 +295,36 @@ void launch_topk(const double* keys, int T, int E, int K, int32_t* ids, float* w
 // keys as decode) and the top K taken by (key desc, id asc).
 // ---------------------------------------------------------------------------
 
+// Largest value over the wave (float, all 64 lanes active).
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x124>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x128>(__float_as_uint(v))));
+  return fmaxf(fmaxf(__uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0)),
+                     __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 16))),
+               fmaxf(__uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 32)),
+                     __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 48))));
+}
+
+// The float64 key of expert e for the token held in xv (canonical chunk order,
+// identical arithmetic to k_router_keys / k_router_keys_dec).
+template <int MAXC>
+__device__ __forceinline__ double lane_dot_f64(const double (&xv)[MAXC][8], const uint4 (&wr)[MAXC],
+                                               int lane, int nchunk) {
+  double acc = 0.0;
+#pragma unroll
+  for (int j = 0; j < MAXC; j++) {
+    if (lane + 64 * j < nchunk) {
+      double w8[8];
+      cvt8_f64<bf16_t>(&wr[j], w8);
+#pragma unroll
+      for (int k = 0; k < 8; k++) acc = __builtin_fma(xv[j][k], w8[k], acc);
+    }
+  }
+  return acc;
+}
+
 template <int KPL, int MAXC>
 __global__ __launch_bounds__(512) void k_topk_recheck(const bf16_t* __restrict__ x,
                                                        const bf16_t* __restrict__ w,
@@ -305,77 +335,80 @@ __global__ __launch_bounds__(512) void k_topk_recheck(const bf16_t* __restrict__
                                                        int32_t* __restrict__ ids,
                                                        float* __restrict__ wts) {
   __shared__ int32_t s_cand[8][64];
+  __shared__ TopkSlot s_scr[8][64];
+  __shared__ double s_keys[8][64 * KPL];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 8 + wv;
   if (t >= T) return;
   const int nchunk = H / 8;
-  // token row in fp64 registers, canonical chunk order
+  // token row in fp64 registers, canonical chunk order; approximate keys
   double xv[MAXC][8];
-  double xx = 0.0;
+  {
+    uint4 xr[MAXC];
 #pragma unroll
-  for (int j = 0; j < MAXC; j++) {
-    const int q = lane + 64 * j;
-    if (q < nchunk) {
-      load8_f64<bf16_t>(x + (size_t)t * H + 8 * q, xv[j]);
-#pragma unroll
-      for (int k = 0; k < 8; k++) xx = __builtin_fma(xv[j][k], xv[j][k], xx);
+    for (int j = 0; j < MAXC; j++) {
+      const int q = lane + 64 * j;
+      xr[j] = reinterpret_cast<const uint4*>(x + (size_t)t * H)[q < nchunk ? q : 0];
     }
-  }
-  // largest router row norm and largest |approx| of this token
-  float wm = 0.0f, am = 0.0f;
-  float ap[KPL];
-  float wn[KPL];
 #pragma unroll
-  for (int j = 0; j < KPL; j++) {   // unconditional loads: all in flight at once
+    for (int j = 0; j < MAXC; j++) cvt8_f64<bf16_t>(&xr[j], xv[j]);
+  }
+  float ap[KPL], wn[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; j++) {
     const int e = lane + 64 * j, ec = e < E ? e : E - 1;
     ap[j] = approx[(size_t)t * E + ec];
     wn[j] = wnorm2[ec];
   }
+  double xx = 0.0;
+#pragma unroll
+  for (int j = 0; j < MAXC; j++)
+    if (lane + 64 * j < nchunk)
+#pragma unroll
+      for (int k = 0; k < 8; k++) xx = __builtin_fma(xv[j][k], xv[j][k], xx);
+  float wm = 0.0f, am = 0.0f, amx = -INFINITY, nmn = -INFINITY;
+  bool bad = false;
 #pragma unroll
   for (int j = 0; j < KPL; j++) {
-    const int e = lane + 64 * j;
-    if (e >= E) ap[j] = 0.0f;
-    if (e < E) {
+    const bool ok = lane + 64 * j < E;
+    bad |= ok && !(fabsf(ap[j]) < INFINITY);
+    if (ok) {
       wm = fmaxf(wm, wn[j]);
       am = fmaxf(am, fabsf(ap[j]));
+      amx = fmaxf(amx, ap[j]);
+      nmn = fmaxf(nmn, -ap[j]);
+    } else {
+      ap[j] = -INFINITY;
     }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    wm = fmaxf(wm, __shfl_xor(wm, off, 64));
-    am = fmaxf(am, __shfl_xor(am, off, 64));
-  }
+  bad = __ballot(bad) != 0;
+  wm = wave_max_f32(wm);
+  am = wave_max_f32(am);
+  amx = wave_max_f32(amx);
+  nmn = wave_max_f32(nmn);
   xx = wave_sum_f64(xx);
   const double gamma = 1.1 * (double)(H + 64) * 0x1.0p-23;
   const double delta =
       gamma * sqrt(xx) * sqrt((double)wm * 1.001) + 0x1.0p-21 * ((double)am + 1.0);
-  // K-th largest approximate key
-  SortedKeys<KPL> L;
+  // a value th <= the K-th largest approximate key: bisect until between K
+  // and K + 8 keys reach it (or keep the smallest key)
+  float th = -nmn;
+  if (!bad && E > K + 8) {
+    float lo = -nmn, hi = amx;
+    for (int it = 0; it < 40; it++) {
+      const float mid = lo + (hi - lo) * 0.5f;
+      if (!(mid > lo && mid < hi)) break;
+      int c = 0;
 #pragma unroll
-  for (int j = 0; j < KPL; j++) {
-    const int e = lane + 64 * j;
-    L.u[j] = e < E ? order_key((double)ap[j]) : 0ull;
-    L.id[j] = e < E ? (uint32_t)e : 0xFFFFFFFFu;
-  }
-  L.sort();
-  uint64_t kth = 0;
-  for (int r = 0; r < K; r++) {
-    uint64_t bu = L.u[0];
-    uint32_t bid = L.id[0];
-    wave_argmax(bu, bid);
-    kth = bu;
-    if (L.id[0] == bid) {
-#pragma unroll
-      for (int j = 0; j + 1 < KPL; j++) {
-        L.u[j] = L.u[j + 1];
-        L.id[j] = L.id[j + 1];
-      }
-      L.u[KPL - 1] = 0ull;
-      L.id[KPL - 1] = 0xFFFFFFFFu;
+      for (int j = 0; j < KPL; j++) c += __popcll(__ballot(ap[j] >= mid));
+      if (c < K) hi = mid;
+      else if (c > K + 8) lo = mid;
+      else { lo = mid; break; }
     }
+    th = lo;
   }
-  const double theta = key_of_order(kth) - 2.0 * delta;
-  // candidates, compacted in ascending expert id
+  // candidates: approximate key within 2 delta of th (ascending id)
+  const double theta = (double)th - 2.0 * delta;
   int nc = 0;
 #pragma unroll
   for (int j = 0; j < KPL; j++) {
@@ -388,61 +421,54 @@ __global__ __launch_bounds__(512) void k_topk_recheck(const bf16_t* __restrict__
     }
     nc += __popcll(m);
   }
-  // An oversized candidate set, or a non-finite bound (NaN / Inf inputs),
-  // rescores every expert instead.
-  const bool all = nc > 64 || nc < K || !(theta > -INFINITY) || !(delta < INFINITY);
+  // an oversized candidate set, or non-finite inputs, rescore every expert
+  const bool all = bad || nc > 64 || nc < K || !(theta > -INFINITY) || !(delta < INFINITY);
   const int ncand = all ? E : nc;
-  // rescored key of candidate i lives on lane i % 64, slot i / 64
-  SortedKeys<KPL> C;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // rescore, CB candidate rows in flight at a time; candidate i's key ends
+  // in lane i (all: in s_keys)
+  constexpr int CB = MAXC >= 8 ? 2 : 4;
+  uint64_t mu = 0;
+  uint32_t mid_ = 0xFFFFFFFFu;
+  for (int i0 = 0; i0 < ncand; i0 += CB) {
+    uint4 wr[CB][MAXC];
+    int ee[CB];
 #pragma unroll
-  for (int j = 0; j < KPL; j++) {
-    C.u[j] = 0ull;
-    C.id[j] = 0xFFFFFFFFu;
-  }
-  for (int i = 0; i < ncand; i++) {
-    const int e = all ? i : s_cand[wv][i];
-    const bf16_t* wr = w + (size_t)e * H;
-    double acc = 0.0;
+    for (int c = 0; c < CB; c++) {
+      const int i = i0 + c < ncand ? i0 + c : ncand - 1;
+      ee[c] = all ? i : s_cand[wv][i];
+      const uint4* row = reinterpret_cast<const uint4*>(w + (size_t)ee[c] * H);
 #pragma unroll
-    for (int j = 0; j < MAXC; j++) {
-      const int q = lane + 64 * j;
-      if (q < nchunk) {
-        double w8[8];
-        load8_f64<bf16_t>(wr + 8 * q, w8);
-#pragma unroll
-        for (int k = 0; k < 8; k++) acc = __builtin_fma(xv[j][k], w8[k], acc);
+      for (int j = 0; j < MAXC; j++) {
+        const int q = lane + 64 * j;
+        wr[c][j] = row[q < nchunk ? q : 0];
       }
     }
-    const double key = wave_sum_f64(acc) + (bias ? (double)bias[e] : 0.0);
-    if (lane == (i & 63)) {
 #pragma unroll
-      for (int j = 0; j < KPL; j++)
-        if (j == (i >> 6)) {
-          C.u[j] = order_key(key);
-          C.id[j] = (uint32_t)e;
-        }
+    for (int c = 0; c < CB; c++) {
+      const int i = i0 + c;
+      if (i >= ncand) break;
+      const double key = wave_sum_f64(lane_dot_f64<MAXC>(xv, wr[c], lane, nchunk)) +
+                         (bias ? (double)bias[ee[c]] : 0.0);
+      if (all) {
+        if (lane == 0) s_keys[wv][i] = key;
+      } else if (lane == i) {
+        mu = order_key(key);
+        mid_ = (uint32_t)ee[c];
+      }
     }
   }
-  C.sort();
-  int sid = -1;
-  uint64_t su = 0;
-  for (int r = 0; r < K; r++) {
-    uint64_t bu = C.u[0];
-    uint32_t bid = C.id[0];
-    wave_argmax(bu, bid);
-    if (lane == r) {
-      sid = (int)bid;
-      su = bu;
-    }
-    if (C.id[0] == bid) {
-#pragma unroll
-      for (int j = 0; j + 1 < KPL; j++) {
-        C.u[j] = C.u[j + 1];
-        C.id[j] = C.id[j + 1];
-      }
-      C.u[KPL - 1] = 0ull;
-      C.id[KPL - 1] = 0xFFFFFFFFu;
-    }
+  int sid;
+  uint64_t su;
+  if (all) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    topk_threshold<KPL>(s_keys[wv], E, K, lane, s_scr[wv], &sid, &su);
+  } else {
+    rank_select(mu, mid_, nc, K, lane, s_scr[wv], &sid, &su);
   }
   const float g = topk_weight(lane < K ? key_of_order(su) : 0.0, lane, K);
   if (lane < K) {
@@ -625,55 +651,108 @@ __global__ __launch_bounds__(256) void k_sort_count(const int32_t* __restrict__ 
   }
 }
 
-// One block: per-expert totals over chunks, exclusive scan over experts,
-// then per-chunk bases.  chunk_base holds the counts on entry.
-__global__ __launch_bounds__(1024) void k_sort_scan(int n_chunks, int E, int32_t* __restrict__ chunk_base,
-                                                    int32_t* __restrict__ offsets) {
+// Bucket offsets (exclusive scan of the per-expert totals), each chunk's
+// base inside every bucket, and the GEMM tile list: bucket e splits into
+// ceil(n_e / tile_rows) tiles, recorded as (e, first row of the tile inside
+// the bucket) in expert order.  chunk_base holds the counts on entry.  One
+// workgroup; E <= 4096.
+__global__ __launch_bounds__(1024) void k_sort_scan(int n_chunks, int E, int tile_rows,
+                                                    int32_t* __restrict__ chunk_base,
+                                                    int32_t* __restrict__ offsets,
+                                                    int2* __restrict__ tiles,
+                                                    int32_t* __restrict__ n_tiles) {
   __shared__ int32_t s_tot[4096];
-  __shared__ int32_t s_wave[16];
+  __shared__ int32_t s_til[4096];
+  __shared__ int32_t s_wave[16][2];
+  __shared__ int32_t s_total;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // per-expert totals over the chunks, 8 loads in flight per thread
   for (int e = tid; e < E; e += blockDim.x) {
     int sum = 0;
-    for (int c = 0; c < n_chunks; c++) sum += chunk_base[(size_t)c * E + e];
+    for (int c0 = 0; c0 < n_chunks; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int c = c0 + j < n_chunks ? c0 + j : n_chunks - 1;
+        v[j] = chunk_base[(size_t)c * E + e];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        if (c0 + j < n_chunks) sum += v[j];
+    }
     s_tot[e] = sum;
+    s_til[e] = (sum + tile_rows - 1) / tile_rows;
   }
   __syncthreads();
-  // exclusive scan of s_tot[0..E) with 1024 threads, 4 consecutive per thread
-  int v[4];
-  int local = 0;
+  // exclusive scans of s_tot and s_til, 4 consecutive experts per thread
+  int v[4], u[4];
+  int local = 0, ulocal = 0;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int e = tid * 4 + j;
     v[j] = e < E ? s_tot[e] : 0;
+    u[j] = e < E ? s_til[e] : 0;
     local += v[j];
+    ulocal += u[j];
   }
-  int incl = local;
+  int incl = local, uincl = ulocal;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
+    const int uo = __shfl_up(uincl, off, 64);
+    if (lane >= off) {
+      incl += o;
+      uincl += uo;
+    }
   }
-  if (lane == 63) s_wave[wv] = incl;
+  if (lane == 63) {
+    s_wave[wv][0] = incl;
+    s_wave[wv][1] = uincl;
+  }
   __syncthreads();
-  int wbase = 0;
-  for (int i = 0; i < wv; i++) wbase += s_wave[i];
-  int run = wbase + incl - local;
+  int wbase = 0, ubase = 0;
+  for (int i = 0; i < wv; i++) {
+    wbase += s_wave[i][0];
+    ubase += s_wave[i][1];
+  }
+  int run = wbase + incl - local, urun = ubase + uincl - ulocal;
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int e = tid * 4 + j;
-    if (e < E) s_tot[e] = run;
+    if (e < E) {
+      s_tot[e] = run;
+      s_til[e] = urun;
+    }
     run += v[j];
+    urun += u[j];
   }
-  if (tid == blockDim.x - 1) offsets[E] = run;
+  if (tid == blockDim.x - 1) {
+    offsets[E] = run;
+    *n_tiles = urun;
+    s_total = run;
+  }
   __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) {
-    int base = s_tot[e];
-    offsets[e] = base;
-    for (int c = 0; c < n_chunks; c++) {
-      const int cnt = chunk_base[(size_t)c * E + e];
-      chunk_base[(size_t)c * E + e] = base;
-      base += cnt;
+    const int base0 = s_tot[e];
+    offsets[e] = base0;
+    const int n_e = (e + 1 < E ? s_tot[e + 1] : s_total) - base0;
+    for (int p = 0; p * tile_rows < n_e; p++) tiles[s_til[e] + p] = make_int2(e, p * tile_rows);
+    int base = base0;
+    for (int c0 = 0; c0 < n_chunks; c0 += 8) {
+      int cnt[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int c = c0 + j < n_chunks ? c0 + j : n_chunks - 1;
+        cnt[j] = chunk_base[(size_t)c * E + e];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        if (c0 + j < n_chunks) {
+          chunk_base[(size_t)(c0 + j) * E + e] = base;
+          base += cnt[j];
+        }
+      }
     }
   }
 }
@@ -700,11 +779,13 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict_
 
 void launch_sort_routes(const int32_t* ids, int T, int K, int E, uint64_t* chunk_mask,
                         int32_t* chunk_base, int32_t* offsets, int32_t* sorted_routes,
-                        int32_t* route_pos, hipStream_t s) {
+                        int32_t* route_pos, int tile_rows, int2* tiles, int32_t* n_tiles,
+                        hipStream_t s) {
   const int n_chunks = (T + 63) / 64;
   MOE_LAUNCH(MOE_K_SORT_COUNT, k_sort_count, dim3(n_chunks), dim3(256), E * sizeof(uint64_t), s, ids, T, K, E,
                      chunk_mask, chunk_base);
-  MOE_LAUNCH(MOE_K_SORT_SCAN, k_sort_scan, dim3(1), dim3(1024), 0, s, n_chunks, E, chunk_base, offsets);
+  MOE_LAUNCH(MOE_K_SORT_SCAN, k_sort_scan, dim3(1), dim3(1024), 0, s, n_chunks, E, tile_rows,
+             chunk_base, offsets, tiles, n_tiles);
   MOE_LAUNCH(MOE_K_SORT_SCATTER, k_sort_scatter, dim3(n_chunks), dim3(256), 0, s, ids, T, K, E, chunk_mask,
                      chunk_base, sorted_routes, route_pos);
 }

@@ -125,8 +125,9 @@ DecodeWs decode_ws(const moe_dims* d) {
 }
 
 struct PrefillWs {
-  size_t keys, approx, wnorm2, ids, w, chunk_mask, chunk_base, offsets, sorted, route_pos, h, h_s,
-      route_rows, shared_rows, total;
+  size_t keys, approx, wnorm2, ids, w, chunk_mask, chunk_base, offsets, tiles, n_tiles, sorted,
+      route_pos, h, h_s, route_rows, shared_rows, total;
+  int max_tiles;
 };
 // The bf16 prefill router: MFMA keys + exact float64 rescoring of the
 // candidates (the recheck kernel holds up to 512 keys per token and H <= 4096
@@ -150,6 +151,10 @@ PrefillWs prefill_ws(const moe_dims* d, int64_t T) {
   w.chunk_mask = c.take((size_t)n_chunks * E * sizeof(uint64_t));
   w.chunk_base = c.take((size_t)n_chunks * E * sizeof(int32_t));
   w.offsets = c.take((size_t)(E + 1) * sizeof(int32_t));
+  const int64_t rows = prefill_tile_rows(d->act);
+  w.max_tiles = (int)(E + (T * K + rows - 1) / rows);
+  w.tiles = c.take((size_t)w.max_tiles * 2 * sizeof(int32_t));
+  w.n_tiles = c.take(sizeof(int32_t));
   w.sorted = c.take((size_t)T * K * sizeof(int32_t));
   w.route_pos = c.take((size_t)T * K * sizeof(int32_t));
   w.h = c.take((size_t)T * K * d->inter * act_bytes(d->act));
@@ -507,16 +512,19 @@ int moe_forward_prefill(const moe_dims* dims, const moe_layer* layer, const void
     launch_router_keys(dims->act, x, layer->w_router, layer->b_router, keys, T, H, E, stream);
     launch_topk(keys, T, E, K, ids, wts, stream);
   }
+  int2* tiles = reinterpret_cast<int2*>(base + w.tiles);
+  int32_t* n_tiles = reinterpret_cast<int32_t*>(base + w.n_tiles);
   launch_sort_routes(ids, T, K, E, reinterpret_cast<uint64_t*>(base + w.chunk_mask),
                      reinterpret_cast<int32_t*>(base + w.chunk_base), offsets, sorted, route_pos,
-                     stream);
-  launch_prefill_gateup(dims->act, offsets, sorted, layer->tier_map, E, K, x, tb, h, H, I, stream);
+                     prefill_tile_rows(dims->act), tiles, n_tiles, stream);
+  launch_prefill_gateup(dims->act, offsets, sorted, tiles, n_tiles, w.max_tiles, layer->tier_map,
+                        E, K, x, tb, h, H, I, stream);
   if (dims->has_shared) {
     launch_prefill_shared_gateup(dims->act, x, T, tb, h_s, H, I, stream);
     launch_prefill_shared_down(dims->act, h_s, T, tb, shared_rows, H, I, stream);
   }
-  launch_prefill_down(dims->act, offsets, sorted, layer->tier_map, E, K, h, tb, route_rows, H, I,
-                      stream);
+  launch_prefill_down(dims->act, offsets, sorted, tiles, n_tiles, w.max_tiles, layer->tier_map, E,
+                      K, h, tb, route_rows, H, I, stream);
   launch_combine(y_dt, shared_rows, route_rows, route_pos, wts, T, K, H, y, stream);
   return hip_status();
 }
