@@ -121,6 +121,28 @@ struct SinkBf16 {
   __device__ __forceinline__ void operator()(int j, float lo, float hi) { v[j] = pack_bf16(lo, hi); }
 };
 
+// Sink that keeps only pairs 4K .. 4K + 3 of a block (the 8 codes of MFMA
+// k-step K), as packed bf16; the other pairs are dead code once inlined.
+template <int K>
+struct SinkBf16Step {
+  uint32_t v[4];
+  __device__ __forceinline__ void operator()(int j, float lo, float hi) {
+    if ((j >> 2) == K) v[j & 3] = pack_bf16(lo, hi);
+  }
+};
+
+// The bf16 MFMA operand words of k-step k (0..3) of one block.
+template <int BITS>
+__device__ __forceinline__ void dequant_kstep(int k, const uint32_t* w, uint32_t dm,
+                                              uint32_t (&out)[4]) {
+  switch (k) {
+    case 0: { SinkBf16Step<0> s; dequant_block<BITS>(w, dm, s); for (int i = 0; i < 4; i++) out[i] = s.v[i]; break; }
+    case 1: { SinkBf16Step<1> s; dequant_block<BITS>(w, dm, s); for (int i = 0; i < 4; i++) out[i] = s.v[i]; break; }
+    case 2: { SinkBf16Step<2> s; dequant_block<BITS>(w, dm, s); for (int i = 0; i < 4; i++) out[i] = s.v[i]; break; }
+    default: { SinkBf16Step<3> s; dequant_block<BITS>(w, dm, s); for (int i = 0; i < 4; i++) out[i] = s.v[i]; break; }
+  }
+}
+
 // Sink that keeps fp32 values (fp32 activations).
 struct SinkF32 {
   float v[32];

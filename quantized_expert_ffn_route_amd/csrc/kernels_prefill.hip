@@ -4,16 +4,25 @@
 //
 // A workgroup of 8 waves owns 128 weight rows (gate/up: 16 rows of gate and
 // of up per wave) or 256 weight rows (down, router: 32 rows per wave) of one
-// expert, and walks that expert's bucket of routes in passes of up to ROWS
-// token rows.  For each 128-wide slice of the contraction axis the gathered
-// token rows are staged once in LDS (double-buffered, rows padded to 272
-// bytes so the fragment reads are bank-conflict free) and shared by the
-// waves.  Every lane dequantises its own weight blocks straight into MFMA
-// operand registers and reuses them for all token tiles of the pass; both the
-// next slice's token rows and the next weight blocks are loaded while the
-// current slice is multiplied.  The down projection writes one fp32 row per
-// route; the combine kernel then sums each token's K rows in rank order on
-// top of the shared expert's output -- no atomics, deterministic.  The pages'
+// expert and one tile of that expert's bucket of routes.  Every lane
+// dequantises its own weight blocks straight into MFMA operand registers,
+// one MFMA k-step at a time, and reuses them for all token tiles of the
+// tile.  Dequantisation is vector-ALU work that shares the SIMD's issue
+// slots with the MFMAs, so a routed bf16 tile holds 96 token rows: about one
+// whole bucket at the usual prefill load, so that each weight block is
+// dequantised once per expert.
+//
+// Routed bf16 tiles: the gathered token rows of each 128-wide slice of the
+// contraction axis go from global memory straight into LDS (one 16-byte
+// direct-to-LDS load per lane and piece) through a three-stage ring, two
+// slices ahead; weight blocks are loaded one slice ahead into registers.
+// The K loop is unrolled at compile time, so every wait is an exact count of
+// the loads still allowed in flight.  The other cases (dense weights, fp32
+// activations, odd shapes) stage the token rows through registers into a
+// double-buffered LDS tile (rows padded so the fragment reads are
+// bank-conflict free).  The down projection writes one fp32 row per route;
+// the combine kernel then sums each token's K rows in rank order on top of
+// the shared expert's output -- no atomics, deterministic.  The pages'
 // prefill path is the weak spot of the consumer-GPU build (P1, "speed vs
 // context, and the 256k profile").
 #include "device_common.hpp"
@@ -169,20 +178,23 @@ __device__ __forceinline__ void prefill_body(const PArgs& a, int grp, int row0, 
       if constexpr (MODE == kRoutedGateUp) srcrow = a.sorted[row0 + pass0 + srow] / a.K;
       else srcrow = row0 + pass0 + srow;
     }
+    // thread (srow, spart) moves 16-byte pieces spart, spart + PARTS, ... of
+    // its row: the PARTS threads of a row cover contiguous 16 * PARTS bytes per
+    // step, in global memory and in LDS (no bank conflicts on the store)
     auto load_a = [&](uint4 (&r)[U4], int c) {
       if (srcrow >= 0) {
-        const uint4* q = reinterpret_cast<const uint4*>(src + (size_t)srcrow * Kc + 128 * c) + spart * U4;
+        const uint4* q = reinterpret_cast<const uint4*>(src + (size_t)srcrow * Kc + 128 * c) + spart;
 #pragma unroll
-        for (int i = 0; i < U4; i++) r[i] = q[i];
+        for (int i = 0; i < U4; i++) r[i] = q[PARTS * i];
       } else {
 #pragma unroll
         for (int i = 0; i < U4; i++) r[i] = make_uint4(0u, 0u, 0u, 0u);
       }
     };
     auto store_a = [&](const uint4 (&r)[U4], int buf) {
-      uint32_t* d = sA + buf * ROWS * RU + srow * RU + spart * U4 * 4;
+      uint32_t* d = sA + buf * ROWS * RU + srow * RU + spart * 4;
 #pragma unroll
-      for (int i = 0; i < U4; i++) *reinterpret_cast<uint4*>(d + 4 * i) = r[i];
+      for (int i = 0; i < U4; i++) *reinterpret_cast<uint4*>(d + 4 * PARTS * i) = r[i];
     };
 
     f32x4_t acc[RGW][NMAT][MT];
@@ -305,11 +317,200 @@ __device__ __forceinline__ void prefill_body(const PArgs& a, int grp, int row0, 
   }
 }
 
-template <typename A, int MODE>
+// ---------------------------------------------------------------------------
+// bf16 routed grouped GEMM with a deeper pipeline.  The 64 x 128 token tile of a
+// chunk goes from global memory straight into LDS (global_load_lds_dwordx4:
+// every lane gathers one 16-byte piece of a token row, the wave's 64 pieces
+// land contiguously), through a ring of three stages; in LDS, piece p of row
+// r sits at position p ^ (r & 15), so the fragment reads of 8 consecutive
+// rows hit distinct banks.  Weight fragments are prefetched two chunks ahead
+// in three register slots (the chunk loop is unrolled by three, so the slots
+// rotate without copies).  Per chunk: wait for the chunk's own loads (issued
+// two chunks earlier), one barrier, issue the loads two chunks ahead, then
+// dequantise and multiply.
+// ---------------------------------------------------------------------------
+
+constexpr int kStages = 3;
+// Routed bf16 tiles: 96 token rows, so that one tile holds a whole expert
+// bucket at the usual prefill load (about 80 routes per expert at 4096 tokens,
+// top-10 of 512) and each weight block is dequantised once per expert.
+constexpr int kTileRows = 96;
+constexpr int kPieces = kTileRows * 16;           // 16-byte pieces per stage
+constexpr int kStagePieces = kPieces;
+
+// s_waitcnt with vmcnt(n) (expcnt, lgkmcnt left at their maxima), n < 64.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// One 16-byte piece per lane from global memory straight into LDS: lane i's
+// piece lands at lds + 16 i (lds is wave-uniform).  The ring stages are
+// distinct LDS objects, so the compiler's wait tracking tells them apart and
+// adds no drain before LDS reads; completion of a stage is awaited explicitly
+// (vmcnt, then a barrier) before any wave reads it.
+__device__ __forceinline__ void lds_dma16(const void* g, const void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Barrier for LDS hand-over only: waits for this wave's LDS operations, not
+// for its outstanding global loads (which __syncthreads would drain).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The whole K loop is unrolled at compile time (NBG chunks), so the stage,
+// the weight register slot and the exact wait of every step are constants and
+// the code is straight-line (the compiler's own waits then stay precise too).
+template <int BITS, int MODE, int NBG>
+__device__ __forceinline__ void prefill_body_lds(const PArgs& a, int grp, int row0, int nrows,
+                                                 int tier, int slot, int nt,
+                                                 uint4* __restrict__ s0, uint4* __restrict__ s1,
+                                                 uint4* __restrict__ s2) {
+  using A = bf16_t;
+  using C = MC<MODE>;
+  constexpr int NMAT = C::NMAT, RGW = C::RGW;
+  constexpr int MT = kTileRows / 16;
+  constexpr int LA = kPieces / kThreads;                          // A loads per wave per chunk
+  constexpr int LB = RGW * NMAT * (BITS == 0 ? 2 * (int)sizeof(A) : 2);  // B loads per wave per chunk
+  const int Kc = MODE == kRoutedDown || MODE == kSharedDown ? a.I : a.H;
+  const int Nr = C::GATEUP ? a.I : (MODE == kRouterApprox ? a.E : a.H);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lm = lane & 15, lg = lane >> 4;
+  const A* src = reinterpret_cast<const A*>(a.src);
+  const int n0 = nt * C::NWG + wave * RGW * 16;
+  // routed modes: the weight rows are a multiple of the workgroup's rows, so
+  // every wave is active (a compile-time fact keeps the loads unconditional)
+  const bool active = C::ROUTED || n0 < Nr;
+  const int rows_here = min(kTileRows, nrows);
+  const int ntiles = (rows_here + 15) / 16;
+
+  // this lane's pieces: LA of them, LDS slot (LA * wave + j) * 64 + lane
+  const A* arow[LA];
+#pragma unroll
+  for (int j = 0; j < LA; j++) {
+    const int sidx = (LA * wave + j) * 64 + lane;
+    const int r = sidx >> 4, p = sidx & 15;
+    const int lp = p ^ (r & 15);                                  // logical piece
+    const int rr = r < rows_here ? r : 0;                         // rows past the tile: any valid row
+    int srcrow;
+    if constexpr (MODE == kRoutedGateUp) srcrow = a.sorted[row0 + rr] / a.K;
+    else srcrow = row0 + rr;
+    arow[j] = src + (size_t)srcrow * Kc + 8 * lp;
+  }
+  auto load_a = [&](int c, uint4* __restrict__ st) {
+#pragma unroll
+    for (int j = 0; j < LA; j++) lds_dma16(arow[j] + 128 * c, st + (LA * wave + j) * 64);
+  };
+  auto load_b = [&](BRaw<A, BITS> (&r)[RGW][NMAT], int c) {
+#pragma unroll
+    for (int q = 0; q < RGW; q++)
+#pragma unroll
+      for (int m = 0; m < NMAT; m++) {
+        if (C::ROUTED || active)
+          load_braw<A, BITS>(r[q][m], a.tb, tier, C::GATEUP ? m : MOE_DOWN, slot, Nr, Kc,
+                             n0 / 16 + q, c, lane, nullptr);
+      }
+  };
+
+  f32x4_t acc[RGW][NMAT][MT];
+#pragma unroll
+  for (int q = 0; q < RGW; q++)
+#pragma unroll
+    for (int m = 0; m < NMAT; m++)
+#pragma unroll
+      for (int t = 0; t < MT; t++) acc[q][m][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // one MFMA k-step at a time: dequantise its 8 codes of every weight block,
+  // then multiply all token tiles (8 operand registers live instead of 32)
+  auto compute = [&](const uint4* __restrict__ st, const BRaw<A, BITS> (&rb)[RGW][NMAT]) {
+    static_assert(BITS != 0 && C::ROUTED, "quantised routed weights");
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      uint32_t bq[RGW][NMAT][4];
+#pragma unroll
+      for (int q = 0; q < RGW; q++)
+#pragma unroll
+        for (int m = 0; m < NMAT; m++) dequant_kstep<BITS>(i, rb[q][m].v, rb[q][m].v[4], bq[q][m]);
+#pragma unroll
+      for (int t = 0; t < MT; t++) {
+        if (t >= ntiles) break;
+        const uint4 av = st[(16 * t + lm) * 16 + ((4 * lg + i) ^ lm)];
+#pragma unroll
+        for (int q = 0; q < RGW; q++)
+#pragma unroll
+          for (int m = 0; m < NMAT; m++)
+            acc[q][m][t] = mfma_bf16(av.x, av.y, av.z, av.w, bq[q][m][0], bq[q][m][1],
+                                     bq[q][m][2], bq[q][m][3], acc[q][m][t]);
+      }
+    }
+  };
+
+  // token rows run two chunks ahead (three LDS stages), weight blocks one
+  // chunk ahead (two register slots); step c issues B(c + 1) before A(c + 2),
+  // so at the start of step c the newest loads are B(c) then A(c + 1)
+  BRaw<A, BITS> b0[RGW][NMAT], b1[RGW][NMAT];
+  load_a(0, s0);
+  load_b(b0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (NBG > 1) load_a(1, s1);
+  auto step = [&](int c, const uint4* __restrict__ st, uint4* __restrict__ st2,
+                  const BRaw<A, BITS> (&cur)[RGW][NMAT], BRaw<A, BITS> (&nxt)[RGW][NMAT]) {
+    if (c + 1 < NBG) wait_vmcnt<LA>();   // A(c + 1) may stay in flight
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (c + 1 < NBG) load_b(nxt, c + 1);
+    // keep the issue order: the waits above count on the A pieces being the
+    // newest loads in flight
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 2 < NBG) load_a(c + 2, st2);
+    compute(st, cur);
+  };
+#pragma unroll
+  for (int c = 0; c < NBG; c += 6) {
+    step(c, s0, s2, b0, b1);
+    if (c + 1 < NBG) step(c + 1, s1, s0, b1, b0);
+    if (c + 2 < NBG) step(c + 2, s2, s1, b0, b1);
+    if (c + 3 < NBG) step(c + 3, s0, s2, b1, b0);
+    if (c + 4 < NBG) step(c + 4, s1, s0, b0, b1);
+    if (c + 5 < NBG) step(c + 5, s2, s1, b1, b0);
+  }
+
+  if (!C::ROUTED && !active) return;
+#pragma unroll
+  for (int t = 0; t < MT; t++) {
+    if (t >= ntiles) break;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int p = 16 * t + 4 * lg + i;
+      if (p >= rows_here) continue;
+      const int gp = row0 + p;
+#pragma unroll
+      for (int q = 0; q < RGW; q++) {
+        const int n = n0 + 16 * q + lm;
+        if (n >= Nr) continue;
+        if constexpr (C::GATEUP) {
+          const float v = silu_f32(acc[q][0][t][i]) * acc[q][1][t][i];
+          reinterpret_cast<A*>(a.dst)[(size_t)gp * a.I + n] = to_bf16(v);
+        } else {
+          reinterpret_cast<float*>(a.dst)[(size_t)gp * a.H + n] = acc[q][0][t][i];
+        }
+      }
+    }
+  }
+}
+
+// NBG > 0 (bf16 routed modes): the unrolled pipeline for NBG chunks; the
+// launcher picks it when the contraction has NBG chunks and the workgroup
+// rows divide the weight rows.  NBG == 0: the register-staged body.
+template <typename A, int MODE, int NBG>
 __device__ __forceinline__ void prefill_wg(const PArgs& a) {
   using C = MC<MODE>;
-  constexpr int ROWS = PR<A, MODE>::ROWS, RU = PT<A>::RU;
-  __shared__ uint32_t sA[2 * ROWS * RU];
+  constexpr int ROWS = PR<A, MODE>::ROWS;
+  // routed modes: rows per tile of the sorted routes (the register-staged
+  // body walks a tile in passes of ROWS)
+  constexpr int TILE = sizeof(A) == 2 ? kTileRows : ROWS;
   const int Nr = C::GATEUP ? a.I : (MODE == kRouterApprox ? a.E : a.H);
   const int NT = (Nr + C::NWG - 1) / C::NWG;
   // XCD-aware mapping: the workgroups that share one expert's (or one token
@@ -321,33 +522,46 @@ __device__ __forceinline__ void prefill_wg(const PArgs& a) {
     const int2 tile = a.tiles[grp];
     const int e = tile.x;
     const int row0 = a.offsets[e] + tile.y;
-    const int nrows = min(ROWS, a.offsets[e + 1] - row0);
+    const int nrows = min(TILE, a.offsets[e + 1] - row0);
     if (nrows <= 0) return;
     const int tm = a.tier_map[e];
     const int tier = tm >> 16, slot = tm & 0xFFFF;
     if (tier < 0 || tier > 2 || slot >= a.tb.n_slots[tier]) return;
     // the tier's code width is uniform over the workgroup
-    switch (a.tb.bits[tier]) {
-      case 4: prefill_body<A, 4, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
-      case 3: prefill_body<A, 3, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
-      default: prefill_body<A, 2, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
+    if constexpr (sizeof(A) == 2 && NBG > 0) {
+      __shared__ uint4 sL0[kStagePieces], sL1[kStagePieces], sL2[kStagePieces];
+      switch (a.tb.bits[tier]) {
+        case 4: prefill_body_lds<4, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2); break;
+        case 3: prefill_body_lds<3, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2); break;
+        default: prefill_body_lds<2, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2); break;
+      }
+    } else {
+      __shared__ uint32_t sA[2 * ROWS * PT<A>::RU];
+      switch (a.tb.bits[tier]) {
+        case 4: prefill_body<A, 4, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
+        case 3: prefill_body<A, 3, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
+        default: prefill_body<A, 2, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
+      }
     }
   } else {
     const int row0 = grp * ROWS;
     if (row0 >= a.T) return;
+    // dense weights (router, shared expert): register-staged pipeline (three
+    // dense weight slots would not fit the register budget)
+    __shared__ uint32_t sA[2 * ROWS * PT<A>::RU];
     prefill_body<A, 0, MODE>(a, grp, row0, min(ROWS, a.T - row0), 0, 0, nt, sA);
   }
 }
 
 // bf16: four waves per SIMD (two workgroups per CU); the fp32 variants keep
 // their registers (no spills) at lower occupancy.
-template <int MODE>
+template <int MODE, int NBG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_prefill_bf16(PArgs a) {
-  prefill_wg<bf16_t, MODE>(a);
+  prefill_wg<bf16_t, MODE, NBG>(a);
 }
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void k_prefill_f32(PArgs a) {
-  prefill_wg<float, MODE>(a);
+  prefill_wg<float, MODE, 0>(a);
 }
 
 template <typename A, int MODE>
@@ -361,8 +575,24 @@ void launch_mode(const PArgs& a, int n_groups, hipStream_t s) {
                       : MODE == kSharedDown   ? MOE_K_PREFILL_SHARED_DOWN
                       : MODE == kRoutedDown   ? MOE_K_PREFILL_DOWN
                                               : MOE_K_ROUTER_APPROX;
-  if constexpr (sizeof(A) == 2) MOE_LAUNCH(kid, (k_prefill_bf16<MODE>), grid, dim3(kThreads), 0, s, a);
-  else MOE_LAUNCH(kid, (k_prefill_f32<MODE>), grid, dim3(kThreads), 0, s, a);
+  if constexpr (sizeof(A) == 2 && !C::ROUTED) {
+    MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 0>), grid, dim3(kThreads), 0, s, a);
+  } else if constexpr (sizeof(A) == 2) {
+    int nbg = 0;
+    const int k = (MODE == kRoutedDown ? a.I : a.H) / 128;
+    if (Nr % C::NWG == 0 && (k & (k - 1)) == 0 && k <= 32) nbg = k;
+    switch (nbg) {
+      case 1: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 1>), grid, dim3(kThreads), 0, s, a); break;
+      case 2: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 2>), grid, dim3(kThreads), 0, s, a); break;
+      case 4: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 4>), grid, dim3(kThreads), 0, s, a); break;
+      case 8: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 8>), grid, dim3(kThreads), 0, s, a); break;
+      case 16: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 16>), grid, dim3(kThreads), 0, s, a); break;
+      case 32: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 32>), grid, dim3(kThreads), 0, s, a); break;
+      default: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 0>), grid, dim3(kThreads), 0, s, a); break;
+    }
+  } else {
+    MOE_LAUNCH(kid, (k_prefill_f32<MODE>), grid, dim3(kThreads), 0, s, a);
+  }
 }
 
 PArgs make_args(const int32_t* offsets, const int32_t* sorted, const int32_t* tier_map, int E,
@@ -431,7 +661,7 @@ void launch_router_approx(const void* x, int T, const void* w_router, const floa
 }
 
 int prefill_tile_rows(int act) {
-  return act == MOE_BF16 ? PR<bf16_t, kRoutedGateUp>::ROWS : PR<float, kRoutedGateUp>::ROWS;
+  return act == MOE_BF16 ? kTileRows : PR<float, kRoutedGateUp>::ROWS;
 }
 
 void launch_prefill_gateup(int act, const int32_t* offsets, const int32_t* sorted_routes,
