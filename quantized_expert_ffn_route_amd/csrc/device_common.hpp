@@ -403,13 +403,16 @@ __device__ __forceinline__ int count_ge(const double (&kv)[KPL], double th) {
 
 // ---------------------------------------------------------------------------
 // Threshold top-K of one wave (E <= 64 * KPL keys, lane l holding ids
-// l + 64 j).  A value threshold is bisected between the smallest and the
-// largest key with ballot counts until between `rounds` and rounds + 8 keys
-// (at most 64) reach it; those candidates are compacted one per lane and each
-// is ranked exactly by (key desc, id asc) against the others, read from the
-// other lanes' registers.  The result equals the sorted-list selection above,
-// which remains the fallback when the field cannot be narrowed to 64 keys
-// (many equal keys) or holds NaN or infinite keys.  `scratch` is 64 slots of
+// l + 64 j).  The keys are counted into 256 value bins of equal width between
+// the smallest and the largest key; one scan from the top bin down finds the
+// bin that holds the rounds-th key, and the keys in it and above are the
+// candidates.  When that leaves more than 64 (clustered keys), a value
+// threshold is bisected with ballot counts until between `rounds` and
+// rounds + 8 keys reach it.  The candidates are compacted one per lane and
+// each is ranked exactly by (key desc, id asc) against the others, read from
+// the other lanes' registers.  The result equals the sorted-list selection
+// above, which remains the fallback when the field cannot be narrowed to 64
+// keys (many equal keys) or holds NaN or infinite keys.  `scratch` is 64 slots of
 // LDS owned by this wave.  Lanes r < rounds end with the r-th best id and its
 // order key; the other lanes with -1 and 0.
 // ---------------------------------------------------------------------------
@@ -455,6 +458,18 @@ __device__ __forceinline__ void rank_select(uint64_t mu, uint32_t mid_, int nc, 
   wave_sync_lds();
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active): four
+// shifts inside each row of 16, then the row totals broadcast upwards.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
 template <int KPL>
 __device__ __forceinline__ void topk_threshold(const double* __restrict__ krow, int E, int rounds,
                                                int lane, TopkSlot* __restrict__ scratch,
@@ -480,15 +495,56 @@ __device__ __forceinline__ void topk_threshold(const double* __restrict__ krow, 
   }
   bad = __ballot(bad) != 0;
   const int want = rounds + 8 < 64 ? rounds + 8 : 64;
-  bool found = false;
+  // Candidate set: the keys in value bin >= cb (histogram pass), else the
+  // keys >= th (bisection).  Either way every key outside the set is smaller
+  // than every key inside it, so the top `rounds` are among the candidates.
+  bool found = false, use_bins = false;
+  int cb = 0;
   double th = 0.0;
+  int bin[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; j++) bin[j] = -1;
   if (!bad) {
     wave_max2_f64(mx, nmn);
     double lo = -nmn, hi = mx;               // count(>= lo) = E >= rounds
     if (E <= want) {
       th = lo;
       found = true;
-    } else {
+    } else if (hi > lo) {
+      // 256 bins of equal width over [lo, hi] (the bin index is monotone in
+      // the key), counted in an LDS histogram that aliases the scratch slots;
+      // one scan from the top bin down finds the bin holding the rounds-th key
+      uint32_t* hist = reinterpret_cast<uint32_t*>(scratch);
+      reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+      wave_sync_lds();
+      const double scale = 256.0 / (hi - lo);
+#pragma unroll
+      for (int j = 0; j < KPL; j++) {
+        const double f = fmin(fmax((kv[j] - lo) * scale, 0.0), 255.0);
+        if (lane + 64 * j < E) {
+          bin[j] = (int)f;
+          atomicAdd(&hist[bin[j]], 1u);
+        }
+      }
+      wave_sync_lds();
+      int cum = 0;
+      cb = -1;
+      for (int pass = 0; pass < 4 && cb < 0; pass++) {
+        const int c = wave_incl_scan((int)hist[255 - 64 * pass - lane]) + cum;
+        const uint64_t m = __ballot(c >= rounds);
+        if (m) cb = 255 - 64 * pass - (int)__builtin_ctzll(m);
+        else cum = __builtin_amdgcn_readlane(c, 63);
+      }
+      wave_sync_lds();
+      int nb = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; j++) nb += __popcll(__ballot(bin[j] >= 0 && bin[j] >= cb));
+      if (cb >= 0 && nb >= rounds && nb <= 64) {
+        use_bins = true;
+        found = true;
+      }
+    }
+    if (!found && hi > lo) {
       for (int it = 0; it < 64 && !found; it++) {
         const double mid = lo + (hi - lo) * 0.5;
         if (!(mid > lo && mid < hi)) break;   // no room left: equal keys
@@ -497,10 +553,10 @@ __device__ __forceinline__ void topk_threshold(const double* __restrict__ krow, 
         else if (c > want) lo = mid;
         else { th = mid; found = true; }
       }
-      if (!found && count_ge<KPL>(kv, lo) <= 64) {   // ties: take the wider set
-        th = lo;
-        found = true;
-      }
+    }
+    if (!found && count_ge<KPL>(kv, lo) <= 64) {   // ties: take the wider set
+      th = lo;
+      found = true;
     }
   }
   if (!found) {
@@ -511,7 +567,7 @@ __device__ __forceinline__ void topk_threshold(const double* __restrict__ krow, 
   int nc = 0;
 #pragma unroll
   for (int j = 0; j < KPL; j++) {
-    const bool c = kv[j] >= th;
+    const bool c = use_bins ? (bin[j] >= 0 && bin[j] >= cb) : kv[j] >= th;
     const uint64_t m = __ballot(c);
     if (c) {
       const int pos = nc + __popcll(m & ((1ull << lane) - 1ull));

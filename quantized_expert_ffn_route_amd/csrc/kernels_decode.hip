@@ -294,11 +294,128 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode_gateup(const Item*
 // ---- A2 + A3 + A5 for one token ----------------------------------------------
 //
 // Batch-1 decode.  Work item u < K is the token's rank-u expert, item K the
-// shared expert, so workgroup (u, rg) needs only the first u + 1 ranks of the
-// top-K: wave 0 selects them from the keys while the other waves prefetch the
-// tier map into LDS, and the shared-expert workgroups skip routing.
-// Workgroup (K - 1, 0) selects all K and publishes ids, weights and the work
-// items for the down kernel.
+// shared expert; the shared-expert workgroups skip routing.  When every
+// thread can hold one key (E <= threads), the workgroup selects the top-K
+// together (topk_block); otherwise wave 0 selects the first u + 1 ranks while
+// the other waves prefetch the tier map into LDS.  Workgroup (K - 1, 0)
+// publishes ids, weights and the work items for the down kernel.
+
+// Workgroup-wide exact top-K of one token's keys, one key per thread
+// (E <= blockDim.x), with the tier map copied into LDS in the same round
+// trip.  The keys are counted into 256 value bins of equal width between the
+// block's smallest and largest key, computed in fp32 (rounding to fp32,
+// subtracting and scaling are all monotone, so the bin index never decreases
+// as the key grows); wave 0 scans the histogram from the top bin down to the
+// bin holding the K-th key.  The keys in that bin and above -- each larger
+// than every key outside -- are gathered in LDS and ranked exactly by (key
+// desc, id asc) in wave 0.  NaN or infinite keys, or more than 64 candidates,
+// hand over to the wave-level selection.  Wave 0's lanes r < K end with the
+// r-th id and its order key.
+struct TopkBlockLds {
+  TopkSlot cand[64];
+  uint32_t hist[256];
+  float mx[kGateUpWaves], mn[kGateUpWaves];
+  int bad[kGateUpWaves];
+  int cnt, cb, nb;
+};
+
+__device__ __forceinline__ void wave_maxmin_f32(float& mx, float& mn) {
+#define MOE_MM_STEP(C)                                                   \
+  mx = fmaxf(mx, __uint_as_float(dpp_u32<C>(__float_as_uint(mx))));     \
+  mn = fminf(mn, __uint_as_float(dpp_u32<C>(__float_as_uint(mn))));
+  MOE_MM_STEP(0xB1)    // quad_perm [1,0,3,2]
+  MOE_MM_STEP(0x4E)    // quad_perm [2,3,0,1]
+  MOE_MM_STEP(0x124)   // row_ror:4
+  MOE_MM_STEP(0x128)   // row_ror:8
+#undef MOE_MM_STEP
+  const auto rl = [](float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+  mx = fmaxf(fmaxf(rl(mx, 0), rl(mx, 16)), fmaxf(rl(mx, 32), rl(mx, 48)));
+  mn = fminf(fminf(rl(mn, 0), rl(mn, 16)), fminf(rl(mn, 32), rl(mn, 48)));
+}
+
+__device__ __forceinline__ void topk_block(const double* __restrict__ keys, int E, int K,
+                                           const int32_t* __restrict__ tier_map,
+                                           int32_t* __restrict__ s_tm, TopkBlockLds& S, int lane,
+                                           int wave, int NW, int* sel_id, uint64_t* sel_u) {
+  const int t = threadIdx.x;
+  const bool ok = t < E;
+  const double k = keys[ok ? t : E - 1];
+  const int tm = tier_map[ok ? t : E - 1];
+  const bool bad = ok && !(fabs(k) < INFINITY);
+  const float kf = (float)k;
+  float mx = ok && !bad ? kf : -INFINITY, mn = ok && !bad ? kf : INFINITY;
+  wave_maxmin_f32(mx, mn);
+  const bool wbad = __ballot(bad) != 0;
+  if (t < 256) S.hist[t] = 0u;
+  if (ok) s_tm[t] = tm;
+  if (lane == 0) {
+    S.mx[wave] = mx;
+    S.mn[wave] = mn;
+    S.bad[wave] = wbad ? 1 : 0;
+  }
+  if (t == 0) S.cnt = 0;
+  __syncthreads();
+  float hi = -INFINITY, lo = INFINITY;
+  int anybad = 0;
+  for (int w = 0; w < NW; w++) {
+    hi = fmaxf(hi, S.mx[w]);
+    lo = fminf(lo, S.mn[w]);
+    anybad |= S.bad[w];
+  }
+  // mode 0: histogram; 1: every key is a candidate; 2: wave-level selection
+  int mode = anybad ? 2 : (E <= 64 ? 1 : (hi > lo ? 0 : 2));
+  int bin = -1;
+  if (mode == 0) {
+    const float scale = 256.0f / (hi - lo);
+    if (ok) {
+      bin = (int)fminf(fmaxf((kf - lo) * scale, 0.0f), 255.0f);
+      atomicAdd(&S.hist[bin], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int cum = 0, cb = -1, nb = 0;
+      for (int pass = 0; pass < 4 && cb < 0; pass++) {
+        const int c = wave_incl_scan((int)S.hist[255 - 64 * pass - lane]) + cum;
+        const uint64_t m = __ballot(c >= K);
+        if (m) {
+          const int l = (int)__builtin_ctzll(m);
+          cb = 255 - 64 * pass - l;
+          nb = __builtin_amdgcn_readlane(c, l);
+        } else {
+          cum = __builtin_amdgcn_readlane(c, 63);
+        }
+      }
+      if (lane == 0) {
+        S.cb = cb;
+        S.nb = nb;
+      }
+    }
+    __syncthreads();
+    if (S.cb < 0 || S.nb > 64) mode = 2;
+  }
+  if (mode != 2) {
+    if (ok && (mode == 1 || bin >= S.cb)) {
+      const int pos = atomicAdd(&S.cnt, 1);
+      S.cand[pos].u = order_key(k);
+      S.cand[pos].id = (uint32_t)t;
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+  if (mode == 2) {
+    topk_threshold<8>(keys, E, K, lane, S.cand, sel_id, sel_u);
+    return;
+  }
+  const int nc = S.cnt;
+  uint64_t mu = 0;
+  uint32_t mid_ = 0xFFFFFFFFu;
+  if (lane < nc) {
+    mu = S.cand[lane].u;
+    mid_ = S.cand[lane].id;
+  }
+  wave_sync_lds();
+  rank_select(mu, mid_, nc, K, lane, S.cand, sel_id, sel_u);
+}
 
 template <typename A, int NC, int KPL>
 __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode1_gateup(const double* __restrict__ keys, int E, int K,
@@ -313,17 +430,35 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode1_gateup(const doub
   __shared__ float red[kGateUpWaves][8][64];
   __shared__ int32_t s_tm[4096];
   __shared__ int32_t s_sel;
-  __shared__ TopkSlot s_scr[64];
+  __shared__ TopkBlockLds s_tk;
   const int nrg = I / 16;
   const int u = blockIdx.x / nrg, rg = blockIdx.x % nrg;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, NW = blockDim.x >> 6;
   int tier = kDenseTier, slot = 0, bits = 0;
   if (u < K) {
     const bool writer = u == K - 1 && rg == 0;
+    int sid = -1;
+    uint64_t su = 0;
+    if (E <= (int)blockDim.x) {
+      topk_block(keys, E, K, tier_map, s_tm, s_tk, lane, wave, NW, &sid, &su);
+    } else if (wave == 0) {
+      topk_threshold<KPL>(keys, E, writer ? K : u + 1, lane, s_tk.cand, &sid, &su);
+    } else {
+      // tier map into LDS; four clamped loads in flight per thread per pass
+      const int nt = blockDim.x - 64;
+      for (int e0 = threadIdx.x - 64; e0 < E; e0 += 4 * nt) {
+        int v[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int e = e0 + j * nt;
+          v[j] = tier_map[e < E ? e : E - 1];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          if (e0 + j * nt < E) s_tm[e0 + j * nt] = v[j];
+      }
+    }
     if (wave == 0) {
-      int sid;
-      uint64_t su;
-      topk_threshold<KPL>(keys, E, writer ? K : u + 1, lane, s_scr, &sid, &su);
       if (lane == u) s_sel = sid;
       if (writer) {
         const double key = lane < K ? key_of_order(su) : 0.0;
@@ -365,20 +500,6 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode1_gateup(const doub
           }
           *n_items = K + (has_shared ? 1 : 0);
         }
-      }
-    } else {
-      // tier map into LDS; four clamped loads in flight per thread per pass
-      const int nt = blockDim.x - 64;
-      for (int e0 = threadIdx.x - 64; e0 < E; e0 += 4 * nt) {
-        int v[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const int e = e0 + j * nt;
-          v[j] = tier_map[e < E ? e : E - 1];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-          if (e0 + j * nt < E) s_tm[e0 + j * nt] = v[j];
       }
     }
     __syncthreads();
