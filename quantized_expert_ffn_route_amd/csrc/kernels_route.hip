@@ -97,27 +97,26 @@ __global__ __launch_bounds__(256) void k_router_keys(const A* __restrict__ x, co
   }
 }
 
-// Decode variant (T <= 16, tokens fit in 64 KiB of LDS): the group's tokens
-// are staged in LDS once per workgroup and every lane issues all loads of
-// its router row before the first FMA.  Same per-lane order and butterfly as
-// k_router_keys, so the keys are bit-identical.
+// Decode variant (T <= 16, tokens fit in 64 KiB of LDS): two experts per
+// workgroup (one wave each), so the router rows spread over every CU.  Each
+// lane issues all loads of its router row first, then the group's tokens are
+// staged in LDS; both round trips overlap.  Same per-lane order and butterfly
+// as k_router_keys, so the keys are bit-identical.
+constexpr int kRouterDecWaves = 2;
+
 template <typename A, int MAXC>
-__global__ __launch_bounds__(512) void k_router_keys_dec(const A* __restrict__ x,
-                                                         const A* __restrict__ w,
-                                                         const float* __restrict__ bias,
-                                                         double* __restrict__ keys, int T, int H,
-                                                         int E) {
+__global__ __launch_bounds__(64 * kRouterDecWaves) void k_router_keys_dec(const A* __restrict__ x,
+                                                                          const A* __restrict__ w,
+                                                                          const float* __restrict__ bias,
+                                                                          double* __restrict__ keys,
+                                                                          int T, int H, int E) {
   extern __shared__ uint4 s_x[];
-  const int n16 = T * H * (int)sizeof(A) / 16;
-  for (int i = threadIdx.x; i < n16; i += blockDim.x) s_x[i] = reinterpret_cast<const uint4*>(x)[i];
-  __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 8 + (threadIdx.x >> 6);
-  if (e >= E) return;
+  const int e = blockIdx.x * kRouterDecWaves + (threadIdx.x >> 6);
   const int nchunk = H / 8;
   constexpr int U4 = (int)sizeof(A) / 2;     // uint4 per 8-element chunk
   uint4 wraw[MAXC][U4];
-  const A* wr = w + (size_t)e * H;
+  const A* wr = w + (size_t)(e < E ? e : E - 1) * H;
 #pragma unroll
   for (int j = 0; j < MAXC; j++) {
     const int q = lane + 64 * j;
@@ -125,6 +124,10 @@ __global__ __launch_bounds__(512) void k_router_keys_dec(const A* __restrict__ x
 #pragma unroll
       for (int u = 0; u < U4; u++) wraw[j][u] = reinterpret_cast<const uint4*>(wr + 8 * q)[u];
   }
+  const int n16 = T * H * (int)sizeof(A) / 16;
+  for (int i = threadIdx.x; i < n16; i += blockDim.x) s_x[i] = reinterpret_cast<const uint4*>(x)[i];
+  __syncthreads();
+  if (e >= E) return;
   const double b = bias ? (double)bias[e] : 0.0;
   const A* sxa = reinterpret_cast<const A*>(s_x);
   for (int t = 0; t < T; t++) {
@@ -152,10 +155,11 @@ void launch_router_keys(int act, const void* x, const void* w, const float* b, d
                         int T, int H, int E, hipStream_t s) {
   const size_t xbytes = (size_t)T * H * (act == MOE_BF16 ? 2 : 4);
   if (T <= kGroup && xbytes <= 65536 && H <= 4096) {
-    dim3 grid((E + 7) / 8);
+    dim3 grid((E + kRouterDecWaves - 1) / kRouterDecWaves);
     const int maxc = (H / 8 + 63) / 64;
 #define MOE_RK(AT, MC)                                                                          \
-  MOE_LAUNCH(MOE_K_ROUTER_KEYS, (k_router_keys_dec<AT, MC>), grid, dim3(512), xbytes, s,        \
+  MOE_LAUNCH(MOE_K_ROUTER_KEYS, (k_router_keys_dec<AT, MC>), grid, dim3(64 * kRouterDecWaves), \
+             xbytes, s,                                                                         \
              (const AT*)x, (const AT*)w, b, keys, T, H, E)
     if (act == MOE_BF16) {
       if (maxc <= 1) MOE_RK(bf16_t, 1);
