@@ -24,7 +24,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
 ARCH = "gfx950"
-DEVICE_SOURCES = ["kernels_route.hip", "kernels_decode.hip", "kernels_prefill.hip"]
+DEVICE_SOURCES = ["kernels_route.hip", "kernels_decode.hip", "kernels_prefill.hip",
+                  "kernels_dense.hip"]
 HOST_SOURCES = ["moe_abi.cpp", "pack.cpp"]
 
 

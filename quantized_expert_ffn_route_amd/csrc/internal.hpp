@@ -143,6 +143,20 @@ void launch_topk_recheck(const void* x, const void* w, const float* bias, const 
                          const float* wnorm2, int T, int H, int E, int K, int32_t* ids, float* wts,
                          hipStream_t s);
 
+// ---- dense bf16 GEMMs of the prefill (kernels_dense.hip) ----
+
+// True when the contraction length suits the dense kernels (a multiple of 32).
+bool dense_supported(int K);
+// keys_approx[t][e] = fp32 x[t] . w[e] + b[e]; wnorm2[e] = |w[e]|^2 (fp32).
+void launch_dense_router(const void* x, int T, const void* w_router, const float* bias, int E,
+                         int H, float* keys_approx, float* wnorm2, hipStream_t s);
+// h_s[t][i] = bf16(silu(x[t] . w_gate[i]) * (x[t] . w_up[i])).
+void launch_dense_shared_gateup(const void* x, int T, const void* w_gate, const void* w_up,
+                                void* h_s, int H, int I, hipStream_t s);
+// rows[t][n] = fp32 h_s[t] . w_down[n].
+void launch_dense_shared_down(const void* h_s, int T, const void* w_down, float* rows, int H,
+                              int I, hipStream_t s);
+
 // ---- host packer (pack.cpp; no HIP calls) ----
 
 // Quantise one block of 32 floats; returns MOE_OK or MOE_EINVAL.

@@ -1,0 +1,284 @@
+// Dense bf16 GEMMs of the prefill: the MFMA router pass (A1), the shared
+// expert's gate/up with the SwiGLU activation and its down projection (A7,
+// A8 for the always-on expert).  out[m][n] = sum_k a[m][k] * b[n][k] with
+// both operands row-major along the contraction axis: token rows against
+// weight rows.
+//
+// A workgroup of four waves owns a tile of (32 * MTW) token rows and 128
+// weight rows; each wave owns a (16 * MTW) x 64 sub-tile, i.e. MTW x 4 MFMA
+// 16x16x32 accumulators, fed by MTW + 4 LDS fragment reads per k-step.  The
+// contraction axis goes in chunks of 64 (two MFMA k-steps), so each row read
+// is one whole 128-byte line.  Both operands
+// move from global memory straight into LDS (one 16-byte direct-to-LDS load
+// per lane and piece) through a three-stage ring, two chunks ahead of the
+// multiply.  A row of a stage is 8 pieces of 16 bytes; piece p of row r sits
+// in slot p ^ ((r >> 1) & 7), so the 16 rows of a fragment read hit 16
+// distinct bank groups.  The loads are issued from inline assembly and the
+// loop waits for exactly the loads of the chunk it is about to read (vmcnt),
+// then hands the stage over with a barrier: the only global loads inside the
+// loop are these, so no other wait is needed.
+#include "device_common.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kDWaves = 4;
+constexpr int kDThreads = 64 * kDWaves;
+constexpr int kDKC = 64;                // contraction elements per chunk (two MFMA k-steps)
+constexpr int kDPPR = kDKC / 8;         // 16-byte pieces per row of a stage
+constexpr int kDRowsB = 128;            // weight rows per workgroup tile
+constexpr int kDStages = 3;
+
+enum DenseMode { kDRouter = 0, kDGateUp = 1, kDDown = 2 };
+
+struct DArgs {
+  const bf16_t* a;    // token rows [M][K]
+  const bf16_t* b0;   // weight rows [N][K] (router, down projection, gate)
+  const bf16_t* b1;   // up rows [N][K] (gate/up)
+  int M, N, K;        // N: router experts, hidden size (down) or intermediate size (gate/up)
+  const float* bias;  // router bias or null
+  float* outf;        // router keys / shared rows, [M][N] fp32
+  bf16_t* outh;       // gate/up activations, [M][N] bf16
+  float* wnorm2;      // router: squared row norms [N]
+};
+
+template <int N>
+__device__ __forceinline__ void dwait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Waits until at most `ahead` chunks of DPC loads each are still in flight.
+template <int DPC>
+__device__ __forceinline__ void dwait_chunks(int ahead) {
+  static_assert(DPC * 3 < 64, "vmcnt");
+  switch (ahead) {
+    case 0: dwait_vmcnt<0>(); break;
+    case 1: dwait_vmcnt<DPC>(); break;
+    case 2: dwait_vmcnt<2 * DPC>(); break;
+    default: dwait_vmcnt<3 * DPC>(); break;
+  }
+}
+
+// One 16-byte piece per lane from global memory into LDS: lane i's piece
+// lands at lds + 16 i (lds wave-uniform).  No register destination.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(g)
+               : "memory", "m0");
+}
+
+// LDS hand-over: this wave's LDS operations done, then the workgroup barrier
+// (not __syncthreads, which would also drain the loads still in flight).
+__device__ __forceinline__ void dlds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ int dswz(int r) { return (r >> 1) & 7; }
+
+template <int MODE, int MTW>
+__global__ __launch_bounds__(kDThreads) void k_dense(DArgs a) {
+  constexpr int MROWS = 32 * MTW;                         // token rows per workgroup
+  constexpr int APIECES = MROWS * kDPPR, BPIECES = kDRowsB * kDPPR;
+  constexpr int LA = APIECES / kDThreads, LB = BPIECES / kDThreads;
+  constexpr int DPC = LA + LB;                            // loads per thread per chunk
+  constexpr int STAGE = (APIECES + BPIECES) * 16;         // bytes
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kDStages * STAGE];
+
+  const int ncols = MODE == kDGateUp ? kDRowsB / 2 : kDRowsB;   // output columns per workgroup
+  const int NT = (a.N + ncols - 1) / ncols;
+  // XCD-aware order: workgroups go to the 8 XCDs round-robin, so all column
+  // tiles of token tile mt run on XCD mt % 8 and share its L2 copy of the rows
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int mt = (j / NT) * 8 + xcd, nt = j % NT;
+  const int m0 = mt * MROWS, n0 = nt * ncols;
+  if (m0 >= a.M) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lm = lane & 15, lg = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int K = a.K, NC = K / kDKC;
+
+  // this thread's load sources (chunk 0) and LDS slots
+  const bf16_t* asrc[LA];
+  const bf16_t* bsrc[LB];
+#pragma unroll
+  for (int j = 0; j < LA; j++) {
+    const int q = threadIdx.x + kDThreads * j;            // slot in the A part
+    const int r = q / kDPPR, p = (q % kDPPR) ^ dswz(r);
+    const int gm = min(m0 + r, a.M - 1);
+    asrc[j] = a.a + (size_t)gm * K + 8 * p;
+  }
+#pragma unroll
+  for (int j = 0; j < LB; j++) {
+    const int q = threadIdx.x + kDThreads * j;
+    const int r = q / kDPPR, p = (q % kDPPR) ^ dswz(r);
+    const bf16_t* base;
+    int gn;
+    if constexpr (MODE == kDGateUp) {
+      // rows [64 w, 64 w + 32): gate rows, [64 w + 32, 64 w + 64): up rows
+      const int w = r >> 6, rr = r & 63;
+      gn = min(n0 + 32 * w + (rr & 31), a.N - 1);
+      base = rr < 32 ? a.b0 : a.b1;
+    } else {
+      gn = min(n0 + r, a.N - 1);
+      base = a.b0;
+    }
+    bsrc[j] = base + (size_t)gn * K + 8 * p;
+  }
+  const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)s_ring;
+  auto issue = [&](int c, int st) {
+    const uint32_t sb = ring + (uint32_t)(st * STAGE);
+#pragma unroll
+    for (int j = 0; j < LA; j++)
+      dma16(asrc[j] + kDKC * c, __builtin_amdgcn_readfirstlane(sb + (uint32_t)((kDThreads * j + 64 * wave) * 16)));
+#pragma unroll
+    for (int j = 0; j < LB; j++)
+      dma16(bsrc[j] + kDKC * c,
+            __builtin_amdgcn_readfirstlane(sb + (uint32_t)((APIECES + kDThreads * j + 64 * wave) * 16)));
+  };
+
+  // fragment slots (bytes inside a stage): k-step s of a chunk reads
+  // logical piece 4 s + lg of the lane's row
+  constexpr int KS = kDKC / 32;
+  uint32_t aoff[KS][MTW], boff[KS][4];
+#pragma unroll
+  for (int s = 0; s < KS; s++) {
+#pragma unroll
+    for (int t = 0; t < MTW; t++) {
+      const int r = wm * 16 * MTW + 16 * t + lm;
+      aoff[s][t] = (uint32_t)((r * kDPPR + ((4 * s + lg) ^ dswz(r))) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int r = wn * 64 + 16 * u + lm;
+      boff[s][u] = (uint32_t)((APIECES + r * kDPPR + ((4 * s + lg) ^ dswz(r))) * 16);
+    }
+  }
+
+  f32x4_t acc[MTW][4];
+#pragma unroll
+  for (int t = 0; t < MTW; t++)
+#pragma unroll
+    for (int u = 0; u < 4; u++) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float wsq = 0.f;   // router: this thread's weight row norm (first token tile, threads < 128)
+  const bool norms = MODE == kDRouter && mt == 0 && a.wnorm2 != nullptr && threadIdx.x < kDRowsB;
+
+  static_assert(kDStages - 2 <= 3, "dwait_chunks covers up to three chunks ahead");
+  for (int c = 0; c < kDStages - 1 && c < NC; c++) issue(c, c);
+  for (int c = 0; c < NC; c++) {
+    // chunks c + 1 .. c + kDStages - 2 may stay in flight
+    dwait_chunks<DPC>(min(kDStages - 2, NC - 1 - c));
+    dlds_barrier();
+    const int st = c % kDStages;
+    if (c + kDStages - 1 < NC) issue(c + kDStages - 1, (c + kDStages - 1) % kDStages);
+    const uint8_t* sp = s_ring + st * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      uint4 bf[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) bf[u] = *reinterpret_cast<const uint4*>(sp + boff[ks][u]);
+#pragma unroll
+      for (int t = 0; t < MTW; t++) {
+        const uint4 af = *reinterpret_cast<const uint4*>(sp + aoff[ks][t]);
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+          acc[t][u] = mfma_bf16(af.x, af.y, af.z, af.w, bf[u].x, bf[u].y, bf[u].z, bf[u].w, acc[t][u]);
+      }
+    }
+    if (norms) {
+      const uint4* row = reinterpret_cast<const uint4*>(sp + APIECES * 16) + threadIdx.x * kDPPR;
+#pragma unroll
+      for (int p = 0; p < kDPPR; p++) {
+        const uint4 v = row[p];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const float lo = bf16_lo(w4[i]), hi = bf16_hi(w4[i]);
+          wsq = __builtin_fmaf(lo, lo, wsq);
+          wsq = __builtin_fmaf(hi, hi, wsq);
+        }
+      }
+    }
+  }
+  if (norms && n0 + (int)threadIdx.x < a.N) a.wnorm2[n0 + threadIdx.x] = wsq;
+
+  // epilogue: lane holds C[4 lg + i][lm] of each 16x16 tile
+#pragma unroll
+  for (int t = 0; t < MTW; t++) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int m = m0 + wm * 16 * MTW + 16 * t + 4 * lg + i;
+      if (m >= a.M) continue;
+      if constexpr (MODE == kDGateUp) {
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+          const int n = n0 + wn * 32 + 16 * u + lm;
+          if (n < a.N)
+            a.outh[(size_t)m * a.N + n] = to_bf16(silu_f32(acc[t][u][i]) * acc[t][u + 2][i]);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const int n = n0 + wn * 64 + 16 * u + lm;
+          if (n < a.N) {
+            float v = acc[t][u][i];
+            if constexpr (MODE == kDRouter) v += a.bias ? a.bias[n] : 0.0f;
+            a.outf[(size_t)m * a.N + n] = v;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int MODE, int MTW>
+void launch_dense(const DArgs& a, int kid, hipStream_t s) {
+  const int ncols = MODE == kDGateUp ? kDRowsB / 2 : kDRowsB;
+  const int NT = (a.N + ncols - 1) / ncols;
+  const int MTt = (a.M + 32 * MTW - 1) / (32 * MTW);
+  if (MTt <= 0 || NT <= 0) return;
+  // token tiles rounded up to a multiple of 8 (one per XCD); the extra ones exit
+  MOE_LAUNCH(kid, (k_dense<MODE, MTW>), dim3(((MTt + 7) / 8) * 8 * NT), dim3(kDThreads), 0, s, a);
+}
+
+DArgs dargs(const void* a, int M, int N, int K) {
+  DArgs d = {};
+  d.a = reinterpret_cast<const bf16_t*>(a);
+  d.M = M;
+  d.N = N;
+  d.K = K;
+  return d;
+}
+
+}  // namespace
+
+bool dense_supported(int K) { return K >= kDKC && K % kDKC == 0; }
+
+void launch_dense_router(const void* x, int T, const void* w_router, const float* bias, int E,
+                         int H, float* keys_approx, float* wnorm2, hipStream_t s) {
+  DArgs d = dargs(x, T, E, H);
+  d.b0 = reinterpret_cast<const bf16_t*>(w_router);
+  d.bias = bias;
+  d.outf = keys_approx;
+  d.wnorm2 = wnorm2;
+  launch_dense<kDRouter, 2>(d, MOE_K_ROUTER_APPROX, s);
+}
+
+void launch_dense_shared_gateup(const void* x, int T, const void* w_gate, const void* w_up,
+                                void* h_s, int H, int I, hipStream_t s) {
+  DArgs d = dargs(x, T, I, H);
+  d.b0 = reinterpret_cast<const bf16_t*>(w_gate);
+  d.b1 = reinterpret_cast<const bf16_t*>(w_up);
+  d.outh = reinterpret_cast<bf16_t*>(h_s);
+  launch_dense<kDGateUp, 2>(d, MOE_K_PREFILL_SHARED_GATEUP, s);
+}
+
+void launch_dense_shared_down(const void* h_s, int T, const void* w_down, float* rows, int H,
+                              int I, hipStream_t s) {
+  DArgs d = dargs(h_s, T, H, I);
+  d.b0 = reinterpret_cast<const bf16_t*>(w_down);
+  d.outf = rows;
+  launch_dense<kDDown, 2>(d, MOE_K_PREFILL_SHARED_DOWN, s);
+}
+
+}  // namespace moe

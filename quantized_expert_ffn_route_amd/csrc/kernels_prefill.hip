@@ -651,6 +651,10 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ share
 
 void launch_router_approx(const void* x, int T, const void* w_router, const float* bias, int E,
                           int H, float* keys_approx, float* wnorm2, hipStream_t s) {
+  if (dense_supported(H)) {
+    launch_dense_router(x, T, w_router, bias, E, H, keys_approx, wnorm2, s);
+    return;
+  }
   Tables tb = {};
   PArgs a = make_args(nullptr, nullptr, nullptr, E, 0, T, H, 0, x, keys_approx, tb);
   a.wdense = w_router;
@@ -677,6 +681,10 @@ void launch_prefill_gateup(int act, const int32_t* offsets, const int32_t* sorte
 
 void launch_prefill_shared_gateup(int act, const void* x, int T, const Tables& tb, void* h_s,
                                   int H, int I, hipStream_t s) {
+  if (act == MOE_BF16 && dense_supported(H)) {
+    launch_dense_shared_gateup(x, T, tb.dense[MOE_GATE], tb.dense[MOE_UP], h_s, H, I, s);
+    return;
+  }
   const PArgs a = make_args(nullptr, nullptr, nullptr, 0, 0, T, H, I, x, h_s, tb);
   constexpr int RB = PR<bf16_t, kSharedGateUp>::ROWS, RF = PR<float, kSharedGateUp>::ROWS;
   if (act == MOE_BF16) launch_mode<bf16_t, kSharedGateUp>(a, (T + RB - 1) / RB, s);
@@ -685,6 +693,10 @@ void launch_prefill_shared_gateup(int act, const void* x, int T, const Tables& t
 
 void launch_prefill_shared_down(int act, const void* h_s, int T, const Tables& tb, float* rows,
                                 int H, int I, hipStream_t s) {
+  if (act == MOE_BF16 && dense_supported(I)) {
+    launch_dense_shared_down(h_s, T, tb.dense[MOE_DOWN], rows, H, I, s);
+    return;
+  }
   const PArgs a = make_args(nullptr, nullptr, nullptr, 0, 0, T, H, I, h_s, rows, tb);
   if (act == MOE_BF16) launch_mode<bf16_t, kSharedDown>(a, (T + PR<bf16_t, kSharedDown>::ROWS - 1) / PR<bf16_t, kSharedDown>::ROWS, s);
   else launch_mode<float, kSharedDown>(a, (T + PR<float, kSharedDown>::ROWS - 1) / PR<float, kSharedDown>::ROWS, s);
