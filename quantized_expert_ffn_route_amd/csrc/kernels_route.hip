@@ -311,19 +311,47 @@ __device__ __forceinline__ float wave_max_f32(float v) {
                      __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 48))));
 }
 
-// The float64 key of expert e for the token held in xv (canonical chunk order,
-// identical arithmetic to k_router_keys / k_router_keys_dec).
+// Wave sums of 8 candidates at once: p[c] is this lane's partial of
+// candidate c.  Each exchange hands the half of the candidates this lane does
+// not keep to its partner, so candidate c's total ends in lanes 8c .. 8c + 7
+// after 10 fp64 exchanges instead of 48.  Every addition pairs the same two
+// partial sums as wave_sum_f64 (partners at distance 32, 16, 8, 4, 2, 1), so
+// each total is bit-identical to wave_sum_f64 of that candidate's partials.
+__device__ __forceinline__ double wave_sum8_f64(const double (&p)[8], int lane) {
+  double q4[4], q2[2];
+  const bool h32 = (lane >> 5) & 1, h16 = (lane >> 4) & 1, h8 = (lane >> 3) & 1;
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    const double keep = h32 ? p[c + 4] : p[c], send = h32 ? p[c] : p[c + 4];
+    q4[c] = keep + __shfl_xor(send, 32, 64);
+  }
+#pragma unroll
+  for (int c = 0; c < 2; c++) {
+    const double keep = h16 ? q4[c + 2] : q4[c], send = h16 ? q4[c] : q4[c + 2];
+    q2[c] = keep + __shfl_xor(send, 16, 64);
+  }
+  double v = (h8 ? q2[1] : q2[0]) + __shfl_xor(h8 ? q2[0] : q2[1], 8, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 1, 64);
+  return v;
+}
+
+// The float64 key partial of this lane for a token held as raw bf16 pairs
+// (canonical chunk order, identical arithmetic to k_router_keys): both
+// operands are widened per use, which keeps the register footprint small.
 template <int MAXC>
-__device__ __forceinline__ double lane_dot_f64(const double (&xv)[MAXC][8], const uint4 (&wr)[MAXC],
-                                               int lane, int nchunk) {
+__device__ __forceinline__ double lane_dot_bf16(const uint4 (&xr)[MAXC], const uint4 (&wr)[MAXC],
+                                                int lane, int nchunk) {
   double acc = 0.0;
 #pragma unroll
   for (int j = 0; j < MAXC; j++) {
     if (lane + 64 * j < nchunk) {
-      double w8[8];
+      double x8[8], w8[8];
+      cvt8_f64<bf16_t>(&xr[j], x8);
       cvt8_f64<bf16_t>(&wr[j], w8);
 #pragma unroll
-      for (int k = 0; k < 8; k++) acc = __builtin_fma(xv[j][k], w8[k], acc);
+      for (int k = 0; k < 8; k++) acc = __builtin_fma(x8[k], w8[k], acc);
     }
   }
   return acc;
@@ -346,16 +374,11 @@ __global__ __launch_bounds__(512) void k_topk_recheck(const bf16_t* __restrict__
   if (t >= T) return;
   const int nchunk = H / 8;
   // token row in fp64 registers, canonical chunk order; approximate keys
-  double xv[MAXC][8];
-  {
-    uint4 xr[MAXC];
+  uint4 xr[MAXC];   // token row, raw bf16 (widened per use)
 #pragma unroll
-    for (int j = 0; j < MAXC; j++) {
-      const int q = lane + 64 * j;
-      xr[j] = reinterpret_cast<const uint4*>(x + (size_t)t * H)[q < nchunk ? q : 0];
-    }
-#pragma unroll
-    for (int j = 0; j < MAXC; j++) cvt8_f64<bf16_t>(&xr[j], xv[j]);
+  for (int j = 0; j < MAXC; j++) {
+    const int q = lane + 64 * j;
+    xr[j] = reinterpret_cast<const uint4*>(x + (size_t)t * H)[q < nchunk ? q : 0];
   }
   float ap[KPL], wn[KPL];
 #pragma unroll
@@ -367,9 +390,12 @@ __global__ __launch_bounds__(512) void k_topk_recheck(const bf16_t* __restrict__
   double xx = 0.0;
 #pragma unroll
   for (int j = 0; j < MAXC; j++)
-    if (lane + 64 * j < nchunk)
+    if (lane + 64 * j < nchunk) {
+      double x8[8];
+      cvt8_f64<bf16_t>(&xr[j], x8);
 #pragma unroll
-      for (int k = 0; k < 8; k++) xx = __builtin_fma(xv[j][k], xv[j][k], xx);
+      for (int k = 0; k < 8; k++) xx = __builtin_fma(x8[k], x8[k], xx);
+    }
   float wm = 0.0f, am = 0.0f, amx = -INFINITY, nmn = -INFINITY;
   bool bad = false;
 #pragma unroll
@@ -431,36 +457,45 @@ __global__ __launch_bounds__(512) void k_topk_recheck(const bf16_t* __restrict__
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // rescore, CB candidate rows in flight at a time; candidate i's key ends
-  // in lane i (all: in s_keys)
-  constexpr int CB = MAXC >= 8 ? 2 : 4;
+  // rescore in rounds of 8 candidates (rows loaded CB at a time), the 8
+  // wave sums taken together; candidate i's key ends in lane i (all: in s_keys)
   uint64_t mu = 0;
   uint32_t mid_ = 0xFFFFFFFFu;
-  for (int i0 = 0; i0 < ncand; i0 += CB) {
-    uint4 wr[CB][MAXC];
-    int ee[CB];
+  constexpr int CB = MAXC >= 8 ? 1 : 2;
+  for (int r0 = 0; r0 < ncand; r0 += 8) {
+    double part[8];
 #pragma unroll
-    for (int c = 0; c < CB; c++) {
-      const int i = i0 + c < ncand ? i0 + c : ncand - 1;
-      ee[c] = all ? i : s_cand[wv][i];
-      const uint4* row = reinterpret_cast<const uint4*>(w + (size_t)ee[c] * H);
+    for (int b = 0; b < 8; b += CB) {
+      uint4 wr[CB][MAXC];
 #pragma unroll
-      for (int j = 0; j < MAXC; j++) {
-        const int q = lane + 64 * j;
-        wr[c][j] = row[q < nchunk ? q : 0];
+      for (int c = 0; c < CB; c++) {
+        const int i = r0 + b + c < ncand ? r0 + b + c : ncand - 1;
+        const int e = all ? i : s_cand[wv][i];
+        const uint4* row = reinterpret_cast<const uint4*>(w + (size_t)e * H);
+#pragma unroll
+        for (int j = 0; j < MAXC; j++) {
+          const int q = lane + 64 * j;
+          wr[c][j] = row[q < nchunk ? q : 0];
+        }
       }
-    }
 #pragma unroll
-    for (int c = 0; c < CB; c++) {
-      const int i = i0 + c;
-      if (i >= ncand) break;
-      const double key = wave_sum_f64(lane_dot_f64<MAXC>(xv, wr[c], lane, nchunk)) +
-                         (bias ? (double)bias[ee[c]] : 0.0);
-      if (all) {
-        if (lane == 0) s_keys[wv][i] = key;
-      } else if (lane == i) {
-        mu = order_key(key);
-        mid_ = (uint32_t)ee[c];
+      for (int c = 0; c < CB; c++) part[b + c] = lane_dot_bf16<MAXC>(xr, wr[c], lane, nchunk);
+    }
+    const double sum = wave_sum8_f64(part, lane);   // candidate r0 + j in lanes 8j .. 8j + 7
+    const int jc = lane >> 3;
+    const int ic = r0 + jc < ncand ? r0 + jc : ncand - 1;
+    const int ec = all ? ic : s_cand[wv][ic];
+    const double key = sum + (bias ? (double)bias[ec] : 0.0);
+    if (all) {
+      if ((lane & 7) == 0 && r0 + jc < ncand) s_keys[wv][r0 + jc] = key;
+    } else {
+      // candidate i = r0 + j moves from lane 8 j to lane i
+      const int src = 8 * ((lane - r0) & 7);
+      const double ki = __shfl(key, src, 64);
+      const int ei = __shfl(ec, src, 64);
+      if (lane >= r0 && lane < r0 + 8 && lane < ncand) {
+        mu = order_key(ki);
+        mid_ = (uint32_t)ei;
       }
     }
   }
