@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run an elementwise copy of 256 MiB (fp32 -> fp32) three times, the "
                          "known-size reference for HBM byte counters")
+    ap.add_argument("--traffic-json", nargs="+", metavar="DIR",
+                    help="write profiles/hbm_traffic.json from the FETCH_SIZE / WRITE_SIZE "
+                         "counter runs under DIR(s) (taken with --calib-copy)")
     ap.add_argument("--prof-summary", nargs=3, metavar=("DIR", "COMMAND", "TITLE"),
                     help="print a markdown summary of a rocprofv3 output directory and exit")
     return ap.parse_args()
@@ -303,8 +306,68 @@ def prof_summary(out_dir, command, title):
         print()
 
 
+# kernel symbol fragment -> name used by the launch trace and the bench line
+TRAFFIC_KERNELS = [
+    ("k_router_keys", "router_keys"), ("k_decode1_gateup", "decode_gateup"),
+    ("k_decode_gateup", "decode_gateup"), ("k_decode_down", "decode_down"),
+    ("k_prefill_bf16<0,", "prefill_gateup"), ("k_prefill_bf16<2,", "prefill_down"),
+    ("k_dense<0,", "router_approx"), ("k_dense<1,", "prefill_shared_gateup"),
+    ("k_dense<2,", "prefill_shared_down"), ("k_topk_recheck", "topk_recheck"),
+    ("k_combine", "combine"),
+]
+
+
+def traffic_record(dirs):
+    """HBM bytes per launch of each library kernel from FETCH_SIZE / WRITE_SIZE
+    counter runs (KiB per dispatch), each scaled by the factor that maps the
+    256 MiB reference copy (--calib-copy) onto its true size; stamped with the
+    hash of the kernel sources they were taken on."""
+    import csv
+    import glob
+    rows = []
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            with open(f, newline="") as fh:
+                rows.extend(csv.DictReader(fh))
+    calib = {}
+    for r in rows:
+        if "neg_kernel" in r.get("Kernel_Name", ""):
+            g, c = int(r.get("Grid_Size", 0)), r["Counter_Name"]
+            if g >= calib.get(c, (0, 0.0))[0]:
+                calib[c] = (g, float(r["Counter_Value"]))
+    factor = {c: (256 * 1024) / v for c, (g, v) in calib.items() if v > 0}
+    acc = {}
+    for r in rows:
+        name = r.get("Kernel_Name", "").replace("(anonymous namespace)::", "").replace(" ", "")
+        c = r["Counter_Name"]
+        key = next((k for frag, k in TRAFFIC_KERNELS if frag.replace(" ", "") in name), None)
+        if key is None or c not in factor or "moe::" not in name:
+            continue
+        a = acc.setdefault(key, {}).setdefault(c, [0, 0.0])
+        a[0] += 1
+        a[1] += float(r["Counter_Value"]) * 1024 * factor[c]
+    per = {k: {"read": int(v["FETCH_SIZE"][1] / v["FETCH_SIZE"][0]),
+               "write": int(v["WRITE_SIZE"][1] / v["WRITE_SIZE"][0])}
+           for k, v in acc.items() if "FETCH_SIZE" in v and "WRITE_SIZE" in v}
+    return {
+        "what": "HBM bytes per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE, each scaled by the "
+                "factor that maps a 256 MiB reference copy onto its true size",
+        "summary": "profiles/moe_decode_b1_prefill4096_hbm_bytes.md",
+        "sources_sha256": sources_sha256(),
+        "factors": {c: round(f, 4) for c, f in sorted(factor.items())},
+        "per_launch_bytes": per,
+    }
+
+
 def main():
     args = parse()
+    if args.traffic_json:
+        rec = traffic_record(args.traffic_json)
+        with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
+        print(json.dumps(rec["per_launch_bytes"]))
+        return
     if args.prof_summary:
         prof_summary(*args.prof_summary)
         return
