@@ -131,11 +131,14 @@ def make_stack(M, torch, spec, n_layers, seed):
 
 
 def sources_sha256():
-    """Hash of the library's kernel sources (every file under csrc/)."""
+    """Hash of the library's device sources (the .hip kernels with their
+    launchers and the shared device header): a kernel's memory traffic depends
+    on nothing else."""
     import glob
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "quantized_expert_ffn_route_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "quantized_expert_ffn_route_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())

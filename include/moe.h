@@ -187,7 +187,9 @@ int moe_build_tiers(const moe_dims* dims, const uint64_t* popularity,
  *
  *   x         device [T][H] act dtype.
  *   topk_ids  device [T][K] int32 (out).   topk_w device [T][K] fp32 (out).
- * T == 0 is a no-op. */
+ * T == 0 is a no-op.  For bf16 and more than 16 tokens the keys are first
+ * formed in fp32 with MFMA and only the candidates within the fp32 error
+ * bound of the K-th key are rescored in float64; the result is identical. */
 int moe_route(const moe_dims* dims, const moe_layer* layer, const void* x, int32_t T,
               int32_t* topk_ids, float* topk_w, void* ws, size_t* ws_bytes,
               hipStream_t stream);

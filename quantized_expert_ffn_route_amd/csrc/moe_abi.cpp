@@ -411,10 +411,20 @@ int moe_route(const moe_dims* dims, const moe_layer* layer, const void* x, int32
   if (!x || !aligned(x, 16) || !topk_ids || !topk_w) return MOE_EINVAL;
   clear_hip_error();
   char* base = static_cast<char*>(ws);
+  const int H = dims->hidden, E = dims->n_experts, K = dims->top_k;
+  if (mfma_router(dims) && T > kGroup) {
+    // many tokens: MFMA keys + exact float64 rescoring of the candidates (the
+    // fp32 keys and row norms fit in the space of the float64 keys)
+    float* approx = reinterpret_cast<float*>(base + w.keys);
+    float* wnorm2 = approx + (size_t)T * E;
+    launch_router_approx(x, T, layer->w_router, layer->b_router, E, H, approx, wnorm2, stream);
+    launch_topk_recheck(x, layer->w_router, layer->b_router, approx, wnorm2, T, H, E, K, topk_ids,
+                        topk_w, stream);
+    return hip_status();
+  }
   double* keys = reinterpret_cast<double*>(base + w.keys);
-  launch_router_keys(dims->act, x, layer->w_router, layer->b_router, keys, T, dims->hidden,
-                     dims->n_experts, stream);
-  launch_topk(keys, T, dims->n_experts, dims->top_k, topk_ids, topk_w, stream);
+  launch_router_keys(dims->act, x, layer->w_router, layer->b_router, keys, T, H, E, stream);
+  launch_topk(keys, T, E, K, topk_ids, topk_w, stream);
   return hip_status();
 }
 
