@@ -618,7 +618,9 @@ PArgs make_args(const int32_t* offsets, const int32_t* sorted, const int32_t* ti
 }
 
 // y[t] = shared[t] + sum_k w[t][k] * rows[pos[t*K + k]], k in rank order.
-template <typename Y>
+// The rows of up to KB routes are loaded before any is added, so they are in
+// flight together; the sum itself runs in rank order.
+template <typename Y, int KB>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ shared_rows,
                                                  const float* __restrict__ route_rows,
                                                  const int32_t* __restrict__ route_pos,
@@ -629,14 +631,24 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ share
   if (c >= H) return;
   float4 acc = shared_rows ? *reinterpret_cast<const float4*>(shared_rows + (size_t)t * H + c)
                            : make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k = 0; k < K; k++) {
-    const int pos = route_pos[(size_t)t * K + k];
-    const float g = topk_w[(size_t)t * K + k];
-    const float4 v = *reinterpret_cast<const float4*>(route_rows + (size_t)pos * H + c);
-    acc.x = __builtin_fmaf(g, v.x, acc.x);
-    acc.y = __builtin_fmaf(g, v.y, acc.y);
-    acc.z = __builtin_fmaf(g, v.z, acc.z);
-    acc.w = __builtin_fmaf(g, v.w, acc.w);
+  for (int k0 = 0; k0 < K; k0 += KB) {
+    float4 v[KB];
+    float g[KB];
+#pragma unroll
+    for (int j = 0; j < KB; j++) {
+      const int k = k0 + j < K ? k0 + j : K - 1;
+      const int pos = route_pos[(size_t)t * K + k];
+      g[j] = topk_w[(size_t)t * K + k];
+      v[j] = *reinterpret_cast<const float4*>(route_rows + (size_t)pos * H + c);
+    }
+#pragma unroll
+    for (int j = 0; j < KB; j++) {
+      if (k0 + j >= K) continue;
+      acc.x = __builtin_fmaf(g[j], v[j].x, acc.x);
+      acc.y = __builtin_fmaf(g[j], v[j].y, acc.y);
+      acc.z = __builtin_fmaf(g[j], v[j].z, acc.z);
+      acc.w = __builtin_fmaf(g[j], v[j].w, acc.w);
+    }
   }
   Y* out = y + (size_t)t * H + c;
   if constexpr (sizeof(Y) == 4) {
@@ -720,10 +732,10 @@ void launch_combine(int y_dt, const float* shared_rows, const float* route_rows,
   const int nb = (H / 4 + 255) / 256;
   dim3 grid((unsigned)((size_t)T * nb));
   if (y_dt == MOE_BF16)
-    MOE_LAUNCH(MOE_K_COMBINE, k_combine<bf16_t>, grid, dim3(256), 0, s, shared_rows, route_rows,
+    MOE_LAUNCH(MOE_K_COMBINE, (k_combine<bf16_t, 16>), grid, dim3(256), 0, s, shared_rows, route_rows,
                route_pos, topk_w, K, H, nb, (bf16_t*)y);
   else
-    MOE_LAUNCH(MOE_K_COMBINE, k_combine<float>, grid, dim3(256), 0, s, shared_rows, route_rows,
+    MOE_LAUNCH(MOE_K_COMBINE, (k_combine<float, 16>), grid, dim3(256), 0, s, shared_rows, route_rows,
                route_pos, topk_w, K, H, nb, (float*)y);
 }
 

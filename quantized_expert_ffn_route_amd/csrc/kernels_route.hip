@@ -705,8 +705,25 @@ __global__ __launch_bounds__(1024) void k_sort_scan(int n_chunks, int E, int til
   __shared__ int32_t s_wave[16][2];
   __shared__ int32_t s_total;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  // per-expert totals over the chunks, 8 loads in flight per thread
-  for (int e = tid; e < E; e += blockDim.x) {
+  // one expert per thread and at most 64 chunks (4096 tokens): every count is
+  // loaded at once and kept in registers for the second pass
+  constexpr int CMAX = 64;
+  const bool regs = E <= (int)blockDim.x && n_chunks <= CMAX;
+  int rc[CMAX];
+  if (regs) {
+    const int e = tid < E ? tid : E - 1;
+#pragma unroll
+    for (int c = 0; c < CMAX; c++) rc[c] = chunk_base[(size_t)(c < n_chunks ? c : n_chunks - 1) * E + e];
+    if (tid < E) {
+      int sum = 0;
+#pragma unroll
+      for (int c = 0; c < CMAX; c++) sum += c < n_chunks ? rc[c] : 0;
+      s_tot[tid] = sum;
+      s_til[tid] = (sum + tile_rows - 1) / tile_rows;
+    }
+  }
+  // otherwise: per-expert totals over the chunks, 8 loads in flight per thread
+  for (int e = tid; e < E && !regs; e += blockDim.x) {
     int sum = 0;
     for (int c0 = 0; c0 < n_chunks; c0 += 8) {
       int v[8];
@@ -778,6 +795,16 @@ __global__ __launch_bounds__(1024) void k_sort_scan(int n_chunks, int E, int til
     const int n_e = (e + 1 < E ? s_tot[e + 1] : s_total) - base0;
     for (int p = 0; p * tile_rows < n_e; p++) tiles[s_til[e] + p] = make_int2(e, p * tile_rows);
     int base = base0;
+    if (regs) {
+#pragma unroll
+      for (int c = 0; c < CMAX; c++) {
+        if (c < n_chunks) {
+          chunk_base[(size_t)c * E + e] = base;
+          base += rc[c];
+        }
+      }
+      continue;
+    }
     for (int c0 = 0; c0 < n_chunks; c0 += 8) {
       int cnt[8];
 #pragma unroll
