@@ -275,6 +275,34 @@ def test_prefill_mid(mid, T):
     check_y(yb, O.output_cast(ref["y"], "bf16"), "bf16", f"prefill mid T={T} bf16 out")
 
 
+# Shapes off the fast paths: 3 chunks of 128 along H and I (not a power of
+# two: the routed GEMMs take the register-staged pipeline) and 48 experts (not
+# a multiple of 32: the prefill router keeps the float64 GEMV + sorted top-K).
+ODD = synth.LayerSpec(hidden=384, inter=384, n_experts=48, top_k=6, has_shared=True, act="bf16",
+                      n_slots=(12, 24, 12))
+
+
+@pytest.fixture(scope="module")
+def odd():
+    print("\n[fixture] odd-shape layer", flush=True)
+    return make_layer(ODD, seed=9)
+
+
+@pytest.mark.parametrize("T", [1, 5, 200])
+def test_odd_shapes_decode_and_prefill(odd, T):
+    x = synth.tokens(ODD, T, 50 + T)
+    ref = O.moe_layer(act_f64(x, "bf16"), odd.ol)
+    y, ids, w = run_decode(odd, x)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    check_y(y, ref["y"], "bf16", f"decode odd T={T}")
+    yp, idp, wp, off, srt = run_prefill(odd, x)
+    np.testing.assert_array_equal(idp, ref["ids"])
+    o_off, o_srt = O.sort_routes(idp, ODD.n_experts)
+    np.testing.assert_array_equal(off, o_off)
+    np.testing.assert_array_equal(srt, o_srt)
+    check_y(yp, ref["y"], "bf16", f"prefill odd T={T}")
+
+
 def test_prefill_full_4096_sampled(full):
     T = 4096
     x = synth.tokens(full.spec, T, 21)
