@@ -34,6 +34,18 @@
  * - Expert ids are int32 in [0, E); "no expert" is never encoded in an id
  *   ([P1] "the four bugs, briefly": a -1 sentinel promoted to unsigned read
  *   four billion rows past a buffer).
+ *
+ * Steps of the layer (the labels the comments of this library use)
+ * ----------------------------------------------------------------
+ *   A0  tier build: rank experts by popularity, assign (tier, slot), pack.
+ *   A1  router scores: key[t][e] = x[t] . W_r[e] + b[e].
+ *   A2  top-K by (key desc, id asc) and softmax weights over the K kept.
+ *   A3  tier dispatch of a decode group: the union of its experts.
+ *   A4  stable counting sort of the routes t*K + k by expert (prefill).
+ *   A5  decode gate/up: dequantise and multiply, h = silu(gate) * up.
+ *   A6  decode down projection and weighted combine (+ shared expert).
+ *   A7  prefill gate/up as grouped GEMMs over the expert buckets.
+ *   A8  prefill down projection, shared expert and weighted combine.
  */
 #ifndef MOE_H
 #define MOE_H

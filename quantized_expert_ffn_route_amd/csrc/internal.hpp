@@ -131,11 +131,6 @@ void launch_combine(int y_dt, const float* shared_rows, const float* route_rows,
                     const int32_t* route_pos, const float* topk_w, int T, int K, int H, void* y,
                     hipStream_t s);
 
-// Approximate router keys with bf16 MFMA (bf16 activations only):
-// keys_approx[t][e] = fp32 sum of x[t] * w[e] + b[e]; wnorm2[e] = |w[e]|^2 (fp32).
-void launch_router_approx(const void* x, int T, const void* w_router, const float* bias, int E,
-                          int H, float* keys_approx, float* wnorm2, hipStream_t s);
-
 // Exact top-K from approximate keys (bf16 activations): candidates within the
 // rounding bound of the K-th approximate key are rescored in float64 with the
 // arithmetic of launch_router_keys, then ranked (key desc, id asc).
@@ -145,8 +140,9 @@ void launch_topk_recheck(const void* x, const void* w, const float* bias, const 
 
 // ---- dense bf16 GEMMs of the prefill (kernels_dense.hip) ----
 
-// True when the contraction length suits the dense kernels (a multiple of 32).
-bool dense_supported(int K);
+// The dense kernels take any contraction length that is a multiple of 64
+// (every H and I the entry points accept, which are multiples of 128).
+// Approximate router keys with bf16 MFMA (bf16 activations only):
 // keys_approx[t][e] = fp32 x[t] . w[e] + b[e]; wnorm2[e] = |w[e]|^2 (fp32).
 void launch_dense_router(const void* x, int T, const void* w_router, const float* bias, int E,
                          int H, float* keys_approx, float* wnorm2, hipStream_t s);

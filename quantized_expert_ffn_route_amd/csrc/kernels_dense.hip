@@ -252,8 +252,6 @@ DArgs dargs(const void* a, int M, int N, int K) {
 
 }  // namespace
 
-bool dense_supported(int K) { return K >= kDKC && K % kDKC == 0; }
-
 void launch_dense_router(const void* x, int T, const void* w_router, const float* bias, int E,
                          int H, float* keys_approx, float* wnorm2, hipStream_t s) {
   DArgs d = dargs(x, T, E, H);

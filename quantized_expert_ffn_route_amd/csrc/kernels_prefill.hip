@@ -1,24 +1,24 @@
-// Prefill path (A7, A8, and the MFMA router pass of A1): grouped GEMMs over
-// the expert buckets produced by the counting sort, the shared expert's dense
-// GEMMs, and a deterministic combine.
+// Prefill path (A7, A8): grouped GEMMs over the expert buckets produced by
+// the counting sort, and a deterministic combine.  The shared expert's bf16
+// GEMMs and the MFMA router pass run on the dense kernels (kernels_dense.hip).
 //
 // A workgroup of 8 waves owns 128 weight rows (gate/up: 16 rows of gate and
-// of up per wave) or 256 weight rows (down, router: 32 rows per wave) of one
-// expert and one tile of that expert's bucket of routes.  Every lane
-// dequantises its own weight blocks straight into MFMA operand registers,
-// one MFMA k-step at a time, and reuses them for all token tiles of the
-// tile.  Dequantisation is vector-ALU work that shares the SIMD's issue
-// slots with the MFMAs, so a routed bf16 tile holds 96 token rows: about one
-// whole bucket at the usual prefill load, so that each weight block is
-// dequantised once per expert.
+// of up per wave) or 256 weight rows (down: 32 rows per wave) of one expert
+// and one tile of that expert's bucket of routes.  Every lane dequantises its
+// own weight blocks straight into MFMA operand registers, one MFMA k-step at
+// a time, and reuses them for all token tiles of the tile.  Dequantisation
+// is vector-ALU work that shares the SIMD's issue slots with the MFMAs, so a
+// routed bf16 tile holds 96 token rows: about one whole bucket at the usual
+// prefill load, so that each weight block is dequantised once per expert.
 //
 // Routed bf16 tiles: the gathered token rows of each 128-wide slice of the
 // contraction axis go from global memory straight into LDS (one 16-byte
 // direct-to-LDS load per lane and piece) through a three-stage ring, two
 // slices ahead; weight blocks are loaded one slice ahead into registers.
 // The K loop is unrolled at compile time, so every wait is an exact count of
-// the loads still allowed in flight.  The other cases (dense weights, fp32
-// activations, odd shapes) stage the token rows through registers into a
+// the loads still allowed in flight.  The other cases (fp32 activations,
+// routed or shared, and contractions the unrolled loop does not cover)
+// stage the token rows through registers into a
 // double-buffered LDS tile (rows padded so the fragment reads are
 // bank-conflict free).  The down projection writes one fp32 row per route;
 // the combine kernel then sums each token's K rows in rank order on top of
@@ -35,8 +35,7 @@ enum Mode {
   kRoutedGateUp = 0,
   kSharedGateUp = 1,
   kRoutedDown = 2,
-  kSharedDown = 3,
-  kRouterApprox = 4
+  kSharedDown = 3
 };
 
 struct PArgs {
@@ -46,11 +45,8 @@ struct PArgs {
   const int32_t* sorted;
   const int32_t* tier_map;
   int E, K, T, H, I;
-  const void* src;       // x (gate/up, router) or h (down)
-  void* dst;             // h / fp32 route rows / fp32 shared rows / fp32 approximate keys
-  const void* wdense;    // router weights (kRouterApprox)
-  const float* bias;     // router bias or null (kRouterApprox)
-  float* wnorm2;         // router: squared row norms (kRouterApprox)
+  const void* src;       // x (gate/up) or h (down)
+  void* dst;             // h / fp32 route rows / fp32 shared rows
   Tables tb;
 };
 
@@ -67,12 +63,13 @@ template <> struct PT<float> {
   static constexpr int RU = 128 + 4;
 };
 
-// Token rows per workgroup: 64 keeps a routed workgroup within 128 VGPRs
-// (two resident per CU) and gives the dense modes (router, shared expert)
-// 64 token tiles, enough to fill 256 CUs at a 4096-token prefill.
+// Token rows per pass of the register-staged body: 64 keeps a routed
+// workgroup within its register budget; the fp32 shared-expert modes take 32
+// rows, so that a 4096-token prefill still has 128 token tiles to spread.
 template <typename A, int MODE> struct PR {
-  static constexpr int ROWS = (MODE == 0 || MODE == 2 || sizeof(A) == 2) ? PT<A>::ROWS
-                                                                        : PT<A>::ROWS / 2;
+  static constexpr int ROWS = (MODE == kRoutedGateUp || MODE == kRoutedDown || sizeof(A) == 2)
+                                  ? PT<A>::ROWS
+                                  : PT<A>::ROWS / 2;
 };
 
 template <int MODE> struct MC {
@@ -146,19 +143,15 @@ __device__ __forceinline__ void prefill_body(const PArgs& a, int grp, int row0, 
   constexpr int PARTS = kThreads / ROWS;                 // threads staging one row
   constexpr int U4 = 128 * (int)sizeof(A) / 16 / PARTS;  // uint4 per staging thread
   const int Kc = MODE == kRoutedDown || MODE == kSharedDown ? a.I : a.H;
-  const int Nr = C::GATEUP ? a.I : (MODE == kRouterApprox ? a.E : a.H);
+  const int Nr = C::GATEUP ? a.I : a.H;
   const int nbg = Kc / 128;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lm = lane & 15, lg = lane >> 4;
   const A* src = reinterpret_cast<const A*>(a.src);
   const int n0 = nt * C::NWG + wave * RGW * 16;           // first weight row of this wave
-  const bool active = n0 < Nr;                            // router: E may be < NWG
+  const bool active = n0 < Nr;                            // down: H may be < NWG
   const int srow = threadIdx.x / PARTS, spart = threadIdx.x % PARTS;
 
-  auto dense_of = [&](int m) -> const void* {
-    if constexpr (MODE == kRouterApprox) return a.wdense;
-    else return a.tb.dense[C::GATEUP ? m : MOE_DOWN];
-  };
   auto load_b = [&](BRaw<A, BITS> (&r)[RGW][NMAT], int c) {
     if (!active) return;
 #pragma unroll
@@ -166,7 +159,7 @@ __device__ __forceinline__ void prefill_body(const PArgs& a, int grp, int row0, 
 #pragma unroll
       for (int m = 0; m < NMAT; m++)
         load_braw<A, BITS>(r[q][m], a.tb, tier, C::GATEUP ? m : MOE_DOWN, slot, Nr, Kc,
-                           n0 / 16 + q, c, lane, dense_of(m));
+                           n0 / 16 + q, c, lane, a.tb.dense[C::GATEUP ? m : MOE_DOWN]);
   };
 
   for (int pass0 = 0; pass0 < nrows; pass0 += ROWS) {
@@ -204,7 +197,6 @@ __device__ __forceinline__ void prefill_body(const PArgs& a, int grp, int row0, 
       for (int m = 0; m < NMAT; m++)
 #pragma unroll
         for (int t = 0; t < MT; t++) acc[q][m][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float wsq[RGW] = {};
 
     uint4 ra[U4];
     BRaw<A, BITS> rb[RGW][NMAT];
@@ -225,17 +217,7 @@ __device__ __forceinline__ void prefill_body(const PArgs& a, int grp, int row0, 
 #pragma unroll
         for (int q = 0; q < RGW; q++)
 #pragma unroll
-          for (int m = 0; m < NMAT; m++) {
-            to_bfrag<A, BITS>(bf[q][m], rb[q][m]);
-            if constexpr (MODE == kRouterApprox) {
-#pragma unroll
-              for (int i = 0; i < 16; i++) {
-                const float lo = bf16_lo(bf[q][m].v[i]), hi = bf16_hi(bf[q][m].v[i]);
-                wsq[q] = __builtin_fmaf(lo, lo, wsq[q]);
-                wsq[q] = __builtin_fmaf(hi, hi, wsq[q]);
-              }
-            }
-          }
+          for (int m = 0; m < NMAT; m++) to_bfrag<A, BITS>(bf[q][m], rb[q][m]);
         const uint32_t* buf = sA + (c & 1) * ROWS * RU;
 #pragma unroll
         for (int t = 0; t < MT; t++) {
@@ -276,18 +258,6 @@ __device__ __forceinline__ void prefill_body(const PArgs& a, int grp, int row0, 
     }
 
     if (!active) continue;
-    if constexpr (MODE == kRouterApprox) {
-      if (grp == 0 && pass0 == 0) {  // the first token chunk publishes the row norms
-#pragma unroll
-        for (int q = 0; q < RGW; q++) {
-          float v = wsq[q];
-          v += __shfl_xor(v, 16, 64);
-          v += __shfl_xor(v, 32, 64);
-          const int n = n0 + 16 * q + lm;
-          if (lg == 0 && n < Nr) a.wnorm2[n] = v;
-        }
-      }
-    }
     // epilogue
 #pragma unroll
     for (int t = 0; t < MT; t++) {
@@ -305,9 +275,6 @@ __device__ __forceinline__ void prefill_body(const PArgs& a, int grp, int row0, 
             const float v = silu_f32(acc[q][0][t][i]) * acc[q][1][t][i];
             A* out = reinterpret_cast<A*>(a.dst) + (size_t)gp * a.I + n;
             if constexpr (sizeof(A) == 2) *out = to_bf16(v); else *out = v;
-          } else if constexpr (MODE == kRouterApprox) {
-            reinterpret_cast<float*>(a.dst)[(size_t)gp * a.E + n] =
-                acc[q][0][t][i] + (a.bias ? a.bias[n] : 0.0f);
           } else {
             reinterpret_cast<float*>(a.dst)[(size_t)gp * a.H + n] = acc[q][0][t][i];
           }
@@ -375,7 +342,7 @@ __device__ __forceinline__ void prefill_body_lds(const PArgs& a, int grp, int ro
   constexpr int LA = kPieces / kThreads;                          // A loads per wave per chunk
   constexpr int LB = RGW * NMAT * (BITS == 0 ? 2 * (int)sizeof(A) : 2);  // B loads per wave per chunk
   const int Kc = MODE == kRoutedDown || MODE == kSharedDown ? a.I : a.H;
-  const int Nr = C::GATEUP ? a.I : (MODE == kRouterApprox ? a.E : a.H);
+  const int Nr = C::GATEUP ? a.I : a.H;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lm = lane & 15, lg = lane >> 4;
   const A* src = reinterpret_cast<const A*>(a.src);
@@ -511,7 +478,7 @@ __device__ __forceinline__ void prefill_wg(const PArgs& a) {
   // routed modes: rows per tile of the sorted routes (the register-staged
   // body walks a tile in passes of ROWS)
   constexpr int TILE = sizeof(A) == 2 ? kTileRows : ROWS;
-  const int Nr = C::GATEUP ? a.I : (MODE == kRouterApprox ? a.E : a.H);
+  const int Nr = C::GATEUP ? a.I : a.H;
   const int NT = (Nr + C::NWG - 1) / C::NWG;
   // XCD-aware mapping: the workgroups that share one expert's (or one token
   // chunk's) rows land on the same XCD, whose L2 then serves the re-reads.
@@ -546,8 +513,7 @@ __device__ __forceinline__ void prefill_wg(const PArgs& a) {
   } else {
     const int row0 = grp * ROWS;
     if (row0 >= a.T) return;
-    // dense weights (router, shared expert): register-staged pipeline (three
-    // dense weight slots would not fit the register budget)
+    // shared expert with fp32 activations: dense weights, register-staged
     __shared__ uint32_t sA[2 * ROWS * PT<A>::RU];
     prefill_body<A, 0, MODE>(a, grp, row0, min(ROWS, a.T - row0), 0, 0, nt, sA);
   }
@@ -567,17 +533,15 @@ __global__ __launch_bounds__(kThreads) void k_prefill_f32(PArgs a) {
 template <typename A, int MODE>
 void launch_mode(const PArgs& a, int n_groups, hipStream_t s) {
   using C = MC<MODE>;
-  const int Nr = C::GATEUP ? a.I : (MODE == kRouterApprox ? a.E : a.H);
+  const int Nr = C::GATEUP ? a.I : a.H;
   const int NT = (Nr + C::NWG - 1) / C::NWG;
   dim3 grid(((n_groups + 7) / 8) * 8 * NT);
   constexpr int kid = MODE == kRoutedGateUp   ? MOE_K_PREFILL_GATEUP
                       : MODE == kSharedGateUp ? MOE_K_PREFILL_SHARED_GATEUP
                       : MODE == kSharedDown   ? MOE_K_PREFILL_SHARED_DOWN
-                      : MODE == kRoutedDown   ? MOE_K_PREFILL_DOWN
-                                              : MOE_K_ROUTER_APPROX;
-  if constexpr (sizeof(A) == 2 && !C::ROUTED) {
-    MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 0>), grid, dim3(kThreads), 0, s, a);
-  } else if constexpr (sizeof(A) == 2) {
+                                              : MOE_K_PREFILL_DOWN;
+  static_assert(sizeof(A) == 4 || C::ROUTED, "bf16 shared GEMMs run on the dense kernels");
+  if constexpr (sizeof(A) == 2) {
     int nbg = 0;
     const int k = (MODE == kRoutedDown ? a.I : a.H) / 128;
     if (Nr % C::NWG == 0 && (k & (k - 1)) == 0 && k <= 32) nbg = k;
@@ -610,9 +574,6 @@ PArgs make_args(const int32_t* offsets, const int32_t* sorted, const int32_t* ti
   a.I = I;
   a.src = src;
   a.dst = dst;
-  a.wdense = nullptr;
-  a.bias = nullptr;
-  a.wnorm2 = nullptr;
   a.tb = tb;
   return a;
 }
@@ -661,21 +622,6 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ share
 
 }  // namespace
 
-void launch_router_approx(const void* x, int T, const void* w_router, const float* bias, int E,
-                          int H, float* keys_approx, float* wnorm2, hipStream_t s) {
-  if (dense_supported(H)) {
-    launch_dense_router(x, T, w_router, bias, E, H, keys_approx, wnorm2, s);
-    return;
-  }
-  Tables tb = {};
-  PArgs a = make_args(nullptr, nullptr, nullptr, E, 0, T, H, 0, x, keys_approx, tb);
-  a.wdense = w_router;
-  a.bias = bias;
-  a.wnorm2 = wnorm2;
-  constexpr int R = PR<bf16_t, kRouterApprox>::ROWS;
-  launch_mode<bf16_t, kRouterApprox>(a, (T + R - 1) / R, s);
-}
-
 int prefill_tile_rows(int act) {
   return act == MOE_BF16 ? kTileRows : PR<float, kRoutedGateUp>::ROWS;
 }
@@ -691,27 +637,28 @@ void launch_prefill_gateup(int act, const int32_t* offsets, const int32_t* sorte
   else launch_mode<float, kRoutedGateUp>(a, max_tiles, s);
 }
 
+// The shared expert's bf16 GEMMs run on the dense kernels (kernels_dense.hip);
+// fp32 activations take the register-staged body with dense weights.
 void launch_prefill_shared_gateup(int act, const void* x, int T, const Tables& tb, void* h_s,
                                   int H, int I, hipStream_t s) {
-  if (act == MOE_BF16 && dense_supported(H)) {
+  if (act == MOE_BF16) {
     launch_dense_shared_gateup(x, T, tb.dense[MOE_GATE], tb.dense[MOE_UP], h_s, H, I, s);
     return;
   }
   const PArgs a = make_args(nullptr, nullptr, nullptr, 0, 0, T, H, I, x, h_s, tb);
-  constexpr int RB = PR<bf16_t, kSharedGateUp>::ROWS, RF = PR<float, kSharedGateUp>::ROWS;
-  if (act == MOE_BF16) launch_mode<bf16_t, kSharedGateUp>(a, (T + RB - 1) / RB, s);
-  else launch_mode<float, kSharedGateUp>(a, (T + RF - 1) / RF, s);
+  constexpr int R = PR<float, kSharedGateUp>::ROWS;
+  launch_mode<float, kSharedGateUp>(a, (T + R - 1) / R, s);
 }
 
 void launch_prefill_shared_down(int act, const void* h_s, int T, const Tables& tb, float* rows,
                                 int H, int I, hipStream_t s) {
-  if (act == MOE_BF16 && dense_supported(I)) {
+  if (act == MOE_BF16) {
     launch_dense_shared_down(h_s, T, tb.dense[MOE_DOWN], rows, H, I, s);
     return;
   }
   const PArgs a = make_args(nullptr, nullptr, nullptr, 0, 0, T, H, I, h_s, rows, tb);
-  if (act == MOE_BF16) launch_mode<bf16_t, kSharedDown>(a, (T + PR<bf16_t, kSharedDown>::ROWS - 1) / PR<bf16_t, kSharedDown>::ROWS, s);
-  else launch_mode<float, kSharedDown>(a, (T + PR<float, kSharedDown>::ROWS - 1) / PR<float, kSharedDown>::ROWS, s);
+  constexpr int R = PR<float, kSharedDown>::ROWS;
+  launch_mode<float, kSharedDown>(a, (T + R - 1) / R, s);
 }
 
 

@@ -417,7 +417,7 @@ int moe_route(const moe_dims* dims, const moe_layer* layer, const void* x, int32
     // fp32 keys and row norms fit in the space of the float64 keys)
     float* approx = reinterpret_cast<float*>(base + w.keys);
     float* wnorm2 = approx + (size_t)T * E;
-    launch_router_approx(x, T, layer->w_router, layer->b_router, E, H, approx, wnorm2, stream);
+    launch_dense_router(x, T, layer->w_router, layer->b_router, E, H, approx, wnorm2, stream);
     launch_topk_recheck(x, layer->w_router, layer->b_router, approx, wnorm2, T, H, E, K, topk_ids,
                         topk_w, stream);
     return hip_status();
@@ -514,7 +514,7 @@ int moe_forward_prefill(const moe_dims* dims, const moe_layer* layer, const void
   if (mfma_router(dims)) {
     float* approx = reinterpret_cast<float*>(base + w.approx);
     float* wnorm2 = reinterpret_cast<float*>(base + w.wnorm2);
-    launch_router_approx(x, T, layer->w_router, layer->b_router, E, H, approx, wnorm2, stream);
+    launch_dense_router(x, T, layer->w_router, layer->b_router, E, H, approx, wnorm2, stream);
     launch_topk_recheck(x, layer->w_router, layer->b_router, approx, wnorm2, T, H, E, K, ids, wts,
                         stream);
   } else {
