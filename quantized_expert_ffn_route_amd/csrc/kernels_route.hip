@@ -693,17 +693,27 @@ __global__ __launch_bounds__(256) void k_sort_count(const int32_t* __restrict__ 
 // Bucket offsets (exclusive scan of the per-expert totals), each chunk's
 // base inside every bucket, and the GEMM tile list: bucket e splits into
 // ceil(n_e / tile_rows) tiles, recorded as (e, first row of the tile inside
-// the bucket) in expert order.  chunk_base holds the counts on entry.  One
-// workgroup; E <= 4096.
+// the bucket).  Longest first: the full tiles of every bucket (expert
+// order), then the ragged last tiles of more than half a tile, then the
+// rest, so the short workgroups fill the end of the grouped GEMMs.
+// chunk_base holds the counts on entry.  One workgroup; E <= 4096.
+// Class of a bucket's ragged last tile: 1 when it holds more than half a
+// tile of rows, 1 << 16 when it holds fewer, 0 when there is none.
+__device__ __forceinline__ int tile_class(int n_e, int tile_rows) {
+  const int r = n_e % tile_rows;
+  return r == 0 ? 0 : (2 * r > tile_rows ? 1 : 1 << 16);
+}
+
 __global__ __launch_bounds__(1024) void k_sort_scan(int n_chunks, int E, int tile_rows,
                                                     int32_t* __restrict__ chunk_base,
                                                     int32_t* __restrict__ offsets,
                                                     int2* __restrict__ tiles,
                                                     int32_t* __restrict__ n_tiles) {
   __shared__ int32_t s_tot[4096];
-  __shared__ int32_t s_til[4096];
-  __shared__ int32_t s_wave[16][2];
-  __shared__ int32_t s_total;
+  __shared__ int32_t s_til[4096];   // full tiles of the bucket, then their scan
+  __shared__ int32_t s_prt[4096];   // ragged tile: 1 (long) or 1 << 16 (short), then the scan
+  __shared__ int32_t s_wave[16][3];
+  __shared__ int32_t s_total, s_full, s_long;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   // one expert per thread and at most 64 chunks (4096 tokens): every count is
   // loaded at once and kept in registers for the second pass
@@ -719,7 +729,8 @@ __global__ __launch_bounds__(1024) void k_sort_scan(int n_chunks, int E, int til
 #pragma unroll
       for (int c = 0; c < CMAX; c++) sum += c < n_chunks ? rc[c] : 0;
       s_tot[tid] = sum;
-      s_til[tid] = (sum + tile_rows - 1) / tile_rows;
+      s_til[tid] = sum / tile_rows;
+      s_prt[tid] = tile_class(sum, tile_rows);
     }
   }
   // otherwise: per-expert totals over the chunks, 8 loads in flight per thread
@@ -737,41 +748,49 @@ __global__ __launch_bounds__(1024) void k_sort_scan(int n_chunks, int E, int til
         if (c0 + j < n_chunks) sum += v[j];
     }
     s_tot[e] = sum;
-    s_til[e] = (sum + tile_rows - 1) / tile_rows;
+    s_til[e] = sum / tile_rows;
+    s_prt[e] = tile_class(sum, tile_rows);
   }
   __syncthreads();
-  // exclusive scans of s_tot and s_til, 4 consecutive experts per thread
-  int v[4], u[4];
-  int local = 0, ulocal = 0;
+  // exclusive scans of s_tot, s_til and s_prt (two 16-bit counts packed;
+  // each stays <= E), 4 consecutive experts per thread
+  int v[4], u[4], w[4];
+  int local = 0, ulocal = 0, wlocal = 0;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int e = tid * 4 + j;
     v[j] = e < E ? s_tot[e] : 0;
     u[j] = e < E ? s_til[e] : 0;
+    w[j] = e < E ? s_prt[e] : 0;
     local += v[j];
     ulocal += u[j];
+    wlocal += w[j];
   }
-  int incl = local, uincl = ulocal;
+  int incl = local, uincl = ulocal, wincl = wlocal;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int o = __shfl_up(incl, off, 64);
     const int uo = __shfl_up(uincl, off, 64);
+    const int wo = __shfl_up(wincl, off, 64);
     if (lane >= off) {
       incl += o;
       uincl += uo;
+      wincl += wo;
     }
   }
   if (lane == 63) {
     s_wave[wv][0] = incl;
     s_wave[wv][1] = uincl;
+    s_wave[wv][2] = wincl;
   }
   __syncthreads();
-  int wbase = 0, ubase = 0;
+  int wbase = 0, ubase = 0, pbase = 0;
   for (int i = 0; i < wv; i++) {
     wbase += s_wave[i][0];
     ubase += s_wave[i][1];
+    pbase += s_wave[i][2];
   }
-  int run = wbase + incl - local, urun = ubase + uincl - ulocal;
+  int run = wbase + incl - local, urun = ubase + uincl - ulocal, wrun = pbase + wincl - wlocal;
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 4; j++) {
@@ -779,21 +798,31 @@ __global__ __launch_bounds__(1024) void k_sort_scan(int n_chunks, int E, int til
     if (e < E) {
       s_tot[e] = run;
       s_til[e] = urun;
+      s_prt[e] = wrun;
     }
     run += v[j];
     urun += u[j];
+    wrun += w[j];
   }
   if (tid == blockDim.x - 1) {
     offsets[E] = run;
-    *n_tiles = urun;
+    *n_tiles = urun + (wrun & 0xFFFF) + (wrun >> 16);
     s_total = run;
+    s_full = urun;
+    s_long = wrun & 0xFFFF;
   }
   __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) {
     const int base0 = s_tot[e];
     offsets[e] = base0;
     const int n_e = (e + 1 < E ? s_tot[e + 1] : s_total) - base0;
-    for (int p = 0; p * tile_rows < n_e; p++) tiles[s_til[e] + p] = make_int2(e, p * tile_rows);
+    const int nf = n_e / tile_rows, r = n_e - nf * tile_rows;
+    for (int p = 0; p < nf; p++) tiles[s_til[e] + p] = make_int2(e, p * tile_rows);
+    if (r > 0) {
+      const int pr = s_prt[e];
+      const int pos = 2 * r > tile_rows ? s_full + (pr & 0xFFFF) : s_full + s_long + (pr >> 16);
+      tiles[pos] = make_int2(e, nf * tile_rows);
+    }
     int base = base0;
     if (regs) {
 #pragma unroll
