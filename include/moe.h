@@ -233,9 +233,9 @@ int moe_forward_decode(const moe_dims* dims, const moe_layer* layer, const void*
  * offsets[e]..offsets[e+1] in ascending r), the grouping the batched path
  * needs ([P1] "the four bugs, briefly").  Each expert's bucket then runs a
  * grouped GEMM on bf16 MFMA (fp32 MFMA for f32 activations) with weights
- * dequantised on the fly; the down projection is scattered into y weighted
- * by topk_w with fp32 atomics on top of the shared expert's output, so the
- * summation order of y varies between runs (within fp32 rounding).
+ * dequantised on the fly; the down projection writes one fp32 row per route,
+ * and each token's K rows are then added in rank order, weighted by topk_w,
+ * on top of the shared expert's output.  Deterministic (no atomics).
  *
  *   topk_ids, topk_w, expert_offsets, sorted_routes: optional device outputs
  *   (may be NULL).
