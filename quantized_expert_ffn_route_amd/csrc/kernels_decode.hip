@@ -644,6 +644,125 @@ __global__ __launch_bounds__(1024) void k_decode_down(const Item* __restrict__ i
   }
 }
 
+// One bf16 token: two work items per MFMA.  Token row 0 of the A operand
+// carries item X's h row and row 1 item Y's; weight-column lanes 0-7 hold
+// this workgroup's eight rows of X, lanes 8-15 the same rows of Y, so every
+// lane loads and dequantises a real block (the general kernel leaves half
+// the lanes at zero).  C[0][n < 8] and C[1][n >= 8] are the two items'
+// partial rows; the cross terms are not used.  X and Y always share a tier
+// (the pairing below), so the dequantisation path is uniform per wave.
+template <typename Y>
+__global__ __launch_bounds__(1024) void k_decode1_down(const Item* __restrict__ items,
+                                                       const int32_t* __restrict__ n_items,
+                                                       int max_items, const bf16_t* __restrict__ h,
+                                                       int h_rows, Tables tb, Y* __restrict__ y,
+                                                       int H, int I) {
+  __shared__ float red[16][16];
+  __shared__ int8_t s_pair[64][2];
+  __shared__ int s_npairs;
+  extern __shared__ uint4 s_dyn[];
+  Item* s_items = reinterpret_cast<Item*>(s_dyn);
+  const bf16_t* s_h = reinterpret_cast<const bf16_t*>(s_dyn + (size_t)max_items * (sizeof(Item) / 16));
+  const int rg = blockIdx.x >> 1, half = blockIdx.x & 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, NW = blockDim.x >> 6;
+  const int lm = lane & 15, lg = lane >> 4;
+  const int nbg = I / 128, nrg = H / 16;
+  {
+    const int nh = max_items * (int)(sizeof(Item) / 16);
+    const int n16 = h_rows * I * (int)sizeof(bf16_t) / 16;
+    const uint4* si = reinterpret_cast<const uint4*>(items);
+    const uint4* sh = reinterpret_cast<const uint4*>(h);
+    for (int i = threadIdx.x; i < nh + n16; i += blockDim.x)
+      s_dyn[i] = i < nh ? si[i] : sh[i - nh];
+  }
+  const int n = min(*n_items, 64);
+  __syncthreads();
+  if (wave == 0) {
+    // pair the items of each tier (dense last) in item order; an odd one out
+    // pairs with nothing.  Lane i holds item i (n <= 64).
+    const int t = lane < n ? s_items[lane].tier : -1;
+    const int cls = t == kDenseTier ? 3 : (t >= 0 && t < 3 ? t : -1);
+    const uint64_t below = (1ull << lane) - 1ull;
+    int base = 0, my_pair = -1, my_side = 0;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const uint64_t m = __ballot(cls == c);
+      if (cls == c) {
+        const int rank = __popcll(m & below);
+        my_pair = base + (rank >> 1);
+        my_side = rank & 1;
+      }
+      base += (__popcll(m) + 1) >> 1;
+    }
+    if (my_pair >= 0 && my_side == 0) {
+      s_pair[my_pair][0] = (int8_t)lane;
+      s_pair[my_pair][1] = (int8_t)-1;
+    }
+    if (my_pair >= 0 && my_side == 1) s_pair[my_pair][1] = (int8_t)lane;
+    if (lane == 0) s_npairs = base;
+  }
+  __syncthreads();
+  const int units = s_npairs * nbg;
+  float acc = 0.f;
+  constexpr int PB = 2;
+  for (int p0 = wave; p0 < units; p0 += NW * PB) {
+    Raw<bf16_t> raw[PB];
+#pragma unroll
+    for (int j = 0; j < PB; j++) {
+      const int p = p0 + NW * j;
+      if (p >= units) continue;
+      const int c = p % nbg;
+      const int it = s_pair[p / nbg][lm >> 3];
+#pragma unroll
+      for (int i = 0; i < 16; i++) raw[j].v[i] = 0u;
+      if (it < 0) continue;
+      const Item& item = s_items[it];
+      const int row = rg * 16 + half * 8 + (lm & 7);
+      if (item.tier == kDenseTier) {
+        load_raw_dense<bf16_t>(raw[j], reinterpret_cast<const bf16_t*>(tb.dense[MOE_DOWN]) +
+                                           (size_t)row * I + 128 * c + 32 * lg);
+      } else {
+        const size_t idx = (((size_t)item.slot * nrg + rg) * nbg + c) * 64 + 16 * lg + half * 8 + (lm & 7);
+        if (item.bits == 4) load_raw<bf16_t, 4>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
+        else if (item.bits == 3) load_raw<bf16_t, 3>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
+        else load_raw<bf16_t, 2>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PB; j++) {
+      const int p = p0 + NW * j;
+      if (p >= units) continue;
+      const int c = p % nbg;
+      const int ix = s_pair[p / nbg][0], iy = s_pair[p / nbg][1];
+      // A: row 0 = h of X, row 1 = h of Y (lanes with lm >= 2 carry zeros)
+      const int ia = lm == 0 ? ix : (lm == 1 ? iy : -1);
+      Frag<bf16_t> ha;
+      ha.load_act(s_h + (size_t)(ia >= 0 ? s_items[ia].route[0] : 0) * I + 128 * c + 32 * lg, ia >= 0);
+      const Item& hx = s_items[ix];           // the pair's tier (X always exists)
+      Frag<bf16_t> b;
+      if (hx.tier == kDenseTier) to_frag<bf16_t, 0>(b, raw[j]);
+      else if (hx.bits == 4) to_frag<bf16_t, 4>(b, raw[j]);
+      else if (hx.bits == 3) to_frag<bf16_t, 3>(b, raw[j]);
+      else to_frag<bf16_t, 2>(b, raw[j]);
+      const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+      const f32x4_t part = mma_step(ha, b, z);
+      // lanes 0-7: C[0][lane] (item X); lanes 8-15: C[1][lane] (item Y)
+      const int mine = lm < 8 ? ix : iy;
+      if (lg == 0 && mine >= 0) acc += s_items[mine].gw[0] * (lm < 8 ? part[0] : part[1]);
+    }
+  }
+  if (lane < 16) red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0 || lane >= 8) return;
+  float sum = 0.f;
+#pragma unroll
+  for (int w = 0; w < 16; w++) {
+    if (w < NW) sum += red[w][lane] + red[w][lane + 8];
+  }
+  Y* out = y + rg * 16 + half * 8 + lane;
+  if constexpr (sizeof(Y) == 4) *out = sum; else *out = to_bf16(sum);
+}
+
 }  // namespace
 
 void launch_decode_gateup(int act, const Item* items, const int32_t* n_items, int max_items,
@@ -720,6 +839,16 @@ void launch_decode_down(int act, int y_dt, const Item* items, const int32_t* n_i
   const size_t stage_bytes = (size_t)h_rows * I * (act == MOE_BF16 ? 2 : 4);
   const bool stage = act == MOE_BF16 && item_bytes + stage_bytes <= 48 * 1024;
   const size_t lds = item_bytes + (stage ? stage_bytes : 0);
+  if (T == 1 && act == MOE_BF16 && stage && max_items <= 64) {
+    // one token: two items per MFMA, no zero lanes
+    if (y_dt == MOE_BF16)
+      MOE_LAUNCH(MOE_K_DECODE_DOWN, k_decode1_down<bf16_t>, grid, dim3(1024), lds, s, items,
+                 n_items, max_items, (const bf16_t*)h, h_rows, tb, (bf16_t*)y, H, I);
+    else
+      MOE_LAUNCH(MOE_K_DECODE_DOWN, k_decode1_down<float>, grid, dim3(1024), lds, s, items,
+                 n_items, max_items, (const bf16_t*)h, h_rows, tb, (float*)y, H, I);
+    return;
+  }
 #define MOE_DN(AT, YT, PB, ST)                                                                 \
   MOE_LAUNCH(MOE_K_DECODE_DOWN, (k_decode_down<AT, YT, PB, ST>), grid, block, lds, s, items,   \
              n_items, max_items, (const AT*)h, h_rows, T, tb, (YT*)y, H, I)
