@@ -551,7 +551,9 @@ __global__ __launch_bounds__(1024) void k_decode_down(const Item* __restrict__ i
   extern __shared__ uint4 s_dyn[];
   Item* s_items = reinterpret_cast<Item*>(s_dyn);
   const A* s_h = reinterpret_cast<const A*>(s_dyn + (size_t)max_items * (sizeof(Item) / 16));
-  const int rg = blockIdx.x >> 1, half = blockIdx.x & 1;
+  // the two row halves of a tile sit 8 apart in the grid, on one XCD, so its
+  // lines are fetched from HBM once (the grid is a multiple of 16)
+  const int rg = ((blockIdx.x >> 4) << 3) | (blockIdx.x & 7), half = (blockIdx.x >> 3) & 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, NW = blockDim.x >> 6;
   const int lm = lane & 15, lg = lane >> 4;
   const bool mine = (lm >> 3) == half;
@@ -663,7 +665,9 @@ __global__ __launch_bounds__(1024) void k_decode1_down(const Item* __restrict__ 
   extern __shared__ uint4 s_dyn[];
   Item* s_items = reinterpret_cast<Item*>(s_dyn);
   const bf16_t* s_h = reinterpret_cast<const bf16_t*>(s_dyn + (size_t)max_items * (sizeof(Item) / 16));
-  const int rg = blockIdx.x >> 1, half = blockIdx.x & 1;
+  // the two row halves of a tile sit 8 apart in the grid, on one XCD, so its
+  // lines are fetched from HBM once (the grid is a multiple of 16)
+  const int rg = ((blockIdx.x >> 4) << 3) | (blockIdx.x & 7), half = (blockIdx.x >> 3) & 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, NW = blockDim.x >> 6;
   const int lm = lane & 15, lg = lane >> 4;
   const int nbg = I / 128, nrg = H / 16;
