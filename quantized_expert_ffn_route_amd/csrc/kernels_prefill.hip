@@ -132,7 +132,7 @@ __device__ __forceinline__ void to_bfrag(BFrag<A>& f, const BRaw<A, BITS>& r) {
 }
 
 // One workgroup's work: weight rows [nt*NWG, nt*NWG + NWG) of one expert (or
-// of the shared expert / router) against `nrows` token rows starting at row0.
+// of the shared expert) against `nrows` token rows starting at row0.
 template <typename A, int BITS, int MODE>
 __device__ __forceinline__ void prefill_body(const PArgs& a, int grp, int row0, int nrows, int tier,
                                              int slot, int nt, uint32_t* __restrict__ sA) {
