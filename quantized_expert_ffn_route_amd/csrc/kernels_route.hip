@@ -100,11 +100,13 @@ __global__ __launch_bounds__(256) void k_router_keys(const A* __restrict__ x, co
 // Decode variant (T <= 16, tokens fit in 64 KiB of LDS): two experts per
 // workgroup (one wave each), so the router rows spread over every CU.  Each
 // lane issues all loads of its router row first, then the group's tokens are
-// staged in LDS; both round trips overlap.  Same per-lane order and butterfly
-// as k_router_keys, so the keys are bit-identical.
+// staged in LDS; both round trips overlap.  A single token (ONE) skips the
+// staging: each lane loads its own chunks of x next to its router chunks, so
+// no barrier sits between the loads and the arithmetic.  Same per-lane order
+// and butterfly as k_router_keys, so the keys are bit-identical.
 constexpr int kRouterDecWaves = 2;
 
-template <typename A, int MAXC>
+template <typename A, int MAXC, bool ONE>
 __global__ __launch_bounds__(64 * kRouterDecWaves) void k_router_keys_dec(const A* __restrict__ x,
                                                                           const A* __restrict__ w,
                                                                           const float* __restrict__ bias,
@@ -123,6 +125,33 @@ __global__ __launch_bounds__(64 * kRouterDecWaves) void k_router_keys_dec(const 
     if (q < nchunk)
 #pragma unroll
       for (int u = 0; u < U4; u++) wraw[j][u] = reinterpret_cast<const uint4*>(wr + 8 * q)[u];
+  }
+  if constexpr (ONE) {
+    uint4 xraw[MAXC][U4];
+#pragma unroll
+    for (int j = 0; j < MAXC; j++) {
+      const int q = lane + 64 * j;
+      if (q < nchunk)
+#pragma unroll
+        for (int u = 0; u < U4; u++) xraw[j][u] = reinterpret_cast<const uint4*>(x + 8 * q)[u];
+    }
+    if (e >= E) return;
+    const double b = bias ? (double)bias[e] : 0.0;
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < MAXC; j++) {
+      const int q = lane + 64 * j;
+      if (q < nchunk) {
+        double wv[8], xv[8];
+        cvt8_f64<A>(wraw[j], wv);
+        cvt8_f64<A>(xraw[j], xv);
+#pragma unroll
+        for (int k = 0; k < 8; k++) acc = __builtin_fma(xv[k], wv[k], acc);
+      }
+    }
+    const double sum = wave_sum_f64(acc);
+    if (lane == 0) keys[e] = sum + b;
+    return;
   }
   const int n16 = T * H * (int)sizeof(A) / 16;
   for (int i = threadIdx.x; i < n16; i += blockDim.x) s_x[i] = reinterpret_cast<const uint4*>(x)[i];
@@ -158,9 +187,15 @@ void launch_router_keys(int act, const void* x, const void* w, const float* b, d
     dim3 grid((E + kRouterDecWaves - 1) / kRouterDecWaves);
     const int maxc = (H / 8 + 63) / 64;
 #define MOE_RK(AT, MC)                                                                          \
-  MOE_LAUNCH(MOE_K_ROUTER_KEYS, (k_router_keys_dec<AT, MC>), grid, dim3(64 * kRouterDecWaves), \
-             xbytes, s,                                                                         \
-             (const AT*)x, (const AT*)w, b, keys, T, H, E)
+  do {                                                                                          \
+    if (T == 1)                                                                                 \
+      MOE_LAUNCH(MOE_K_ROUTER_KEYS, (k_router_keys_dec<AT, MC, true>), grid,                    \
+                 dim3(64 * kRouterDecWaves), 0, s, (const AT*)x, (const AT*)w, b, keys, T, H, E); \
+    else                                                                                        \
+      MOE_LAUNCH(MOE_K_ROUTER_KEYS, (k_router_keys_dec<AT, MC, false>), grid,                   \
+                 dim3(64 * kRouterDecWaves), xbytes, s, (const AT*)x, (const AT*)w, b, keys, T, \
+                 H, E);                                                                         \
+  } while (0)
     if (act == MOE_BF16) {
       if (maxc <= 1) MOE_RK(bf16_t, 1);
       else if (maxc <= 2) MOE_RK(bf16_t, 2);
