@@ -146,6 +146,11 @@ void launch_topk_recheck(const void* x, const void* w, const float* bias, const 
 // keys_approx[t][e] = fp32 x[t] . w[e] + b[e]; wnorm2[e] = |w[e]|^2 (fp32).
 void launch_dense_router(const void* x, int T, const void* w_router, const float* bias, int E,
                          int H, float* keys_approx, float* wnorm2, hipStream_t s);
+// Both of the above in one launch (they multiply the same token rows x).
+void launch_dense_router_shared_gateup(const void* x, int T, const void* w_router,
+                                      const float* bias, int E, int H, float* keys_approx,
+                                      float* wnorm2, const void* w_gate, const void* w_up,
+                                      void* h_s, int I, hipStream_t s);
 // h_s[t][i] = bf16(silu(x[t] . w_gate[i]) * (x[t] . w_up[i])).
 void launch_dense_shared_gateup(const void* x, int T, const void* w_gate, const void* w_up,
                                 void* h_s, int H, int I, hipStream_t s);

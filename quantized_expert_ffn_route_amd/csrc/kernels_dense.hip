@@ -30,7 +30,9 @@ constexpr int kDPPR = kDKC / 8;         // 16-byte pieces per row of a stage
 constexpr int kDRowsB = 128;            // weight rows per workgroup tile
 constexpr int kDStages = 3;
 
-enum DenseMode { kDRouter = 0, kDGateUp = 1, kDDown = 2 };
+// kDRouterGateUp: one launch over the router's column tiles followed by the
+// shared expert's gate/up column tiles -- both multiply the same token rows.
+enum DenseMode { kDRouter = 0, kDGateUp = 1, kDDown = 2, kDRouterGateUp = 3 };
 
 struct DArgs {
   const bf16_t* a;    // token rows [M][K]
@@ -41,6 +43,12 @@ struct DArgs {
   float* outf;        // router keys / shared rows, [M][N] fp32
   bf16_t* outh;       // gate/up activations, [M][N] bf16
   float* wnorm2;      // router: squared row norms [N]
+  // kDRouterGateUp: the gate/up part (b0/b1/outh above belong to the router
+  // then, as b0 / bias / outf / wnorm2 do)
+  const bf16_t* g_gate;
+  const bf16_t* g_up;
+  bf16_t* g_out;
+  int g_N;            // intermediate size
 };
 
 template <int N>
@@ -85,13 +93,25 @@ __global__ __launch_bounds__(kDThreads) void k_dense(DArgs a) {
   constexpr int STAGE = (APIECES + BPIECES) * 16;         // bytes
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[kDStages * STAGE];
 
-  const int ncols = MODE == kDGateUp ? kDRowsB / 2 : kDRowsB;   // output columns per workgroup
-  const int NT = (a.N + ncols - 1) / ncols;
+  constexpr bool COMB = MODE == kDRouterGateUp;
+  // column tiles: router tiles of kDRowsB columns, then (combined mode)
+  // gate/up tiles of kDRowsB / 2 columns
+  const int NTr = MODE == kDGateUp ? 0 : (a.N + kDRowsB - 1) / kDRowsB;
+  const int NTg = MODE == kDGateUp ? (a.N + kDRowsB / 2 - 1) / (kDRowsB / 2)
+                                   : (COMB ? (a.g_N + kDRowsB / 2 - 1) / (kDRowsB / 2) : 0);
+  const int NT = NTr + NTg;
   // XCD-aware order: workgroups go to the 8 XCDs round-robin, so all column
   // tiles of token tile mt run on XCD mt % 8 and share its L2 copy of the rows
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
   const int mt = (j / NT) * 8 + xcd, nt = j % NT;
-  const int m0 = mt * MROWS, n0 = nt * ncols;
+  // this workgroup's part: gate/up (gu) or router / down
+  const bool gu = MODE == kDGateUp || (COMB && nt >= NTr);
+  const int n0 = gu ? (nt - NTr) * (kDRowsB / 2) : nt * kDRowsB;
+  const int NN = COMB && gu ? a.g_N : a.N;                  // columns of this part
+  const bf16_t* bg = COMB ? a.g_gate : a.b0;
+  const bf16_t* bu = COMB ? a.g_up : a.b1;
+  bf16_t* outg = COMB ? a.g_out : a.outh;
+  const int m0 = mt * MROWS;
   if (m0 >= a.M) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lm = lane & 15, lg = lane >> 4;
@@ -114,13 +134,13 @@ __global__ __launch_bounds__(kDThreads) void k_dense(DArgs a) {
     const int r = q / kDPPR, p = (q % kDPPR) ^ dswz(r);
     const bf16_t* base;
     int gn;
-    if constexpr (MODE == kDGateUp) {
+    if (gu) {
       // rows [64 w, 64 w + 32): gate rows, [64 w + 32, 64 w + 64): up rows
       const int w = r >> 6, rr = r & 63;
-      gn = min(n0 + 32 * w + (rr & 31), a.N - 1);
-      base = rr < 32 ? a.b0 : a.b1;
+      gn = min(n0 + 32 * w + (rr & 31), NN - 1);
+      base = rr < 32 ? bg : bu;
     } else {
-      gn = min(n0 + r, a.N - 1);
+      gn = min(n0 + r, NN - 1);
       base = a.b0;
     }
     bsrc[j] = base + (size_t)gn * K + 8 * p;
@@ -161,7 +181,8 @@ __global__ __launch_bounds__(kDThreads) void k_dense(DArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; u++) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float wsq = 0.f;   // router: this thread's weight row norm (first token tile, threads < 128)
-  const bool norms = MODE == kDRouter && mt == 0 && a.wnorm2 != nullptr && threadIdx.x < kDRowsB;
+  const bool norms = (MODE == kDRouter || (COMB && !gu)) && mt == 0 && a.wnorm2 != nullptr &&
+                     threadIdx.x < kDRowsB;
 
   static_assert(kDStages - 2 <= 3, "dwait_chunks covers up to three chunks ahead");
   for (int c = 0; c < kDStages - 1 && c < NC; c++) issue(c, c);
@@ -200,7 +221,7 @@ __global__ __launch_bounds__(kDThreads) void k_dense(DArgs a) {
       }
     }
   }
-  if (norms && n0 + (int)threadIdx.x < a.N) a.wnorm2[n0 + threadIdx.x] = wsq;
+  if (norms && n0 + (int)threadIdx.x < NN) a.wnorm2[n0 + threadIdx.x] = wsq;
 
   // epilogue: lane holds C[4 lg + i][lm] of each 16x16 tile
 #pragma unroll
@@ -209,21 +230,21 @@ __global__ __launch_bounds__(kDThreads) void k_dense(DArgs a) {
     for (int i = 0; i < 4; i++) {
       const int m = m0 + wm * 16 * MTW + 16 * t + 4 * lg + i;
       if (m >= a.M) continue;
-      if constexpr (MODE == kDGateUp) {
+      if (gu) {
 #pragma unroll
         for (int u = 0; u < 2; u++) {
           const int n = n0 + wn * 32 + 16 * u + lm;
-          if (n < a.N)
-            a.outh[(size_t)m * a.N + n] = to_bf16(silu_f32(acc[t][u][i]) * acc[t][u + 2][i]);
+          if (n < NN)
+            outg[(size_t)m * NN + n] = to_bf16(silu_f32(acc[t][u][i]) * acc[t][u + 2][i]);
         }
       } else {
 #pragma unroll
         for (int u = 0; u < 4; u++) {
           const int n = n0 + wn * 64 + 16 * u + lm;
-          if (n < a.N) {
+          if (n < NN) {
             float v = acc[t][u][i];
-            if constexpr (MODE == kDRouter) v += a.bias ? a.bias[n] : 0.0f;
-            a.outf[(size_t)m * a.N + n] = v;
+            if constexpr (MODE == kDRouter || COMB) v += a.bias ? a.bias[n] : 0.0f;
+            a.outf[(size_t)m * NN + n] = v;
           }
         }
       }
@@ -233,8 +254,10 @@ __global__ __launch_bounds__(kDThreads) void k_dense(DArgs a) {
 
 template <int MODE, int MTW>
 void launch_dense(const DArgs& a, int kid, hipStream_t s) {
-  const int ncols = MODE == kDGateUp ? kDRowsB / 2 : kDRowsB;
-  const int NT = (a.N + ncols - 1) / ncols;
+  const int NTr = MODE == kDGateUp ? 0 : (a.N + kDRowsB - 1) / kDRowsB;
+  const int NTg = MODE == kDGateUp ? (a.N + kDRowsB / 2 - 1) / (kDRowsB / 2)
+                                   : (MODE == kDRouterGateUp ? (a.g_N + kDRowsB / 2 - 1) / (kDRowsB / 2) : 0);
+  const int NT = NTr + NTg;
   const int MTt = (a.M + 32 * MTW - 1) / (32 * MTW);
   if (MTt <= 0 || NT <= 0) return;
   // token tiles rounded up to a multiple of 8 (one per XCD); the extra ones exit
@@ -269,6 +292,22 @@ void launch_dense_shared_gateup(const void* x, int T, const void* w_gate, const 
   d.b1 = reinterpret_cast<const bf16_t*>(w_up);
   d.outh = reinterpret_cast<bf16_t*>(h_s);
   launch_dense<kDGateUp, 2>(d, MOE_K_PREFILL_SHARED_GATEUP, s);
+}
+
+void launch_dense_router_shared_gateup(const void* x, int T, const void* w_router,
+                                      const float* bias, int E, int H, float* keys_approx,
+                                      float* wnorm2, const void* w_gate, const void* w_up,
+                                      void* h_s, int I, hipStream_t s) {
+  DArgs d = dargs(x, T, E, H);
+  d.b0 = reinterpret_cast<const bf16_t*>(w_router);
+  d.bias = bias;
+  d.outf = keys_approx;
+  d.wnorm2 = wnorm2;
+  d.g_gate = reinterpret_cast<const bf16_t*>(w_gate);
+  d.g_up = reinterpret_cast<const bf16_t*>(w_up);
+  d.g_out = reinterpret_cast<bf16_t*>(h_s);
+  d.g_N = I;
+  launch_dense<kDRouterGateUp, 2>(d, MOE_K_ROUTER_APPROX, s);
 }
 
 void launch_dense_shared_down(const void* h_s, int T, const void* w_down, float* rows, int H,

@@ -511,10 +511,18 @@ int moe_forward_prefill(const moe_dims* dims, const moe_layer* layer, const void
   float* route_rows = reinterpret_cast<float*>(base + w.route_rows);
   float* shared_rows = dims->has_shared ? reinterpret_cast<float*>(base + w.shared_rows) : nullptr;
 
+  // bf16 with the MFMA router: the shared expert's gate/up rides in the
+  // router's launch (same token rows)
+  const bool shared_gu_done = mfma_router(dims) && dims->has_shared;
   if (mfma_router(dims)) {
     float* approx = reinterpret_cast<float*>(base + w.approx);
     float* wnorm2 = reinterpret_cast<float*>(base + w.wnorm2);
-    launch_dense_router(x, T, layer->w_router, layer->b_router, E, H, approx, wnorm2, stream);
+    if (shared_gu_done)
+      launch_dense_router_shared_gateup(x, T, layer->w_router, layer->b_router, E, H, approx,
+                                        wnorm2, tb.dense[MOE_GATE], tb.dense[MOE_UP], h_s, I,
+                                        stream);
+    else
+      launch_dense_router(x, T, layer->w_router, layer->b_router, E, H, approx, wnorm2, stream);
     launch_topk_recheck(x, layer->w_router, layer->b_router, approx, wnorm2, T, H, E, K, ids, wts,
                         stream);
   } else {
@@ -530,7 +538,7 @@ int moe_forward_prefill(const moe_dims* dims, const moe_layer* layer, const void
   launch_prefill_gateup(dims->act, offsets, sorted, tiles, n_tiles, w.max_tiles, layer->tier_map,
                         E, K, x, tb, h, H, I, stream);
   if (dims->has_shared) {
-    launch_prefill_shared_gateup(dims->act, x, T, tb, h_s, H, I, stream);
+    if (!shared_gu_done) launch_prefill_shared_gateup(dims->act, x, T, tb, h_s, H, I, stream);
     launch_prefill_shared_down(dims->act, h_s, T, tb, shared_rows, H, I, stream);
   }
   launch_prefill_down(dims->act, offsets, sorted, tiles, n_tiles, w.max_tiles, layer->tier_map, E,
