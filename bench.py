@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--prefill-steps", type=int, default=8)
     ap.add_argument("--prefill-tokens", type=int, default=4096)
-    ap.add_argument("--cpu-tokens", type=int, default=160)
+    ap.add_argument("--cpu-tokens", type=int, default=320)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
