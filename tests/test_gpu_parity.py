@@ -406,6 +406,78 @@ def test_decode_router_many_ties():
         check_y(y, ref["y"], "bf16", f"decode T={T}, 100 tied router rows")
 
 
+def test_router_nan_rows_rank_last():
+    # router rows of NaN give NaN keys, which rank below every number
+    # (moe_route's contract): the decode top-K and the prefill recheck both
+    # take their all-experts paths and must still pick the oracle's ids
+    def nan_rows(w_r, b):
+        w_r = w_r.copy()
+        w_r[[2, 9, 30]] = np.uint16(0x7FC0)          # bf16 quiet NaN
+        return w_r, b
+    tl = make_layer(MID, seed=9, router_override=nan_rows)
+    for T in (1, 3):
+        x = synth.tokens(MID, T, 50 + T)
+        y, ids, w = run_decode(tl, x)
+        _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, MID.top_k, exact=True)
+        np.testing.assert_array_equal(ids, oids)
+        assert not np.isin(ids, [2, 9, 30]).any()
+        assert np.max(np.abs(w - g)) <= 1e-6
+        ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+        check_y(y, ref["y"], "bf16", f"decode T={T}, NaN router rows")
+    x = synth.tokens(MID, 200, 53)
+    y, ids, w, _, _ = run_prefill(tl, x)
+    _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, MID.top_k, exact=True)
+    np.testing.assert_array_equal(ids, oids)
+    assert not np.isin(ids, [2, 9, 30]).any()
+    assert np.max(np.abs(w - g)) <= 1e-6
+    ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+    check_y(y, ref["y"], "bf16", "prefill, NaN router rows")
+
+
+# the largest top-K (64) over more experts than one workgroup holds keys for
+BIGK = synth.LayerSpec(hidden=256, inter=128, n_experts=1024, top_k=64, has_shared=False,
+                       act="bf16", n_slots=(256, 512, 256))
+# the largest hidden size: 64 chunks of 128 along the contraction
+MAXH = synth.LayerSpec(hidden=8192, inter=128, n_experts=8, top_k=2, has_shared=True,
+                       act="bf16", n_slots=(2, 4, 2))
+
+
+def test_top_k_64_of_1024_experts():
+    tl = make_layer(BIGK, seed=10)
+    for T in (1, 3):
+        x = synth.tokens(BIGK, T, 60 + T)
+        y, ids, w = run_decode(tl, x)
+        _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, BIGK.top_k, exact=True)
+        np.testing.assert_array_equal(ids, oids)
+        assert np.max(np.abs(w - g)) <= 1e-6
+        ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+        check_y(y, ref["y"], "bf16", f"decode T={T}, K=64 of E=1024")
+    x = synth.tokens(BIGK, 100, 63)
+    y, ids, w, _, _ = run_prefill(tl, x)
+    _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, BIGK.top_k, exact=True)
+    np.testing.assert_array_equal(ids, oids)
+    assert np.max(np.abs(w - g)) <= 1e-6
+    ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+    check_y(y, ref["y"], "bf16", "prefill T=100, K=64 of E=1024")
+
+
+def test_largest_hidden_size():
+    tl = make_layer(MAXH, seed=11)
+    for T in (1, 5):
+        x = synth.tokens(MAXH, T, 70 + T)
+        y, ids, w = run_decode(tl, x)
+        _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, MAXH.top_k, exact=True)
+        np.testing.assert_array_equal(ids, oids)
+        ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+        check_y(y, ref["y"], "bf16", f"decode T={T}, H=8192")
+    x = synth.tokens(MAXH, 70, 73)
+    y, ids, w, _, _ = run_prefill(tl, x)
+    _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, MAXH.top_k, exact=True)
+    np.testing.assert_array_equal(ids, oids)
+    ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+    check_y(y, ref["y"], "bf16", "prefill T=70, H=8192")
+
+
 def test_decode_equals_prefill(mid, full):
     for tl, T in ((mid, 16), (full, 8)):
         x = synth.tokens(tl.spec, T, 22)
