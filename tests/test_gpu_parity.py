@@ -442,6 +442,29 @@ MAXH = synth.LayerSpec(hidden=8192, inter=128, n_experts=8, top_k=2, has_shared=
                        act="bf16", n_slots=(2, 4, 2))
 
 
+# intermediate size 640 (down rows of 640, five chunks of 128), the width of
+# the pages' own model
+I640 = synth.LayerSpec(hidden=1024, inter=640, n_experts=32, top_k=4, has_shared=True,
+                       act="bf16", n_slots=(8, 16, 8))
+
+
+def test_intermediate_640():
+    tl = make_layer(I640, seed=12)
+    for T in (1, 7):
+        x = synth.tokens(I640, T, 80 + T)
+        y, ids, w = run_decode(tl, x)
+        _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, I640.top_k, exact=True)
+        np.testing.assert_array_equal(ids, oids)
+        ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+        check_y(y, ref["y"], "bf16", f"decode T={T}, I=640")
+    x = synth.tokens(I640, 150, 83)
+    y, ids, w, _, _ = run_prefill(tl, x)
+    _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, I640.top_k, exact=True)
+    np.testing.assert_array_equal(ids, oids)
+    ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+    check_y(y, ref["y"], "bf16", "prefill T=150, I=640")
+
+
 def test_top_k_64_of_1024_experts():
     tl = make_layer(BIGK, seed=10)
     for T in (1, 3):
