@@ -30,6 +30,9 @@ and ``tests/golden/``):
   strings, brute-force placement on tiny shapes).
 * ``dequantise``: pinned (hand blocks, exact fp64 identity).
 * ``build_tiers``: pinned (brute force, uniform popularity, bijection).
+* ``expert_table_bytes``/``plan_tiers``: pinned (closed forms at the budget
+  extremes, brute force over every per-expert assignment on tiny shapes, the
+  pages' greedy never beating it, budget monotonicity).
 * ``router_keys``/``select_topk``/``gate_weights``: pinned (math.fsum exact
   sums, brute-force tuple sort, exact ties, sum-to-one, K=1, K=E).
 * ``sort_routes``: pinned (lexsort of (route, expert), tiny brute force).

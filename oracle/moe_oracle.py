@@ -30,6 +30,8 @@ __all__ = [
     "dequantise",
     "pack_tiles",
     "build_tiers",
+    "expert_table_bytes",
+    "plan_tiers",
     "router_keys",
     "select_topk",
     "gate_weights",
@@ -287,6 +289,68 @@ def build_tiers(popularity, n_slots: Sequence[int]):
         tier = 0 if rank < starts[1] else (1 if rank < starts[2] else 2)
         tier_map[e] = (tier << 16) | (rank - starts[tier])
     return tier_map, np.asarray(order, dtype=np.int32)
+
+
+def expert_table_bytes(hidden: int, inter: int, bits: int) -> int:
+    """Bytes of one expert's three matrices (gate, up: inter x hidden; down:
+    hidden x inter) at `bits` bits: every block of 32 weights holds a
+    4*bits-byte code field and a 4-byte (d, m) word."""
+    return 3 * hidden * inter // BLOCK * (4 * bits + 4)
+
+
+#: Expected-error weight of a b-bit block per weight, scaled to integers:
+#: 11025 / (2^b - 1)^2 (11025 = 15^2 * 7^2), so 49, 225 and 1225 for 4, 3 and 2
+#: bits.
+ERR_WEIGHT = {4: 49, 3: 225, 2: 1225}
+
+
+def plan_tiers(popularity, tier_bits: Sequence[int], hidden: int, inter: int,
+               budget_bytes: int):
+    """Tier sizes (n0, n1, n2) that fit the expert tables in a byte budget.
+
+    The pages' re-packer fills a memory budget with a planner that gives each
+    byte to the expert where it removes the most expected error, weighting
+    the error by how often the expert is used [P1, "step 4: three shelves,
+    all on the GPU"; the command line of "reproduce it" takes the budget].
+    Readings (the pages give neither the error model nor the search):
+
+    - expected error of an expert at b bits = popularity x (2^b - 1)^-2: the
+      mean square error of a uniform b-bit quantiser over a block's range,
+      whose common factor (range^2 / 12 per weight) cancels.  With no
+      importance data, this width-only model is the only synthetic error
+      available;
+    - a plan is a set of popularity bands, the layout build_tiers stores:
+      ranks [0, n0) in tier 0, the next n1 in tier 1, the rest in tier 2;
+    - the plan minimises the total expected error among the band plans whose
+      tables take at most budget_bytes; equal errors prefer the larger n0,
+      then the larger n1.
+
+    Under a width-only error the greedy of the pages upgrades hotter experts
+    first at every width step, so its result is itself a band plan, and the
+    exhaustive search over bands below never does worse.  Raises ValueError
+    when no plan fits.
+    """
+    pop = [int(v) for v in np.asarray(popularity, dtype=np.uint64)]
+    E = len(pop)
+    order = sorted(range(E), key=lambda e: (-pop[e], e))
+    cost_b = [expert_table_bytes(hidden, inter, b) for b in tier_bits]
+    w = [ERR_WEIGHT[b] for b in tier_bits]
+    best = None
+    for n0 in range(E, -1, -1):
+        for n1 in range(E - n0, -1, -1):
+            n2 = E - n0 - n1
+            nbytes = n0 * cost_b[0] + n1 * cost_b[1] + n2 * cost_b[2]
+            if nbytes > budget_bytes:
+                continue
+            err = 0
+            for rank, e in enumerate(order):
+                tier = 0 if rank < n0 else (1 if rank < n0 + n1 else 2)
+                err += pop[e] * w[tier]
+            if best is None or err < best[0]:
+                best = (err, (n0, n1, n2))
+    if best is None:
+        raise ValueError("no tier plan fits the byte budget")
+    return best[1]
 
 
 # ---------------------------------------------------------------------------

@@ -261,6 +261,143 @@ def test_tiers_reject_bad_counts():
         O.build_tiers(np.zeros(8, np.uint64), (2, 2, 2))
 
 
+# ----------------------------------------------------------------- tier planner
+
+def test_expert_table_bytes_closed_form():
+    # 3 matrices of 2048 x 512 weights in blocks of 32: 98304 blocks, each
+    # 4*bits bytes of codes and 4 bytes of (d, m)
+    assert O.expert_table_bytes(2048, 512, 4) == 98304 * 20
+    assert O.expert_table_bytes(2048, 512, 3) == 98304 * 16
+    assert O.expert_table_bytes(2048, 512, 2) == 98304 * 12
+    # the full-size layer's tiers of 128 / 256 / 128 experts: exactly 768 MiB
+    total = (128 * O.expert_table_bytes(2048, 512, 4) + 256 * O.expert_table_bytes(2048, 512, 3)
+             + 128 * O.expert_table_bytes(2048, 512, 2))
+    assert total == 768 * 2**20
+
+
+def _werr(b):
+    # the error model written out: mean square error of a uniform b-bit
+    # quantiser over a unit range, up to the common factor 1/12
+    return Fraction(1, (2**b - 1) ** 2)
+
+
+def _plan_cost(pop, tiers_of_rank_order, bits):
+    return sum(int(p) * _werr(bits[t]) for p, t in zip(pop, tiers_of_rank_order))
+
+
+def test_plan_budget_extremes():
+    pop = np.array([5, 0, 9, 9, 1, 3], np.uint64)
+    c = [O.expert_table_bytes(256, 128, b) for b in (4, 3, 2)]
+    E = len(pop)
+    assert O.plan_tiers(pop, (4, 3, 2), 256, 128, E * c[0]) == (E, 0, 0)
+    assert O.plan_tiers(pop, (4, 3, 2), 256, 128, 10 * E * c[0]) == (E, 0, 0)
+    assert O.plan_tiers(pop, (4, 3, 2), 256, 128, E * c[2]) == (0, 0, E)
+    with pytest.raises(ValueError):
+        O.plan_tiers(pop, (4, 3, 2), 256, 128, E * c[2] - 1)
+
+
+@pytest.mark.parametrize("bits", [(4, 3, 2), (4, 4, 2), (3, 4, 2), (2, 2, 4)])
+def test_plan_brute_force_every_assignment(bits):
+    # independent search over every assignment of the E experts to the three
+    # tiers (3^E).  Among those whose tier index never decreases down the
+    # popularity order (band plans), the planner's plan has the least error,
+    # and the most experts in tier 0, then in tier 1, among equals.  When the
+    # widths do not increase down the tiers, no assignment at all beats it
+    # (swapping a hotter and a colder expert's widths never hurts).
+    import itertools
+    rng = np.random.default_rng(5)
+    H, I = 128, 128
+    c = [O.expert_table_bytes(H, I, b) for b in bits]
+    for trial in range(12):
+        E = int(rng.integers(1, 7))
+        pop = rng.integers(0, 6, size=E).astype(np.uint64)       # ties and zeros
+        lo, hi = E * min(c), E * max(c)
+        budget = int(rng.integers(lo, hi + 1))
+        n = O.plan_tiers(pop, bits, H, I, budget)
+        assert sum(n) == E and n[0] * c[0] + n[1] * c[1] + n[2] * c[2] <= budget
+        order = sorted(range(E), key=lambda e: (-int(pop[e]), e))
+        best_any = best_band = None
+        for assign in itertools.product(range(3), repeat=E):
+            if sum(c[t] for t in assign) > budget:
+                continue
+            err = sum(int(pop[e]) * _werr(bits[t]) for e, t in enumerate(assign))
+            best_any = err if best_any is None else min(best_any, err)
+            ranked = [assign[e] for e in order]
+            if all(ranked[i] <= ranked[i + 1] for i in range(E - 1)):
+                key = (err, -ranked.count(0), -ranked.count(1))
+                if best_band is None or key < best_band[0]:
+                    best_band = (key, (ranked.count(0), ranked.count(1), ranked.count(2)))
+        assert tuple(n) == best_band[1]
+        if bits[0] >= bits[1] >= bits[2]:
+            bands = [0] * n[0] + [1] * n[1] + [2] * n[2]
+            assert _plan_cost([pop[e] for e in order], bands, bits) == best_any
+
+
+def _greedy(pop, bits, H, I, budget):
+    # the pages' planner: start every expert at the cheapest width, then keep
+    # spending bytes on the single upgrade (one expert, next wider width) that
+    # removes the most expected error per byte, while it fits
+    widths = sorted(set(bits))
+    cost = {b: O.expert_table_bytes(H, I, b) for b in widths}
+    cur = [widths[0]] * len(pop)
+    spent = cost[widths[0]] * len(pop)
+    if spent > budget:
+        return None
+    while True:
+        best = None
+        for e, b in enumerate(cur):
+            k = widths.index(b)
+            if k + 1 == len(widths):
+                continue
+            nb = widths[k + 1]
+            extra = cost[nb] - cost[b]
+            if spent + extra > budget:
+                continue
+            gain = int(pop[e]) * (_werr(b) - _werr(nb)) / extra
+            key = (gain, int(pop[e]), -e)
+            if best is None or key > best[0]:
+                best = (key, e, nb, extra)
+        if best is None or best[0][0] == 0:
+            return cur
+        _, e, nb, extra = best
+        cur[e] = nb
+        spent += extra
+
+
+def test_plan_never_worse_than_the_greedy():
+    rng = np.random.default_rng(6)
+    H, I = 128, 256
+    bits = (4, 3, 2)
+    c = [O.expert_table_bytes(H, I, b) for b in bits]
+    for trial in range(20):
+        E = int(rng.integers(2, 40))
+        pop = rng.zipf(1.6, size=E).astype(np.uint64)
+        budget = int(rng.integers(E * c[2], E * c[0] + 1))
+        n = O.plan_tiers(pop, bits, H, I, budget)
+        order = sorted(range(E), key=lambda e: (-int(pop[e]), e))
+        plan = _plan_cost([pop[e] for e in order], [0] * n[0] + [1] * n[1] + [2] * n[2], bits)
+        g = _greedy(pop, bits, H, I, budget)
+        gerr = sum(int(pop[e]) * _werr(b) for e, b in enumerate(g))
+        assert plan <= gerr
+        # the greedy's widths never increase down the popularity order
+        gw = [g[e] for e in order]
+        assert all(gw[i] >= gw[i + 1] for i in range(E - 1))
+
+
+def test_plan_more_budget_never_worse():
+    rng = np.random.default_rng(7)
+    pop = rng.zipf(1.4, size=30).astype(np.uint64)
+    bits = (4, 3, 2)
+    c = [O.expert_table_bytes(128, 128, b) for b in bits]
+    order = sorted(range(30), key=lambda e: (-int(pop[e]), e))
+    prev = None
+    for budget in range(30 * c[2], 30 * c[0] + 1, (c[0] - c[2]) // 3):
+        n = O.plan_tiers(pop, bits, 128, 128, budget)
+        err = _plan_cost([pop[e] for e in order], [0] * n[0] + [1] * n[1] + [2] * n[2], bits)
+        assert prev is None or err <= prev
+        prev = err
+
+
 # ----------------------------------------------------------------- router
 
 def test_router_keys_exact_vs_fp64():
