@@ -187,6 +187,28 @@ int moe_build_tiers(const moe_dims* dims, const uint64_t* popularity,
                     int32_t* slot_expert_out, moe_layer* dst, int32_t dst_on_device,
                     hipStream_t stream);
 
+/* Tier sizes for a memory budget ([P1] "step 4: three shelves, all on the
+ * GPU": the re-packer's planner fills a memory budget, each byte going where
+ * it removes the most expected error; "reproduce it" passes the budget).
+ *
+ * Chooses n_slots (sum E) for moe_build_tiers: experts in popularity rank
+ * order (as moe_build_tiers ranks them) fill tier 0, then tier 1, then tier
+ * 2.  The expert tables (three matrices per expert, 3*H*I/32 blocks of
+ * 4*bits + 4 bytes) must take at most budget_bytes.  Among such plans the one
+ * of least expected error is returned, the error of an expert at b bits
+ * being popularity * (2^b - 1)^-2 (a uniform b-bit quantiser's mean square
+ * error over a block's range, up to a common factor); on equal error, more
+ * experts in tier 0, then in tier 1.  With tier widths that do not increase
+ * from tier 0 to tier 2, no assignment of widths to experts does better.
+ * Host only, exact integer arithmetic.
+ *
+ *   popularity   host [E] usage counts.   tier_bits  each in {2, 3, 4}.
+ *   n_slots_out  host [3] (out).
+ * Returns MOE_EINVAL for invalid arguments or when no plan fits the budget. */
+int moe_plan_tiers(const moe_dims* dims, const uint64_t* popularity,
+                   const int32_t tier_bits[3], uint64_t budget_bytes,
+                   int32_t n_slots_out[3]);
+
 /* A1-A2 -- router scores, top-K and mixing weights for T tokens.
  *
  * key[t][e] = x[t] . w_router[e] + b[e] accumulated in float64 (all inputs

@@ -25,7 +25,7 @@ __all__ = [
     "MOE_SRC_F32", "MOE_SRC_CODES",
     "MoeError", "MoeLibraryMissing", "MoeDims", "MoeLayer", "MoeExpertSource",
     "lib", "library_path", "status_string", "dims", "tier_table_bytes",
-    "build_tiers", "route", "forward_decode", "forward_prefill", "workspace_bytes",
+    "build_tiers", "plan_tiers", "route", "forward_decode", "forward_prefill", "workspace_bytes",
     "DeviceLayer", "Trace", "KERNEL_NAMES",
 ]
 
@@ -97,6 +97,9 @@ def lib():
         L.moe_build_tiers.argtypes = [POINTER(MoeDims), c_void_p, POINTER(c_int32), POINTER(c_int32),
                                       POINTER(MoeExpertSource), c_void_p, c_void_p,
                                       POINTER(MoeLayer), c_int32, c_void_p]
+        L.moe_plan_tiers.restype = ctypes.c_int
+        L.moe_plan_tiers.argtypes = [POINTER(MoeDims), c_void_p, POINTER(c_int32), ctypes.c_uint64,
+                                     POINTER(c_int32)]
         L.moe_route.restype = ctypes.c_int
         L.moe_route.argtypes = [POINTER(MoeDims), POINTER(MoeLayer), c_void_p, c_int32, c_void_p,
                                 c_void_p, c_void_p, POINTER(c_size_t), c_void_p]
@@ -173,6 +176,18 @@ def build_tiers(d: MoeDims, popularity, n_slots, tier_bits, source: Optional[Moe
                                _stream(stream) if dst_on_device else None)
     _check(rc, "moe_build_tiers")
     return tmap, sexp
+
+
+def plan_tiers(d: MoeDims, popularity, tier_bits, budget_bytes: int):
+    """``moe_plan_tiers``: tier sizes ``(n0, n1, n2)`` for a byte budget."""
+    pop = np.ascontiguousarray(popularity, dtype=np.uint64)
+    if pop.shape != (d.n_experts,):
+        raise ValueError("popularity must hold one count per expert")
+    out = (c_int32 * 3)()
+    rc = lib().moe_plan_tiers(ctypes.byref(d), pop.ctypes.data, _i32x3(tier_bits),
+                              ctypes.c_uint64(int(budget_bytes)), out)
+    _check(rc, "moe_plan_tiers")
+    return tuple(int(v) for v in out)
 
 
 def workspace_bytes(kind: str, d: MoeDims, layer: MoeLayer, T: int, y_dt: int = MOE_F32) -> int:

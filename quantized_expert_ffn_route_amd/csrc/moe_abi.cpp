@@ -254,6 +254,88 @@ size_t moe_tier_table_bytes(const moe_dims* dims, int32_t bits, int32_t n_slots,
 // A0: tier build.
 // ---------------------------------------------------------------------------
 
+// Tier sizes for a byte budget: the popularity-band plan of least expected
+// error.  Error of an expert at b bits = popularity * 11025 / (2^b - 1)^2
+// (exact integers: 49, 225, 1225 for 4, 3, 2 bits).  For a given n0 the
+// error is monotone in n1 (it moves ranks between tiers 1 and 2), so the
+// best n1 is an end of its feasible interval: O(E log E) in all.
+int moe_plan_tiers(const moe_dims* dims, const uint64_t* popularity, const int32_t tier_bits[3],
+                   uint64_t budget_bytes, int32_t n_slots_out[3]) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!popularity || !tier_bits || !n_slots_out) return MOE_EINVAL;
+  for (int t = 0; t < 3; t++)
+    if (tier_bits[t] != 2 && tier_bits[t] != 3 && tier_bits[t] != 4) return MOE_EINVAL;
+  const int E = dims->n_experts;
+  std::vector<int32_t> order(E);
+  std::iota(order.begin(), order.end(), 0);
+  std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    return popularity[a] != popularity[b] ? popularity[a] > popularity[b] : a < b;
+  });
+  typedef unsigned __int128 u128;
+  // P[r]: popularity of ranks < r
+  std::vector<u128> P(E + 1, 0);
+  for (int r = 0; r < E; r++) P[r + 1] = P[r] + popularity[order[r]];
+  auto werr = [](int b) -> u128 { return b == 4 ? 49 : (b == 3 ? 225 : 1225); };
+  const u128 w0 = werr(tier_bits[0]), w1 = werr(tier_bits[1]), w2 = werr(tier_bits[2]);
+  // bytes of one expert's three matrices at b bits
+  const int64_t blocks = 3 * (int64_t)dims->hidden * dims->inter / 32;
+  const int64_t c0 = blocks * (4 * tier_bits[0] + 4), c1 = blocks * (4 * tier_bits[1] + 4),
+                c2 = blocks * (4 * tier_bits[2] + 4);
+  const __int128 budget = (__int128)budget_bytes;
+  bool found = false;
+  u128 best = 0;
+  int bn0 = 0, bn1 = 0;
+  for (int n0 = E; n0 >= 0; n0--) {
+    const int rest = E - n0;
+    // n1 * (c1 - c2) <= R
+    const __int128 R = budget - (__int128)n0 * c0 - (__int128)rest * c2;
+    int lo = 0, hi = rest;
+    if (c1 > c2) {
+      if (R < 0) continue;
+      const __int128 m = R / (c1 - c2);
+      hi = m < rest ? (int)m : rest;
+    } else if (c1 < c2) {
+      const __int128 need = R >= 0 ? 0 : (-R + (c2 - c1) - 1) / (c2 - c1);
+      if (need > rest) continue;
+      lo = (int)need;
+    } else if (R < 0) {
+      continue;
+    }
+    // error of (n0, n1): tier 0 on ranks < n0, tier 1 on [n0, n0 + n1), tier 2 after
+    auto err = [&](int n1) {
+      return w0 * P[n0] + w1 * (P[n0 + n1] - P[n0]) + w2 * (P[E] - P[n0 + n1]);
+    };
+    int n1;
+    if (w1 <= w2) {
+      n1 = hi;                                   // error never rises with n1
+    } else {
+      // error never falls with n1: the largest n1 as good as the smallest
+      n1 = lo;
+      const u128 at = P[n0 + lo];
+      int a = lo, b = hi;                        // P[n0 + a] == at; find the last such
+      while (a < b) {
+        const int mid = a + (b - a + 1) / 2;
+        if (P[n0 + mid] == at) a = mid; else b = mid - 1;
+      }
+      n1 = a;
+    }
+    const u128 e = err(n1);
+    if (!found || e < best) {
+      found = true;
+      best = e;
+      bn0 = n0;
+      bn1 = n1;
+    }
+  }
+  if (!found) return MOE_EINVAL;
+  n_slots_out[0] = bn0;
+  n_slots_out[1] = bn1;
+  n_slots_out[2] = E - bn0 - bn1;
+  return MOE_OK;
+}
+
+
 int moe_build_tiers(const moe_dims* dims, const uint64_t* popularity, const int32_t n_slots[3],
                     const int32_t tier_bits[3], const moe_expert_source* src,
                     int32_t* tier_map_out, int32_t* slot_expert_out, moe_layer* dst,

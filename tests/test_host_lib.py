@@ -258,3 +258,63 @@ def test_build_tiers_rejects_bad_input():
     q[1][3, 0, 0] = 16
     with pytest.raises(M.MoeError):
         M.build_tiers(d, pop, (4, 0, 0), (4, 3, 2), M.source_codes(q, dd, mm), L)
+
+
+# ----------------------------------------------------------------- tier planner
+
+@pytest.mark.parametrize("tier_bits", [(4, 3, 2), (4, 4, 2), (3, 4, 2), (2, 3, 4), (3, 3, 3)])
+def test_plan_tiers_matches_oracle(tier_bits):
+    rng = np.random.default_rng(sum(tier_bits))
+    H, I = 256, 128
+    c = [O.expert_table_bytes(H, I, b) for b in tier_bits]
+    for trial in range(25):
+        E = int(rng.integers(1, 40))
+        d = M.dims(H, I, E, 1, False, "bf16")
+        kind = trial % 3
+        if kind == 0:
+            pop = rng.zipf(1.5, size=E)
+        elif kind == 1:
+            pop = rng.integers(0, 4, size=E)              # many ties and zeros
+        else:
+            pop = np.zeros(E)
+        pop = pop.astype(np.uint64)
+        budget = int(rng.integers(E * min(c) - c[0], E * max(c) + c[0]))
+        try:
+            want = O.plan_tiers(pop, tier_bits, H, I, budget)
+        except ValueError:
+            with pytest.raises(M.MoeError):
+                M.plan_tiers(d, pop, tier_bits, budget)
+            continue
+        assert M.plan_tiers(d, pop, tier_bits, budget) == want
+
+
+def test_plan_tiers_full_size_layer():
+    # the full-size layer: a budget of exactly the 128 / 256 / 128 tables fits
+    # and is used up to the last tier; more budget never raises the error
+    spec = synth.FULL
+    d = M.dims(spec.hidden, spec.inter, spec.n_experts, spec.top_k, True, "bf16")
+    pop = np.random.default_rng(1).zipf(1.3, size=spec.n_experts).astype(np.uint64)
+    c = [O.expert_table_bytes(spec.hidden, spec.inter, b) for b in (4, 3, 2)]
+    order = sorted(range(spec.n_experts), key=lambda e: (-int(pop[e]), e))
+    ranked = [int(pop[e]) for e in order]
+
+    def err(n):
+        w = [49] * n[0] + [225] * n[1] + [1225] * n[2]
+        return sum(p * x for p, x in zip(ranked, w))
+
+    prev = None
+    for budget in (768 * 2**20, 800 * 2**20, 900 * 2**20, 960 * 2**20):
+        n = M.plan_tiers(d, pop, (4, 3, 2), budget)
+        assert sum(n) == spec.n_experts
+        assert n[0] * c[0] + n[1] * c[1] + n[2] * c[2] <= budget
+        assert prev is None or err(n) <= prev
+        prev = err(n)
+
+
+def test_plan_tiers_rejects_bad_input():
+    d = M.dims(256, 128, 8, 2, False, "bf16")
+    pop = np.ones(8, np.uint64)
+    with pytest.raises(M.MoeError):
+        M.plan_tiers(d, pop, (4, 5, 2), 10**9)
+    with pytest.raises(M.MoeError):
+        M.plan_tiers(d, pop, (4, 3, 2), 8 * O.expert_table_bytes(256, 128, 2) - 1)
