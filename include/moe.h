@@ -120,7 +120,14 @@ typedef struct {
  *             b=3: code 10i+2p+s at bit 32i + 16s + 3p (i < 3, p < 5); code
  *                  30+s has its bit r at bit 32r + 16s + 15.
  * w_shared  device, act dtype: gate [I][H], up [I][H], down [H][I]
- *           (row-major); NULL when has_shared == 0. */
+ *           (row-major); NULL when has_shared == 0.
+ * down_bits code width of each tier's down matrices, in {2, 3, 4}, or 0 to
+ *           use tier_bits[t]: the down projection's own precision ladder
+ *           ([P1] "step 4: three shelves, all on the GPU" and [P2] "Lever 2":
+ *           gate/up and down take different formats per tier).  codes[t][2]
+ *           and dm[t][2] are then sized and packed at that width; routing,
+ *           the tier map and gate/up are unchanged.  A zeroed struct keeps
+ *           one width per tier. */
 typedef struct {
   void* w_router;
   float* b_router;
@@ -130,6 +137,7 @@ typedef struct {
   uint8_t* codes[3][3];
   uint32_t* dm[3][3];
   void* w_shared[3];
+  int32_t down_bits[3];
 } moe_layer;
 
 /* Host-side source of the expert weights for moe_build_tiers, indexed by
@@ -164,7 +172,8 @@ size_t moe_tier_table_bytes(const moe_dims* dims, int32_t bits, int32_t n_slots,
  * reordered hottest-first, more bits for the busiest; [P2] "Lever 2").
  *
  *   popularity      host [E] usage counts.
- *   n_slots, tier_bits  as in moe_layer.
+ *   n_slots, tier_bits  as in moe_layer.  The down matrices are packed at
+ *                   dst->down_bits[t] where dst is given and that is non-zero.
  *   src             host expert weights, or NULL to compute only the map.
  *   tier_map_out    host [E] int32: tier << 16 | slot.
  *   slot_expert_out host [E] int32: expert id at each rank, or NULL.

@@ -69,7 +69,7 @@ class MoeLayer(ctypes.Structure):
     _fields_ = [("w_router", c_void_p), ("b_router", c_void_p), ("tier_map", c_void_p),
                 ("n_slots", c_int32 * 3), ("tier_bits", c_int32 * 3),
                 ("codes", (c_void_p * 3) * 3), ("dm", (c_void_p * 3) * 3),
-                ("w_shared", c_void_p * 3)]
+                ("w_shared", c_void_p * 3), ("down_bits", c_int32 * 3)]
 
 
 class MoeExpertSource(ctypes.Structure):
@@ -300,12 +300,15 @@ class DeviceLayer:
     ``shared`` likewise ``(gate, up, down)`` or None.
     """
 
-    def __init__(self, d: MoeDims, n_slots, tier_bits, router, shared=None, device="cuda"):
+    def __init__(self, d: MoeDims, n_slots, tier_bits, router, shared=None, device="cuda",
+                 down_bits=None):
         import torch
 
         self.d = d
         self.n_slots = tuple(int(v) for v in n_slots)
         self.tier_bits = tuple(int(v) for v in tier_bits)
+        # down matrices: their own ladder, or the tier's width (0)
+        self.down_bits = tuple(int(v) for v in down_bits) if down_bits is not None else (0, 0, 0)
         act_t = torch.bfloat16 if d.act == MOE_BF16 else torch.float32
         self.act_dtype = act_t
 
@@ -328,11 +331,16 @@ class DeviceLayer:
             if self.n_slots[t] == 0:
                 continue
             for m in range(3):
-                nc = tier_table_bytes(d, self.tier_bits[t], self.n_slots[t], m, MOE_CODES)
-                nd = tier_table_bytes(d, self.tier_bits[t], self.n_slots[t], m, MOE_DM)
+                bits = self.matrix_bits(t, m)
+                nc = tier_table_bytes(d, bits, self.n_slots[t], m, MOE_CODES)
+                nd = tier_table_bytes(d, bits, self.n_slots[t], m, MOE_DM)
                 self.codes[t][m] = torch.zeros(nc, dtype=torch.uint8, device=device)
                 self.dm[t][m] = torch.zeros(nd // 4, dtype=torch.int32, device=device)
         self.shared = None if shared is None else [to_dev(s, act_t) for s in shared]
+
+    def matrix_bits(self, t: int, m: int) -> int:
+        """Code width of tier t's matrix m."""
+        return self.down_bits[t] if m == MOE_DOWN and self.down_bits[t] else self.tier_bits[t]
 
     def c_struct(self) -> MoeLayer:
         L = MoeLayer()
@@ -341,6 +349,7 @@ class DeviceLayer:
         L.tier_map = _ptr(self.tier_map)
         L.n_slots = _i32x3(self.n_slots)
         L.tier_bits = _i32x3(self.tier_bits)
+        L.down_bits = _i32x3(self.down_bits)
         for t in range(3):
             for m in range(3):
                 L.codes[t][m] = _ptr(self.codes[t][m])

@@ -22,7 +22,7 @@ struct Item {
   int32_t expert;          // expert id, -1 for the shared expert
   int32_t tier;            // 0..2 quantised tier, kDenseTier, or -1 (skip)
   int32_t slot;            // slot inside the tier table
-  int32_t bits;            // code width of the tier (0 for dense)
+  int32_t bits;            // code widths: gate/up | down << 8 (0 for dense)
   int32_t route[kGroup];   // row of h for token t of the group, or -1
   float gw[kGroup];        // mixing weight of token t (0 when not routed)
 };
@@ -31,7 +31,8 @@ struct Item {
 struct Tables {
   const uint8_t* codes[3][3];
   const uint32_t* dm[3][3];
-  int32_t bits[3];
+  int32_t bits[3];         // gate / up code width of each tier
+  int32_t bits_dn[3];      // down code width of each tier
   int32_t n_slots[3];
   const void* dense[3];    // shared expert gate / up / down (act dtype)
 };
@@ -65,7 +66,8 @@ void launch_router_keys(int act, const void* x, const void* w, const float* b, d
 void launch_topk(const double* keys, int T, int E, int K, int32_t* ids, float* w, hipStream_t s);
 
 // Decode group (T <= kGroup): top-K, weights, then the union of experts as
-// work items (ascending expert id, then the shared expert).
+// work items (ascending expert id, then the shared expert).  tier_bits[t] =
+// gate/up width | down width << 8, copied into the items' bits.
 void launch_topk_items(const double* keys, int T, int E, int K, const int32_t* tier_map,
                        const int32_t n_slots[3], const int32_t tier_bits[3], int has_shared,
                        int32_t* ids, float* w, Item* items, int32_t* n_items, hipStream_t s);
@@ -76,7 +78,8 @@ void launch_decode_gateup(int act, const Item* items, const int32_t* n_items, in
                           hipStream_t s);
 
 // Batch-1 decode (one token): top-K + weights + work items fused with the
-// gate/up of each item (E <= 512, K <= 64).  Items are in rank order.
+// gate/up of each item (E <= 512, K <= 64).  Items are in rank order;
+// tier_bits as for launch_topk_items.
 void launch_decode1_gateup(int act, const double* keys, int E, int K, const int32_t* tier_map,
                            const int32_t n_slots[3], const int32_t tier_bits[3], int has_shared,
                            const void* x, const Tables& tb, void* h, int H, int I, int32_t* ids,

@@ -284,7 +284,7 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode_gateup(const Item*
   // the count and this item's header (always inside the items array) in one trip
   const int n = *n_items;
   const int tier = items[u].tier;
-  const int slot = items[u].slot, bits = items[u].bits;
+  const int slot = items[u].slot, bits = items[u].bits & 0xFF;   // gate / up width
   const int4 routes = *reinterpret_cast<const int4*>(&items[u].route[4 * (lane >> 4)]);
   if (u >= n || tier < 0) return;
   const int rt[4] = {routes.x, routes.y, routes.z, routes.w};
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode1_gateup(const doub
     if (t < 0 || t > 2 || sl >= ns) return;
     tier = t;
     slot = sl;
-    bits = t == 0 ? tier_bits.x : (t == 1 ? tier_bits.y : tier_bits.z);
+    bits = (t == 0 ? tier_bits.x : (t == 1 ? tier_bits.y : tier_bits.z)) & 0xFF;
   } else if (!has_shared) {
     return;
   }
@@ -585,8 +585,8 @@ __global__ __launch_bounds__(1024) void k_decode_down(const Item* __restrict__ i
         const A* dense = reinterpret_cast<const A*>(tb.dense[MOE_DOWN]) +
                          (size_t)(rg * 16 + lm) * I + 128 * c + 32 * lg;
         if (t == kDenseTier) load_down<A, 0>(raw[j], tb, t, idx, dense);
-        else if (it.bits == 4) load_down<A, 4>(raw[j], tb, t, idx, dense);
-        else if (it.bits == 3) load_down<A, 3>(raw[j], tb, t, idx, dense);
+        else if ((it.bits >> 8) == 4) load_down<A, 4>(raw[j], tb, t, idx, dense);
+        else if ((it.bits >> 8) == 3) load_down<A, 3>(raw[j], tb, t, idx, dense);
         else load_down<A, 2>(raw[j], tb, t, idx, dense);
       }
       if constexpr (!STAGE) {
@@ -611,8 +611,8 @@ __global__ __launch_bounds__(1024) void k_decode_down(const Item* __restrict__ i
       }
       Frag<A> b;
       if (t == kDenseTier) to_frag<A, 0>(b, raw[j]);
-      else if (it.bits == 4) to_frag<A, 4>(b, raw[j]);
-      else if (it.bits == 3) to_frag<A, 3>(b, raw[j]);
+      else if ((it.bits >> 8) == 4) to_frag<A, 4>(b, raw[j]);
+      else if ((it.bits >> 8) == 3) to_frag<A, 3>(b, raw[j]);
       else to_frag<A, 2>(b, raw[j]);
       const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
       const f32x4_t part = mma_step(*hf, b, z);
@@ -727,8 +727,9 @@ __global__ __launch_bounds__(1024) void k_decode1_down(const Item* __restrict__ 
                                            (size_t)row * I + 128 * c + 32 * lg);
       } else {
         const size_t idx = (((size_t)item.slot * nrg + rg) * nbg + c) * 64 + 16 * lg + half * 8 + (lm & 7);
-        if (item.bits == 4) load_raw<bf16_t, 4>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
-        else if (item.bits == 3) load_raw<bf16_t, 3>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
+        const int dbits = item.bits >> 8;       // down width
+        if (dbits == 4) load_raw<bf16_t, 4>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
+        else if (dbits == 3) load_raw<bf16_t, 3>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
         else load_raw<bf16_t, 2>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
       }
     }
@@ -745,8 +746,8 @@ __global__ __launch_bounds__(1024) void k_decode1_down(const Item* __restrict__ 
       const Item& hx = s_items[ix];           // the pair's tier (X always exists)
       Frag<bf16_t> b;
       if (hx.tier == kDenseTier) to_frag<bf16_t, 0>(b, raw[j]);
-      else if (hx.bits == 4) to_frag<bf16_t, 4>(b, raw[j]);
-      else if (hx.bits == 3) to_frag<bf16_t, 3>(b, raw[j]);
+      else if ((hx.bits >> 8) == 4) to_frag<bf16_t, 4>(b, raw[j]);
+      else if ((hx.bits >> 8) == 3) to_frag<bf16_t, 3>(b, raw[j]);
       else to_frag<bf16_t, 2>(b, raw[j]);
       const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
       const f32x4_t part = mma_step(ha, b, z);

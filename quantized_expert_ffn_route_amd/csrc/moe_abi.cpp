@@ -57,6 +57,9 @@ int check_layer(const moe_dims* d, const moe_layer* L) {
   if (L->b_router && !aligned(L->b_router, 4)) return MOE_EINVAL;
   int rc = check_tiers(d, L->n_slots, L->tier_bits);
   if (rc) return rc;
+  for (int t = 0; t < 3; t++)
+    if (L->down_bits[t] != 0 && L->down_bits[t] != 2 && L->down_bits[t] != 3 && L->down_bits[t] != 4)
+      return MOE_EINVAL;
   for (int t = 0; t < 3; t++) {
     if (L->n_slots[t] == 0) continue;
     for (int m = 0; m < 3; m++)
@@ -74,6 +77,7 @@ Tables make_tables(const moe_dims* d, const moe_layer* L) {
   std::memset(&tb, 0, sizeof(tb));
   for (int t = 0; t < 3; t++) {
     tb.bits[t] = L->tier_bits[t];
+    tb.bits_dn[t] = L->down_bits[t] ? L->down_bits[t] : L->tier_bits[t];
     tb.n_slots[t] = L->n_slots[t];
     for (int m = 0; m < 3; m++) {
       tb.codes[t][m] = L->codes[t][m];
@@ -373,11 +377,18 @@ int moe_build_tiers(const moe_dims* dims, const uint64_t* popularity, const int3
       for (int m = 0; m < 3; m++)
         if (!dst->codes[t][m] || !dst->dm[t][m]) return MOE_EINVAL;
   if (dst_on_device && !dst->tier_map) return MOE_EINVAL;
+  // code width of tier t, matrix m: the down matrices may have their own
+  int32_t mbits[3][3];
+  for (int t = 0; t < 3; t++) {
+    const int dn = dst->down_bits[t];
+    if (dn != 0 && dn != 2 && dn != 3 && dn != 4) return MOE_EINVAL;
+    for (int m = 0; m < 3; m++) mbits[t][m] = m == MOE_DOWN && dn ? dn : tier_bits[t];
+  }
 
   std::atomic<int> status{MOE_OK};
   // pack one (tier, matrix, slot) expert matrix into `codes`/`dm`
   auto pack_one = [&](int t, int m, int slot, uint8_t* codes, uint32_t* dm) {
-    const int bits = tier_bits[t], L = (1 << bits) - 1;
+    const int bits = mbits[t][m], L = (1 << bits) - 1;
     const int e = order[start[t] + slot];
     int R, C;
     mat_shape(dims, m, &R, &C);
@@ -423,8 +434,8 @@ int moe_build_tiers(const moe_dims* dims, const uint64_t* popularity, const int3
   for (int t = 0; t < 3; t++) {
     if (n_slots[t] == 0) continue;
     for (int m = 0; m < 3; m++) {
-      const size_t cb = moe_tier_table_bytes(dims, tier_bits[t], n_slots[t], m, MOE_CODES);
-      const size_t db = moe_tier_table_bytes(dims, tier_bits[t], n_slots[t], m, MOE_DM);
+      const size_t cb = moe_tier_table_bytes(dims, mbits[t][m], n_slots[t], m, MOE_CODES);
+      const size_t db = moe_tier_table_bytes(dims, mbits[t][m], n_slots[t], m, MOE_DM);
       if (dst_on_device) {
         stage_codes[3 * t + m].assign(cb, 0);
         stage_dm[3 * t + m].assign(db, 0);
@@ -532,6 +543,9 @@ int moe_forward_decode(const moe_dims* dims, const moe_layer* layer, const void*
   const int H = dims->hidden, K = dims->top_k, E = dims->n_experts;
   const Tables tb = make_tables(dims, layer);
   const size_t xb = act_bytes(dims->act), yb = y_dt == MOE_BF16 ? 2 : 4;
+  // the work items carry both code widths of a tier: gate/up | down << 8
+  const int32_t wbits[3] = {tb.bits[0] | tb.bits_dn[0] << 8, tb.bits[1] | tb.bits_dn[1] << 8,
+                            tb.bits[2] | tb.bits_dn[2] << 8};
   for (int t0 = 0; t0 < T; t0 += kGroup) {
     const int nt = std::min(kGroup, T - t0);
     const char* xg = static_cast<const char*>(x) + (size_t)t0 * H * xb;
@@ -546,10 +560,10 @@ int moe_forward_decode(const moe_dims* dims, const moe_layer* layer, const void*
     if (nt == 1 && E <= 512) {
       // one token: the top-K is folded into the gate/up kernel
       launch_decode1_gateup(dims->act, keys, E, K, layer->tier_map, layer->n_slots,
-                            layer->tier_bits, dims->has_shared, xg, tb, h, H, dims->inter, ids,
+                            wbits, dims->has_shared, xg, tb, h, H, dims->inter, ids,
                             wts, items, n_items, stream);
     } else {
-      launch_topk_items(keys, nt, E, K, layer->tier_map, layer->n_slots, layer->tier_bits,
+      launch_topk_items(keys, nt, E, K, layer->tier_map, layer->n_slots, wbits,
                         dims->has_shared, ids, wts, items, n_items, stream);
       launch_decode_gateup(dims->act, items, n_items, nt * K + dims->has_shared, xg, nt, tb, h,
                            H, dims->inter, stream);

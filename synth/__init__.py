@@ -52,6 +52,8 @@ class LayerSpec:
     n_slots: Tuple[int, int, int]  # experts per tier (4-bit, 3-bit, 2-bit)
     tier_bits: Tuple[int, int, int] = (4, 3, 2)
     has_bias: bool = True
+    # code width of each tier's down matrices when it differs from tier_bits
+    down_bits: Optional[Tuple[int, int, int]] = None
 
     def with_(self, **kw) -> "LayerSpec":
         return replace(self, **kw)

@@ -60,6 +60,9 @@ def make_layer(spec: synth.LayerSpec, seed: int = 0, source: str = "f32",
     d = M.dims(spec.hidden, spec.inter, spec.n_experts, spec.top_k, spec.has_shared, spec.act)
     tmap_o, _ = O.build_tiers(pop, spec.n_slots)
     bits_of = [spec.tier_bits[int(v) >> 16] for v in tmap_o]
+    # the down matrices' own ladder, if any
+    dbits = spec.down_bits or spec.tier_bits
+    dbits_of = [dbits[int(v) >> 16] for v in tmap_o]
 
     if source == "f32":
         gate, up, down = synth.expert_weights_f32(spec, seed + 2)
@@ -67,12 +70,14 @@ def make_layer(spec: synth.LayerSpec, seed: int = 0, source: str = "f32",
 
         def experts(e):
             if e not in cache:
-                cache[e] = O.ExpertBlocks(bits_of[e], *[O.quantise_rows(w[e], bits_of[e])
-                                                        for w in (gate, up, down)])
+                cache[e] = O.ExpertBlocks(bits_of[e], O.quantise_rows(gate[e], bits_of[e]),
+                                          O.quantise_rows(up[e], bits_of[e]),
+                                          O.quantise_rows(down[e], dbits_of[e]))
             return cache[e]
         src_arrays = (gate, up, down)
         src = M.source_f32(*src_arrays)
     else:
+        assert spec.down_bits is None, "pre-quantised sources use one width per tier"
         per = [synth.expert_codes(spec, bits_of[e], seed + 2, e) for e in range(spec.n_experts)]
 
         def experts(e):
@@ -91,7 +96,8 @@ def make_layer(spec: synth.LayerSpec, seed: int = 0, source: str = "f32",
     dl = None
     tmap = tmap_o
     if device:
-        dl = M.DeviceLayer(d, spec.n_slots, spec.tier_bits, (w_router, bias), shared)
+        dl = M.DeviceLayer(d, spec.n_slots, spec.tier_bits, (w_router, bias), shared,
+                           down_bits=spec.down_bits)
         tmap, _ = dl.load_experts(pop, src)
         del src_arrays
     return TestLayer(spec=spec, ol=ol, dl=dl, tier_map=tmap, popularity=pop)

@@ -509,3 +509,26 @@ def test_decode_equals_prefill(mid, full):
         np.testing.assert_array_equal(idd, idp)
         np.testing.assert_array_equal(wd, wp)
         check_y(yp, yd.cpu().numpy().astype(np.float64), "bf16", "prefill vs decode")
+
+
+# per-matrix ladders: the down matrices of a tier quantised at their own width
+@pytest.mark.parametrize("down_bits", [(4, 4, 3), (3, 2, 4)])
+def test_per_matrix_ladder(down_bits):
+    spec = MID.with_(down_bits=down_bits)
+    tl = make_layer(spec, seed=13)
+    for T in (1, 5):
+        x = synth.tokens(spec, T, 90 + T)
+        y, ids, w = run_decode(tl, x)
+        _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, spec.top_k, exact=True)
+        np.testing.assert_array_equal(ids, oids)
+        ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+        check_y(y, ref["y"], "bf16", f"decode T={T}, down bits {down_bits}")
+        yb, _, _ = run_decode(tl, x, M.MOE_BF16)
+        check_y(yb, O.output_cast(ref["y"], "bf16"), "bf16",
+                f"decode T={T} bf16 out, down bits {down_bits}")
+    x = synth.tokens(spec, 300, 95)
+    y, ids, w, _, _ = run_prefill(tl, x)
+    _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, spec.top_k, exact=True)
+    np.testing.assert_array_equal(ids, oids)
+    ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+    check_y(y, ref["y"], "bf16", f"prefill T=300, down bits {down_bits}")

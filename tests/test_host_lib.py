@@ -152,24 +152,31 @@ def test_forward_argument_checks_without_gpu():
 
 # ------------------------------------------------------------ host tier build
 
-def _host_tables(d, n_slots, tier_bits):
+def _mbits(tier_bits, down_bits, t, m):
+    return down_bits[t] if down_bits is not None and m == M.MOE_DOWN and down_bits[t] else tier_bits[t]
+
+
+def _host_tables(d, n_slots, tier_bits, down_bits=None):
     codes = [[None] * 3 for _ in range(3)]
     dm = [[None] * 3 for _ in range(3)]
     L = M.MoeLayer()
     L.n_slots = (ctypes.c_int32 * 3)(*n_slots)
     L.tier_bits = (ctypes.c_int32 * 3)(*tier_bits)
+    if down_bits is not None:
+        L.down_bits = (ctypes.c_int32 * 3)(*down_bits)
     for t in range(3):
         if n_slots[t] == 0:
             continue
         for m in range(3):
-            codes[t][m] = np.zeros(M.tier_table_bytes(d, tier_bits[t], n_slots[t], m, M.MOE_CODES), np.uint8)
-            dm[t][m] = np.zeros(M.tier_table_bytes(d, tier_bits[t], n_slots[t], m, M.MOE_DM) // 4, np.uint32)
+            b = _mbits(tier_bits, down_bits, t, m)
+            codes[t][m] = np.zeros(M.tier_table_bytes(d, b, n_slots[t], m, M.MOE_CODES), np.uint8)
+            dm[t][m] = np.zeros(M.tier_table_bytes(d, b, n_slots[t], m, M.MOE_DM) // 4, np.uint32)
             L.codes[t][m] = codes[t][m].ctypes.data
             L.dm[t][m] = dm[t][m].ctypes.data
     return L, codes, dm
 
 
-def _oracle_tables(blocks_by_expert, slot_expert, n_slots, tier_bits):
+def _oracle_tables(blocks_by_expert, slot_expert, n_slots, tier_bits, down_bits=None):
     """Oracle packing of every tier table from per-expert (d, m, q)."""
     out = {}
     start = [0, n_slots[0], n_slots[0] + n_slots[1]]
@@ -181,7 +188,7 @@ def _oracle_tables(blocks_by_expert, slot_expert, n_slots, tier_bits):
             q = np.stack([blocks_by_expert[e][m][2] for e in experts])
             dd = np.stack([blocks_by_expert[e][m][0] for e in experts])
             mm = np.stack([blocks_by_expert[e][m][1] for e in experts])
-            out[(t, m)] = O.pack_tiles(q, dd, mm, tier_bits[t])
+            out[(t, m)] = O.pack_tiles(q, dd, mm, _mbits(tier_bits, down_bits, t, m))
     return out
 
 
@@ -196,21 +203,23 @@ def test_build_tiers_map_only_matches_oracle():
         np.testing.assert_array_equal(sexp, want_se)
 
 
-@pytest.mark.parametrize("tier_bits", [(4, 3, 2), (2, 4, 3)])
-def test_build_tiers_f32_bit_exact_vs_oracle(tier_bits):
+@pytest.mark.parametrize("tier_bits,down_bits", [((4, 3, 2), None), ((2, 4, 3), None),
+                                                  ((4, 3, 2), (4, 4, 3)), ((3, 3, 2), (0, 4, 0))])
+def test_build_tiers_f32_bit_exact_vs_oracle(tier_bits, down_bits):
     spec = synth.TINY.with_(n_experts=12, n_slots=(3, 6, 3))
     d = M.dims(spec.hidden, spec.inter, spec.n_experts, spec.top_k, False, spec.act)
     gate, up, down = synth.expert_weights_f32(spec, seed=21)
     pop = np.random.default_rng(22).integers(0, 100, spec.n_experts).astype(np.uint64)
-    L, codes, dm = _host_tables(d, spec.n_slots, tier_bits)
+    L, codes, dm = _host_tables(d, spec.n_slots, tier_bits, down_bits)
     src = M.source_f32(gate, up, down)
     tmap, sexp = M.build_tiers(d, pop, spec.n_slots, tier_bits, src, L, dst_on_device=False)
     want_map, want_se = O.build_tiers(pop, spec.n_slots)
     np.testing.assert_array_equal(tmap, want_map)
-    bits_of = {e: tier_bits[int(want_map[e]) >> 16] for e in range(spec.n_experts)}
-    blocks = {e: [O.quantise_rows(w[e], bits_of[e]) for w in (gate, up, down)]
+    tier_of = {e: int(want_map[e]) >> 16 for e in range(spec.n_experts)}
+    blocks = {e: [O.quantise_rows(w[e], _mbits(tier_bits, down_bits, tier_of[e], m))
+                  for m, w in enumerate((gate, up, down))]
               for e in range(spec.n_experts)}
-    want = _oracle_tables(blocks, want_se, spec.n_slots, tier_bits)
+    want = _oracle_tables(blocks, want_se, spec.n_slots, tier_bits, down_bits)
     for (t, m), (wc, wd) in want.items():
         np.testing.assert_array_equal(codes[t][m], wc, err_msg=f"codes tier {t} mat {m}")
         np.testing.assert_array_equal(dm[t][m], wd, err_msg=f"dm tier {t} mat {m}")
