@@ -26,8 +26,12 @@ and ``tests/golden/``):
 * ``bf16_round``/``f16_round``: pinned (hand ties, torch/numpy conversions).
 * ``quantise_rows``: pinned (hand-computed blocks, half-even tie block,
   reconstruction bound).
-* ``encode_codes``/``decode_codes``/``pack_tiles``: pinned (hand-derived byte
-  strings, brute-force placement on tiny shapes).
+* ``encode_codes``/``decode_codes``/``pack_tiles``/``pack_tiles_mx``: pinned
+  (hand-derived byte strings, brute-force placement on tiny shapes).
+* ``quantise_rows_mx``/``dequantise_mx`` (MXFP4): pinned (hand blocks from the
+  OCP MX definition, E2M1 values from their bit fields, brute force by exact
+  rational search, reconstruction bound, equality with an affine container
+  holding the same values through the whole layer).
 * ``dequantise``: pinned (hand blocks, exact fp64 identity).
 * ``build_tiers``: pinned (brute force, uniform popularity, bijection).
 * ``expert_table_bytes``/``plan_tiers``: pinned (closed forms at the budget

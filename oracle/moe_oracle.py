@@ -24,11 +24,20 @@ __all__ = [
     "f32_to_bf16_bits",
     "f16_round",
     "quantise_rows",
+    "MXFP4",
+    "E2M1",
+    "MX_XMIN",
+    "MX_XMAX",
+    "MxBlocks",
+    "quantise_rows_mx",
+    "dequantise_mx",
+    "dequantise_any",
     "code_bit_positions",
     "encode_codes",
     "decode_codes",
     "dequantise",
     "pack_tiles",
+    "pack_tiles_mx",
     "build_tiers",
     "expert_table_bytes",
     "plan_tiers",
@@ -46,8 +55,13 @@ __all__ = [
     "output_cast",
 ]
 
-#: Highest code of a b-bit block: L = 2**b - 1.
-LEVELS = {4: 15, 3: 7, 2: 3}
+#: Format code of an MXFP4 table (a code, not a bit count): 4-bit E2M1
+#: elements sharing one E8M0 power-of-two scale per block of 32.
+MXFP4 = 0x14
+
+#: Highest code of a block: L = 2**b - 1 for the b-bit affine formats; an
+#: MXFP4 code is a 4-bit sign/magnitude pattern (0..15).
+LEVELS = {4: 15, 3: 7, 2: 3, MXFP4: 15}
 
 BLOCK = 32
 
@@ -132,6 +146,15 @@ def quantise_rows(w, bits: int):
     return d16, m16, q.reshape(w.shape)
 
 
+def _field_words(bits: int) -> int:
+    """32-bit words in the code field of one block of the format."""
+    if bits == MXFP4:
+        return 4
+    if bits not in (2, 3, 4):
+        raise ValueError("bits must be 2, 3, 4 or MXFP4")
+    return bits
+
+
 def code_bit_positions(bits: int) -> Sequence[Sequence[int]]:
     """Bit positions of every code inside a block's code field.
 
@@ -144,6 +167,9 @@ def code_bit_positions(bits: int) -> Sequence[Sequence[int]]:
       b = 2: code k = 16i + 2p + s  -> bits 32i + 16s + 2p + (0..1),  p < 8
       b = 3: code k = 10i + 2p + s  -> bits 32i + 16s + 3p + (0..2),  p < 5, i < 3
              code 30 + s: bit r at 32r + 16s + 15  (r = 0, 1, 2)
+
+    An MXFP4 field (format code ``MXFP4``) is 4 words with code k at bits
+    4k .. 4k + 3: byte j holds codes 2j (low nibble) and 2j + 1 (high nibble).
 
     Returns, for k = 0..31, the list of field bit positions of code k, least
     significant bit first.
@@ -158,6 +184,8 @@ def code_bit_positions(bits: int) -> Sequence[Sequence[int]]:
             i, rem = divmod(k, 16)
             p, s = divmod(rem, 2)
             pos.append([32 * i + 16 * s + 2 * p + r for r in range(2)])
+        elif bits == MXFP4:
+            pos.append([4 * k + r for r in range(4)])
         elif bits == 3:
             if k < 30:
                 i, rem = divmod(k, 10)
@@ -178,20 +206,22 @@ def encode_codes(q, bits: int) -> np.ndarray:
         raise ValueError("last axis must hold 32 codes")
     if np.any(q > LEVELS[bits]):
         raise ValueError("code out of range")
-    words = np.zeros(q.shape[:-1] + (bits,), dtype=np.uint32)
+    nw = _field_words(bits)
+    words = np.zeros(q.shape[:-1] + (nw,), dtype=np.uint32)
     for k, bitpos in enumerate(code_bit_positions(bits)):
         for r, p in enumerate(bitpos):
             bit = (q[..., k] >> np.uint32(r)) & np.uint32(1)
             words[..., p // 32] |= bit << np.uint32(p % 32)
-    return words.astype("<u4").view(np.uint8).reshape(q.shape[:-1] + (4 * bits,))
+    return words.astype("<u4").view(np.uint8).reshape(q.shape[:-1] + (4 * nw,))
 
 
 def decode_codes(field_bytes, bits: int) -> np.ndarray:
     """Unpack code fields ``[..., 4*bits]`` (uint8) into codes ``[..., 32]``."""
     fb = np.ascontiguousarray(np.asarray(field_bytes, dtype=np.uint8))
-    if fb.shape[-1] != 4 * bits:
+    nw = _field_words(bits)
+    if fb.shape[-1] != 4 * nw:
         raise ValueError("code field has the wrong size")
-    words = fb.reshape(fb.shape[:-1] + (bits, 4)).view("<u4")[..., 0]
+    words = fb.reshape(fb.shape[:-1] + (nw, 4)).view("<u4")[..., 0]
     q = np.zeros(fb.shape[:-1] + (BLOCK,), dtype=np.uint32)
     for k, bitpos in enumerate(code_bit_positions(bits)):
         for r, p in enumerate(bitpos):
@@ -223,6 +253,123 @@ def dequantise(d, m, q, act: str) -> np.ndarray:
     return v32.astype(np.float64)
 
 
+# ---------------------------------------------------------------------------
+# A0: MXFP4 blocks (the pages' low tier for the down matrices)
+# ---------------------------------------------------------------------------
+
+#: Magnitudes of the E2M1 codes 0..7; code 8 + i is the negation of code i.
+E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+#: Range of the shared exponent X (block scale 2**X, stored as the E8M0 byte
+#: X + 127).  With X >= -125 every non-zero element (at least 0.5 * 2**X) is a
+#: normal float32/bf16 number, and with X <= 125 the largest (6 * 2**X) is
+#: finite.
+MX_XMIN, MX_XMAX = -125, 125
+
+
+@dataclass(frozen=True)
+class MxBlocks:
+    """One matrix in MXFP4: ``e`` uint8 ``rows x cols/32`` (E8M0 scale bytes,
+    block scale 2**(e - 127)) and ``q`` uint8 ``rows x cols`` (E2M1 codes)."""
+
+    e: np.ndarray
+    q: np.ndarray
+
+
+def _e2m1_round(t: np.ndarray) -> np.ndarray:
+    """E2M1 code nearest to each (exactly scaled) value ``t``.
+
+    Ties go to the code with an even mantissa bit (an even code index), as in
+    IEEE round-to-nearest-even; magnitudes above 6 saturate to 6 (E2M1 has
+    no infinity).  A value that rounds to zero gets code 0 (positive zero).
+    """
+    a = np.abs(t)
+    grid = np.asarray(E2M1, dtype=np.float64)
+    dist = np.abs(a[..., None] - grid)                   # [..., 8]
+    best = dist.min(axis=-1, keepdims=True)
+    # among the nearest, the even index if there is one (a tie is between
+    # neighbours i, i + 1, exactly one of which is even)
+    cand = dist == best
+    even = cand & (np.arange(8) % 2 == 0)
+    idx = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    idx = np.where(a > 6.0, 7, idx)
+    sign = (t < 0) & (idx > 0)
+    return (idx + 8 * sign).astype(np.uint8)
+
+
+def quantise_rows_mx(w) -> MxBlocks:
+    """Quantise each row of ``w`` to MXFP4 in blocks of 32 consecutive weights.
+
+    The pages give MXFP4 as the low-tier format of the down matrices [P1,
+    "step 4: three shelves, all on the GPU"; P2, "Lever 2"] and nothing of its
+    recipe.  Reading taken: the OCP Microscaling (MX) v1.0 definition of
+    MXFP4 and its conversion from wider floats.  Per block:
+
+        amax = max |x|
+        X    = floor(log2(amax)) - 2       (2 = largest E2M1 exponent;
+                                            amax == 0: X = MX_XMIN)
+        X    = clamp(X, MX_XMIN, MX_XMAX)  (kept normal and finite, above)
+        q_i  = E2M1 code nearest to x_i / 2**X (ties to even, saturating at 6)
+
+    x / 2**X is exact in float64, so each code is a decision on exact values.
+    Non-finite input raises ``ValueError``.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    if w.ndim != 2 or w.shape[1] % BLOCK:
+        raise ValueError("rows must be a multiple of 32 wide")
+    if not np.all(np.isfinite(w)):
+        raise ValueError("non-finite weight")
+    blk = w.reshape(w.shape[0], -1, BLOCK).astype(np.float64)
+    amax = np.abs(blk).max(axis=-1)
+    _, ex = np.frexp(amax)                 # amax = f * 2**ex, 0.5 <= f < 1
+    X = np.where(amax > 0, ex - 1 - 2, MX_XMIN)
+    X = np.clip(X, MX_XMIN, MX_XMAX)
+    t = np.ldexp(blk, -X[..., None])
+    q = _e2m1_round(t)
+    return MxBlocks((X + 127).astype(np.uint8), q.reshape(w.shape))
+
+
+def dequantise_mx(e, q, act: str) -> np.ndarray:
+    """Dequantised weights of one MXFP4 matrix, as exact float64 values.
+
+    Value of code q in a block with scale byte e: (-1)**(q >> 3) *
+    E2M1[q & 7] * 2**(e - 127).  For e in [MX_XMIN + 127, MX_XMAX + 127] that
+    value is exactly representable in bfloat16 and float32 (two significant
+    bits, normal exponent), so no rounding is involved for either activation
+    dtype.
+    """
+    e = np.asarray(e, dtype=np.int64)
+    q = np.asarray(q, dtype=np.uint8)
+    if act not in ("f32", "bf16"):
+        raise ValueError("act must be 'f32' or 'bf16'")
+    if np.any(e < MX_XMIN + 127) or np.any(e > MX_XMAX + 127):
+        raise ValueError("scale byte out of range")
+    mag = np.asarray(E2M1, dtype=np.float64)[q & 7]
+    val = np.where(q & 8, -mag, mag)
+    X = np.repeat(e - 127, BLOCK, axis=1)
+    return np.ldexp(val, X)
+
+
+def dequantise_any(mat, act: str) -> np.ndarray:
+    """Dequantised matrix of either format: an :class:`MxBlocks`, or an affine
+    ``(d, m, q)`` triple."""
+    if isinstance(mat, MxBlocks):
+        return dequantise_mx(mat.e, mat.q, act)
+    return dequantise(*mat, act=act)
+
+
+def _tile_index(S: int, R: int, C: int) -> np.ndarray:
+    """Table index of every block ``[S][R][C/32]`` (flattened), in the tile
+    order described in :func:`pack_tiles`."""
+    if R % 16 or C % 128:
+        raise ValueError("tile tables need rows % 16 == 0 and cols % 128 == 0")
+    nb = C // BLOCK
+    s_idx, r_idx, j_idx = np.meshgrid(np.arange(S), np.arange(R), np.arange(nb), indexing="ij")
+    tile = (s_idx * (R // 16) + r_idx // 16) * (C // 128) + j_idx // 4
+    lane = 16 * (j_idx % 4) + r_idx % 16
+    return (tile * 64 + lane).reshape(-1)
+
+
 def pack_tiles(q, d, m, bits: int):
     """Arrange quantised blocks of one tier table in device tile order.
 
@@ -239,11 +386,11 @@ def pack_tiles(q, d, m, bits: int):
     and the tables are ``codes[index]`` (the 4*bits-byte code field of the
     block) and ``dm[index]`` = fp16 bits of d | (fp16 bits of m) << 16.
     Returns ``(codes uint8 [S*R*C/32 * 4*bits], dm uint32 [S*R*C/32])``.
+    MXFP4 tables are packed by :func:`pack_tiles_mx`.
     """
     q = np.asarray(q, dtype=np.uint8)
     S, R, C = q.shape
-    if R % 16 or C % 128:
-        raise ValueError("tile tables need rows % 16 == 0 and cols % 128 == 0")
+    index = _tile_index(S, R, C)
     nb = C // BLOCK
     fields = encode_codes(q.reshape(S, R, nb, BLOCK), bits)           # [S][R][nb][4b]
     dbits = np.asarray(d, dtype=np.float16).view(np.uint16).astype(np.uint32)
@@ -252,13 +399,30 @@ def pack_tiles(q, d, m, bits: int):
     nbytes = S * R * nb
     codes_out = np.zeros((nbytes, 4 * bits), dtype=np.uint8)
     dm_out = np.zeros(nbytes, dtype=np.uint32)
-    s_idx, r_idx, j_idx = np.meshgrid(np.arange(S), np.arange(R), np.arange(nb), indexing="ij")
-    tile = (s_idx * (R // 16) + r_idx // 16) * (C // 128) + j_idx // 4
-    lane = 16 * (j_idx % 4) + r_idx % 16
-    index = (tile * 64 + lane).reshape(-1)
     codes_out[index] = fields.reshape(-1, 4 * bits)
     dm_out[index] = dm.reshape(-1)
     return codes_out.reshape(-1), dm_out
+
+
+def pack_tiles_mx(q, e):
+    """MXFP4 counterpart of :func:`pack_tiles`: the same tile order, a 16-byte
+    code field per block (code k at bits 4k .. 4k + 3) and a one-byte scale
+    table (the E8M0 byte of each block).
+
+    ``q``: uint8 ``[S][R][C]`` E2M1 codes; ``e``: uint8 ``[S][R][C/32]``.
+    Returns ``(codes uint8 [S*R*C/32 * 16], scales uint8 [S*R*C/32])``.
+    """
+    q = np.asarray(q, dtype=np.uint8)
+    S, R, C = q.shape
+    index = _tile_index(S, R, C)
+    nb = C // BLOCK
+    fields = encode_codes(q.reshape(S, R, nb, BLOCK), MXFP4)          # [S][R][nb][16]
+    nbytes = S * R * nb
+    codes_out = np.zeros((nbytes, 16), dtype=np.uint8)
+    sc_out = np.zeros(nbytes, dtype=np.uint8)
+    codes_out[index] = fields.reshape(-1, 16)
+    sc_out[index] = np.asarray(e, dtype=np.uint8).reshape(-1)
+    return codes_out.reshape(-1), sc_out
 
 
 # ---------------------------------------------------------------------------
@@ -294,8 +458,10 @@ def build_tiers(popularity, n_slots: Sequence[int]):
 def expert_table_bytes(hidden: int, inter: int, bits: int) -> int:
     """Bytes of one expert's three matrices (gate, up: inter x hidden; down:
     hidden x inter) at `bits` bits: every block of 32 weights holds a
-    4*bits-byte code field and a 4-byte (d, m) word."""
-    return 3 * hidden * inter // BLOCK * (4 * bits + 4)
+    4*bits-byte code field and a 4-byte (d, m) word; an MXFP4 block holds a
+    16-byte field and a 1-byte scale."""
+    per_block = 17 if bits == MXFP4 else 4 * _field_words(bits) + 4
+    return 3 * hidden * inter // BLOCK * per_block
 
 
 #: Expected-error weight of a b-bit block per weight, scaled to integers:
@@ -328,8 +494,10 @@ def plan_tiers(popularity, tier_bits: Sequence[int], hidden: int, inter: int,
     Under a width-only error the greedy of the pages upgrades hotter experts
     first at every width step, so its result is itself a band plan, and the
     exhaustive search over bands below never does worse.  Raises ValueError
-    when no plan fits.
+    when no plan fits, or for an MXFP4 tier (outside the error model).
     """
+    if any(b not in ERR_WEIGHT for b in tier_bits):
+        raise ValueError("the error model covers the 2-, 3- and 4-bit affine widths only")
     pop = [int(v) for v in np.asarray(popularity, dtype=np.uint64)]
     E = len(pop)
     order = sorted(range(E), key=lambda e: (-pop[e], e))
@@ -506,7 +674,8 @@ def _bf16_from_f64(a: np.ndarray) -> np.ndarray:
 
 @dataclass
 class ExpertBlocks:
-    """Quantised matrices of one expert: (d, m, q) per matrix and the bit width.
+    """Quantised matrices of one expert: (d, m, q) per matrix (or an
+    :class:`MxBlocks` for an MXFP4 matrix) and the gate/up bit width.
 
     gate and up are ``I x H`` (rows along the hidden size), down is ``H x I``.
     """
@@ -538,7 +707,7 @@ class OracleLayer:
         """Dequantised (gate, up, down) of expert ``e`` (cached)."""
         if e not in self._cache:
             blk = self.experts(e)
-            self._cache[e] = tuple(dequantise(*mat, act=self.act)
+            self._cache[e] = tuple(dequantise_any(mat, self.act)
                                    for mat in (blk.gate, blk.up, blk.down))
         return self._cache[e]
 

@@ -221,6 +221,186 @@ def test_tile_pack_is_a_bijection(bits):
     assert sorted(got.tolist()) == list(range(S * R * nb))
 
 
+# ------------------------------------------------------------------ MXFP4
+
+def _mx_case_x(case):
+    x = np.zeros(32, np.float64)
+    x[:len(case["x_head"])] = case["x_head"]
+    return x
+
+
+@pytest.mark.parametrize("case", _load("mx_blocks.json")["cases"], ids=lambda c: c["name"])
+def test_mx_hand_blocks(case):
+    x = _mx_case_x(case).astype(np.float32)            # 0.3, -0.2: their float32 values
+    blk = O.quantise_rows_mx(x[None, :])
+    assert int(blk.e[0, 0]) == case["e"]
+    want_q = np.zeros(32, np.uint8)
+    want_q[:len(case["q_head"])] = case["q_head"]
+    np.testing.assert_array_equal(blk.q[0], want_q)
+    for act in ("f32", "bf16"):
+        v = O.dequantise_mx(blk.e, blk.q, act)[0]
+        if case.get("lossless"):
+            np.testing.assert_array_equal(v, x.astype(np.float64))
+        if "deq_head" in case:
+            np.testing.assert_array_equal(v[:len(case["deq_head"])], case["deq_head"])
+
+
+def test_e2m1_values_from_bit_fields():
+    # each code read as sign | 2 exponent bits (bias 1) | 1 mantissa bit, with
+    # exponent field 0 subnormal: value = 2^(1-1) * mantissa/2
+    for code in range(16):
+        s, ef, mf = code >> 3, (code >> 1) & 3, code & 1
+        mag = Fraction(mf, 2) if ef == 0 else Fraction(2) ** (ef - 1) * (1 + Fraction(mf, 2))
+        want = -mag if s else mag
+        q = np.full((1, 32), code, np.uint8)
+        for e in (127, 127 - 5, 127 + 9):
+            got = O.dequantise_mx(np.array([[e]], np.uint8), q, "f32")[0, 0]
+            assert Fraction(float(got)) == want * Fraction(2) ** (e - 127), (code, e)
+
+
+def _mx_brute_block(x):
+    """Scale exponent and codes of one block by search: X is the integer
+    with 4 * 2^X <= max|x| < 8 * 2^X (walked by doubling); each element takes
+    the grid value of smallest exact distance, ties to the even mantissa."""
+    amax = max(abs(Fraction(float(v))) for v in x)
+    if amax == 0:
+        X = -125
+    else:
+        X = 0
+        while Fraction(4) * Fraction(2) ** X > amax:
+            X -= 1
+        while Fraction(8) * Fraction(2) ** X <= amax:
+            X += 1
+        X = min(max(X, -125), 125)
+    grid = [(c, (Fraction(-1) if c & 8 else Fraction(1)) * m)
+            for c, m in enumerate([Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2),
+                                   Fraction(2), Fraction(3), Fraction(4), Fraction(6)] * 2)]
+    codes = []
+    for v in x:
+        t = Fraction(float(v)) / Fraction(2) ** X
+        if t > 6:
+            codes.append(7)
+            continue
+        if t < -6:
+            codes.append(15)
+            continue
+        best = min(abs(t - g) for _, g in grid)
+        cands = [c for c, g in grid if abs(t - g) == best]
+        if any(((c >> 1) & 3) == 0 and (c & 1) == 0 for c in cands):
+            codes.append(0)                       # zero: the positive code
+            continue
+        even = [c for c in cands if c & 1 == 0]
+        codes.append((even or cands)[0])
+    return X + 127, codes
+
+
+def test_mx_quantiser_brute_force():
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((12, 64)) * np.exp(rng.uniform(-8, 4, (12, 1)))).astype(np.float32)
+    # plant exact grid points and ties in a few blocks
+    w[0, :8] = np.array([6, 5, 3.5, 2.5, 1.75, 1.25, 0.75, 0.25], np.float32) * np.float32(2.0 ** -4)
+    w[1, 32:36] = np.float32(0.0)
+    blk = O.quantise_rows_mx(w)
+    for r in range(12):
+        for b in range(2):
+            e, codes = _mx_brute_block(w[r, 32 * b:32 * b + 32])
+            assert int(blk.e[r, b]) == e, (r, b)
+            np.testing.assert_array_equal(blk.q[r, 32 * b:32 * b + 32], codes, err_msg=f"{r},{b}")
+
+
+def test_mx_reconstruction_bound():
+    rng = np.random.default_rng(22)
+    w = (rng.standard_normal((64, 256)) * np.exp(rng.uniform(-6, 2, (64, 1)))).astype(np.float32)
+    blk = O.quantise_rows_mx(w)
+    v = O.dequantise_mx(blk.e, blk.q, "f32").reshape(64, -1, 32)
+    x = w.astype(np.float64).reshape(64, -1, 32)
+    scale = np.ldexp(1.0, blk.e.astype(np.int64) - 127)[..., None]
+    t = np.abs(x) / scale
+    assert np.all(t < 8) and np.all(t.max(-1) >= 4)
+    # half the gap of the binade below 6; above 6 the error is t - 6 < 2
+    half_gap = np.where(t < 2, 0.25, np.where(t < 4, 0.5, 1.0))
+    err = np.abs(x - v) / scale
+    assert np.all(err <= np.maximum(half_gap, t - 6))
+    # signs kept, magnitudes never grow past the input's saturation point
+    assert np.all((v == 0) | (np.sign(v) == np.sign(x)))
+
+
+def test_mx_field_hand_words_and_layout():
+    case = _load("mx_blocks.json")["field"]
+    k = np.arange(32)
+    q = np.where(k < 16, k % 16, 31 - k).astype(np.uint8)
+    field = O.encode_codes(q, O.MXFP4)
+    assert field.size == 16
+    assert [f"0x{int(w):08X}" for w in field.view("<u4")] == case["words"]
+    np.testing.assert_array_equal(O.decode_codes(field, O.MXFP4), q)
+    pos = O.code_bit_positions(O.MXFP4)
+    assert sorted(p for c in pos for p in c) == list(range(128))
+    for kk in range(32):
+        one = np.zeros(32, np.uint8)
+        one[kk] = 15
+        as_int = int.from_bytes(O.encode_codes(one, O.MXFP4).tobytes(), "little")
+        assert as_int == 15 << (4 * kk)
+
+
+@pytest.mark.parametrize("case", _load("tile_index.json")["cases"])
+def test_mx_tile_index_hand(case):
+    S, R, C = case["S"], case["R"], case["C"]
+    q = np.zeros((S, R, C), np.uint8)
+    e = np.zeros((S, R, C // 32), np.uint8)
+    e[case["s"], case["r"], case["j"]] = 200
+    q[case["s"], case["r"], 32 * case["j"] + 1] = 9
+    codes, sc = O.pack_tiles_mx(q, e)
+    assert list(np.nonzero(sc)[0]) == [case["index"]]
+    assert sc[case["index"]] == 200
+    nz = np.nonzero(codes)[0]
+    assert list(nz) == [16 * case["index"]]       # code 1: high nibble of byte 0
+    assert codes[16 * case["index"]] == 9 << 4
+
+
+def test_mx_tile_pack_is_a_bijection():
+    S, R, C = 2, 32, 128
+    nb = C // 32
+    ident = np.arange(S * R * nb).reshape(S, R, nb)
+    assert ident.max() < 256
+    _, sc = O.pack_tiles_mx(np.zeros((S, R, C), np.uint8), ident.astype(np.uint8))
+    assert sorted(sc.tolist()) == list(range(S * R * nb))
+
+
+def test_mx_table_bytes_and_planner_scope():
+    # 16 code bytes + 1 scale byte per 32 weights: 4.25 bits per weight
+    assert O.expert_table_bytes(2048, 512, O.MXFP4) == 3 * 2048 * 512 * 17 // 32
+    assert O.expert_table_bytes(2048, 512, O.MXFP4) * 20 == O.expert_table_bytes(2048, 512, 4) * 17
+    with pytest.raises(ValueError):
+        O.plan_tiers(np.ones(4, np.uint64), (4, 3, O.MXFP4), 128, 64, 1 << 30)
+
+
+def test_layer_mx_down_equals_affine_container():
+    # MXFP4 codes of magnitude <= 1.5 at scale 2^0 take the values -1.5..1.5 in
+    # steps of 0.5, which the affine 4-bit block d = 0.5, m = -1.5 also holds
+    # exactly: the same down matrices in either container give the same layer
+    layer, blocks = _random_layer(E=4, K=2, H=128, I=64, act="bf16", seed=23, bits=4)
+    rng = np.random.default_rng(24)
+    x = O.act_round(rng.standard_normal((3, 128)), "bf16")
+    mx = {}
+    aff = {}
+    for e, b in blocks.items():
+        mag = rng.integers(0, 4, (128, 64))
+        neg = rng.integers(0, 2, (128, 64)).astype(bool) & (mag > 0)
+        qmx = (mag + 8 * neg).astype(np.uint8)
+        val = np.where(neg, -0.5 * mag, 0.5 * mag)
+        qa = (val / 0.5 + 3).astype(np.uint8)          # value = 0.5 * qa - 1.5
+        d = np.full((128, 2), 0.5, np.float16)
+        m = np.full((128, 2), -1.5, np.float16)
+        mx[e] = O.ExpertBlocks(b.bits, b.gate, b.up, O.MxBlocks(np.full((128, 2), 127, np.uint8), qmx))
+        aff[e] = O.ExpertBlocks(b.bits, b.gate, b.up, (d, m, qa))
+    layer.experts = lambda e: mx[e]
+    layer._cache.clear()
+    y_mx = O.moe_layer(x, layer)["y"]
+    layer.experts = lambda e: aff[e]
+    layer._cache.clear()
+    np.testing.assert_array_equal(O.moe_layer(x, layer)["y"], y_mx)
+
+
 # ------------------------------------------------------------------ tiers
 
 def _brute_tiers(pop, n_slots):
