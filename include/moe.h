@@ -73,6 +73,13 @@ enum { MOE_GATE = 0, MOE_UP = 1, MOE_DOWN = 2 };
 enum { MOE_CODES = 0, MOE_DM = 1 };
 enum { MOE_SRC_F32 = 0, MOE_SRC_CODES = 1 };
 
+/* Format code of an MXFP4 table, accepted wherever a code width is (a code,
+ * not a bit count): 4-bit E2M1 elements sharing one E8M0 power-of-two scale
+ * per block of 32, as in the OCP Microscaling (MX) v1.0 definition.  The
+ * pages give MXFP4 as the low tier of the down matrices ([P1] "step 4: three
+ * shelves, all on the GPU"; [P2] "Lever 2"). */
+#define MOE_MXFP4 0x14
+
 /* Shape of one layer.
  *   hidden (H), inter (I): multiples of 128, H <= 8192 (MOE_EUNSUPPORTED
  *   otherwise).  E in [1, 65535].
@@ -98,7 +105,8 @@ typedef struct {
  *           tier 0 ([P1] "step 2: the experts are not equal", "step 4: three
  *           shelves, all on the GPU"; [P2] "Lever 2").
  * n_slots   experts per tier; they sum to E.
- * tier_bits code width of each tier, each in {2, 3, 4} (4/3/2 by default).
+ * tier_bits code width of each tier, each in {2, 3, 4} (4/3/2 by default),
+ *           or MOE_MXFP4.
  * codes, dm [tier][matrix] device tables of the quantised experts of that
  *           tier, matrix = MOE_GATE ([I][H]), MOE_UP ([I][H]), MOE_DOWN
  *           ([H][I]).  Blocks are 32 consecutive weights along the
@@ -119,9 +127,17 @@ typedef struct {
  *             b=2: code 16i+2p+s at bit 32i + 16s + 2p
  *             b=3: code 10i+2p+s at bit 32i + 16s + 3p (i < 3, p < 5); code
  *                  30+s has its bit r at bit 32r + 16s + 15.
+ *           An MXFP4 table uses the same tile order with a 16-byte code
+ *           field per block (code k at bits 4k..4k+3: byte j holds codes 2j
+ *           in its low nibble and 2j+1 in its high nibble; E2M1 code = sign
+ *           << 3 | exponent << 1 | mantissa) and one scale byte per block:
+ *           dm then addresses uint8 E8M0 bytes, ((uint8_t*)dm)[index] = X +
+ *           127, weight = E2M1(q) * 2^X.  X must lie in [-125, 125], which
+ *           keeps every weight a normal bf16 (exact in bf16 and fp32).
  * w_shared  device, act dtype: gate [I][H], up [I][H], down [H][I]
  *           (row-major); NULL when has_shared == 0.
- * down_bits code width of each tier's down matrices, in {2, 3, 4}, or 0 to
+ * down_bits code width of each tier's down matrices, in {2, 3, 4} or
+ *           MOE_MXFP4, or 0 to
  *           use tier_bits[t]: the down projection's own precision ladder
  *           ([P1] "step 4: three shelves, all on the GPU" and [P2] "Lever 2":
  *           gate/up and down take different formats per tier).  codes[t][2]
@@ -147,7 +163,10 @@ typedef struct {
  *   kind = MOE_SRC_CODES: already-quantised blocks: q[mat] host uint8
  *                         [E][rows][cols] (one code per weight, each <= the
  *                         largest code of the expert's tier), d[mat], m[mat]
- *                         host fp16 bit patterns [E][rows][cols/32].
+ *                         host fp16 bit patterns [E][rows][cols/32].  For a
+ *                         matrix whose table is MXFP4, q holds E2M1 codes
+ *                         (0..15), the low byte of each d entry the block's
+ *                         E8M0 byte (in [2, 252]) and m is not read.
  * rows x cols is I x H for MOE_GATE and MOE_UP, H x I for MOE_DOWN. */
 typedef struct {
   int32_t kind;
@@ -158,8 +177,8 @@ typedef struct {
 } moe_expert_source;
 
 /* Size in bytes of one tier table: `which` = MOE_CODES or MOE_DM, for
- * `n_slots` experts at `bits` bits of matrix `mat`.  Returns 0 for invalid
- * arguments. */
+ * `n_slots` experts at `bits` bits (or MOE_MXFP4) of matrix `mat`.  Returns 0
+ * for invalid arguments. */
 size_t moe_tier_table_bytes(const moe_dims* dims, int32_t bits, int32_t n_slots,
                             int32_t mat, int32_t which);
 
@@ -187,8 +206,12 @@ size_t moe_tier_table_bytes(const moe_dims* dims, int32_t bits, int32_t n_slots,
  * Quantiser (MOE_SRC_F32), per block of 32 weights, each step one IEEE
  * rounding to nearest-even: lo/hi = min/max; m = f16(lo);
  * d = f16(f32(f32(hi - lo) / L)); q = clamp(rint(f32(f32(x - m) / d)), 0, L),
- * q = 0 when d == 0; L = 2^bits - 1.  Non-finite weights, a scale or min
- * that overflows fp16, or (MOE_SRC_CODES) a code above L return MOE_EINVAL.
+ * q = 0 when d == 0; L = 2^bits - 1.  MXFP4 blocks: X = floor(log2(max|x|))
+ * - 2 clamped to [-125, 125] (X = -125 for an all-zero block), each q the
+ * E2M1 code nearest to x / 2^X (exact), ties to the even mantissa, magnitudes
+ * above 6 saturating to 6, zero stored as code 0.  Non-finite weights, a
+ * scale or min that overflows fp16, or (MOE_SRC_CODES) a code above L or an
+ * E8M0 byte outside [2, 252] return MOE_EINVAL.
  * Synchronous; not capturable. */
 int moe_build_tiers(const moe_dims* dims, const uint64_t* popularity,
                     const int32_t n_slots[3], const int32_t tier_bits[3],

@@ -22,7 +22,7 @@ import numpy as np
 __all__ = [
     "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_ENOSPC", "MOE_EHIP",
     "MOE_F32", "MOE_BF16", "MOE_GATE", "MOE_UP", "MOE_DOWN", "MOE_CODES", "MOE_DM",
-    "MOE_SRC_F32", "MOE_SRC_CODES",
+    "MOE_SRC_F32", "MOE_SRC_CODES", "MOE_MXFP4",
     "MoeError", "MoeLibraryMissing", "MoeDims", "MoeLayer", "MoeExpertSource",
     "lib", "library_path", "status_string", "dims", "tier_table_bytes",
     "build_tiers", "plan_tiers", "route", "forward_decode", "forward_prefill", "workspace_bytes",
@@ -34,6 +34,8 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_GATE, MOE_UP, MOE_DOWN = 0, 1, 2
 MOE_CODES, MOE_DM = 0, 1
 MOE_SRC_F32, MOE_SRC_CODES = 0, 1
+# format code of an MXFP4 table (E2M1 codes, one E8M0 scale byte per block)
+MOE_MXFP4 = 0x14
 
 #: Kernel ids reported by the launch trace (moe_kernel_id in moe.h).
 KERNEL_NAMES = {
@@ -335,11 +337,15 @@ class DeviceLayer:
                 nc = tier_table_bytes(d, bits, self.n_slots[t], m, MOE_CODES)
                 nd = tier_table_bytes(d, bits, self.n_slots[t], m, MOE_DM)
                 self.codes[t][m] = torch.zeros(nc, dtype=torch.uint8, device=device)
-                self.dm[t][m] = torch.zeros(nd // 4, dtype=torch.int32, device=device)
+                # (d, m) words, or one E8M0 byte per block for MXFP4
+                if bits == MOE_MXFP4:
+                    self.dm[t][m] = torch.zeros(nd, dtype=torch.uint8, device=device)
+                else:
+                    self.dm[t][m] = torch.zeros(nd // 4, dtype=torch.int32, device=device)
         self.shared = None if shared is None else [to_dev(s, act_t) for s in shared]
 
     def matrix_bits(self, t: int, m: int) -> int:
-        """Code width of tier t's matrix m."""
+        """Code format of tier t's matrix m (a width, or MOE_MXFP4)."""
         return self.down_bits[t] if m == MOE_DOWN and self.down_bits[t] else self.tier_bits[t]
 
     def c_struct(self) -> MoeLayer:
@@ -377,16 +383,19 @@ def source_f32(gate, up, down):
 
 
 def source_codes(q, d, m):
-    """MoeExpertSource over host codes / fp16 scale / fp16 min arrays per matrix."""
+    """MoeExpertSource over host codes / fp16 scale / fp16 min arrays per matrix.
+
+    For a matrix stored as MXFP4, ``d[i]`` holds the E8M0 bytes (uint16
+    entries, low byte used) and ``m[i]`` may be None."""
     s = MoeExpertSource()
     s.kind = MOE_SRC_CODES
     for i in range(3):
         assert q[i].dtype == np.uint8 and q[i].flags.c_contiguous
         for a in (d[i], m[i]):
-            assert a.dtype in (np.float16, np.uint16) and a.flags.c_contiguous
+            assert a is None or (a.dtype in (np.float16, np.uint16) and a.flags.c_contiguous)
         s.q[i] = q[i].ctypes.data
         s.d[i] = d[i].ctypes.data
-        s.m[i] = m[i].ctypes.data
+        s.m[i] = None if m[i] is None else m[i].ctypes.data
     return s
 
 

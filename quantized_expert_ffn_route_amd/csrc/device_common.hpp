@@ -70,10 +70,63 @@ __device__ __forceinline__ void emit_pair(Sink& sink, int j, uint32_t p, float s
   sink(j, __builtin_fmaf(s, f16_lo(p), m), __builtin_fmaf(s, f16_hi(p), m));
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 blocks: byte j of the 16-byte field holds codes 2j (low nibble) and
+// 2j + 1 (high nibble), and the block scale is the E8M0 byte X + 127.  The
+// CDNA4 conversion v_cvt_scalef32_pk_{bf16,f32}_fp4 turns one byte's two
+// E2M1 codes, times an fp32 scale, into a bf16 or fp32 pair; with the scale
+// 2^X (X in [-125, 125]) the product is exact in either type.  One
+// instruction per two weights.
+// ---------------------------------------------------------------------------
+
+// The E8M0 byte X + 127 as the float 2^X (a normal float for X >= -126).
+__device__ __forceinline__ float mx_scale(uint32_t e) { return __uint_as_float(e << 23); }
+
+template <int B>
+__device__ __forceinline__ uint32_t mx_pair_bf16(uint32_t w, float s) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, B));
+}
+
+template <int B, typename Sink>
+__device__ __forceinline__ void mx_pair(Sink& sink, int j, uint32_t w, float s) {
+  if constexpr (Sink::kBf16) {
+    sink.put(j, mx_pair_bf16<B>(w, s));
+  } else {
+    const auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, B);
+    sink(j, p[0], p[1]);
+  }
+}
+
+template <typename Sink>
+__device__ __forceinline__ void dequant_block_mx(const uint32_t* w, uint32_t e, Sink& sink) {
+  const float s = mx_scale(e);
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    mx_pair<0>(sink, 4 * i + 0, w[i], s);
+    mx_pair<1>(sink, 4 * i + 1, w[i], s);
+    mx_pair<2>(sink, 4 * i + 2, w[i], s);
+    mx_pair<3>(sink, 4 * i + 3, w[i], s);
+  }
+}
+
+template <int BITS, typename Sink>
+__device__ __forceinline__ void dequant_block_affine(const uint32_t* w, uint32_t dm, Sink& sink);
+
 // Dequantise the 32 codes of one block (code field words w[0..bits-1]) and
-// hand pairs j = 0..15 (codes 2j, 2j+1) to `sink(j, lo, hi)`.
+// hand pairs j = 0..15 (codes 2j, 2j+1) to the sink: `sink(j, lo, hi)` as
+// floats, or, for bf16 sinks (Sink::kBf16), `sink.put(j, packed bf16 pair)`.
+// `dm` is the block's (d, m) word, or its E8M0 byte for MXFP4.
 template <int BITS, typename Sink>
 __device__ __forceinline__ void dequant_block(const uint32_t* w, uint32_t dm, Sink& sink) {
+  if constexpr (BITS == kMx4) {
+    dequant_block_mx(w, dm, sink);
+  } else {
+    dequant_block_affine<BITS>(w, dm, sink);
+  }
+}
+
+template <int BITS, typename Sink>
+__device__ __forceinline__ void dequant_block_affine(const uint32_t* w, uint32_t dm, Sink& sink) {
   const BlockScale b = block_scale(dm);
   if constexpr (BITS == 4) {
 #pragma unroll
@@ -98,8 +151,7 @@ __device__ __forceinline__ void dequant_block(const uint32_t* w, uint32_t dm, Si
     const uint32_t last = ((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) |
                           ((w[2] >> 13) & 0x00040004u);
     emit_pair(sink, 15, last, b.s24, b.m);
-  } else {
-    static_assert(BITS == 2, "bits must be 2, 3 or 4");
+  } else if constexpr (BITS == 2) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
       const uint32_t t = w[i] >> 10;
@@ -112,22 +164,30 @@ __device__ __forceinline__ void dequant_block(const uint32_t* w, uint32_t dm, Si
       emit_pair(sink, 8 * i + 6, t & 0x000C000Cu, b.s22, b.m);
       emit_pair(sink, 8 * i + 7, t & 0x00300030u, b.s20, b.m);
     }
+  } else {
+    static_assert(BITS == 2, "format must be 2, 3, 4 bits or MXFP4");
   }
 }
 
 // Sink that rounds pairs to packed bf16 (MFMA operand words).
 struct SinkBf16 {
+  static constexpr bool kBf16 = true;
   uint32_t v[16];
   __device__ __forceinline__ void operator()(int j, float lo, float hi) { v[j] = pack_bf16(lo, hi); }
+  __device__ __forceinline__ void put(int j, uint32_t p) { v[j] = p; }
 };
 
 // Sink that keeps only pairs 4K .. 4K + 3 of a block (the 8 codes of MFMA
 // k-step K), as packed bf16; the other pairs are dead code once inlined.
 template <int K>
 struct SinkBf16Step {
+  static constexpr bool kBf16 = true;
   uint32_t v[4];
   __device__ __forceinline__ void operator()(int j, float lo, float hi) {
     if ((j >> 2) == K) v[j & 3] = pack_bf16(lo, hi);
+  }
+  __device__ __forceinline__ void put(int j, uint32_t p) {
+    if ((j >> 2) == K) v[j & 3] = p;
   }
 };
 
@@ -145,6 +205,7 @@ __device__ __forceinline__ void dequant_kstep(int k, const uint32_t* w, uint32_t
 
 // Sink that keeps fp32 values (fp32 activations).
 struct SinkF32 {
+  static constexpr bool kBf16 = false;
   float v[32];
   __device__ __forceinline__ void operator()(int j, float lo, float hi) {
     v[2 * j] = lo;
@@ -152,10 +213,10 @@ struct SinkF32 {
   }
 };
 
-// Loads the code field of a block: `BITS` dwords.
+// Loads the code field of a block: `BITS` dwords (4 for MXFP4).
 template <int BITS>
 __device__ __forceinline__ void load_field(const uint8_t* p, uint32_t* w) {
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 4 || BITS == kMx4) {
     const uint4 v = *reinterpret_cast<const uint4*>(p);
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   } else if constexpr (BITS == 3) {
@@ -165,6 +226,18 @@ __device__ __forceinline__ void load_field(const uint8_t* p, uint32_t* w) {
     const uint2 v = *reinterpret_cast<const uint2*>(p);
     w[0] = v.x; w[1] = v.y;
   }
+}
+
+// The code field of block `idx` of a table and its scale entry: the (d, m)
+// word, or the zero-extended E8M0 byte of an MXFP4 table.
+template <int BITS>
+__device__ __forceinline__ const uint8_t* field_ptr(const uint8_t* codes, size_t idx) {
+  return codes + idx * field_bytes(BITS);
+}
+template <int BITS>
+__device__ __forceinline__ uint32_t load_scale(const uint32_t* dm, size_t idx) {
+  if constexpr (BITS == kMx4) return reinterpret_cast<const uint8_t*>(dm)[idx];
+  else return dm[idx];
 }
 
 // ---------------------------------------------------------------------------

@@ -17,12 +17,21 @@ constexpr int kGroup = 16;
 // Tier index used for the shared expert (dense weights in the act dtype).
 constexpr int kDenseTier = 3;
 
+// Code formats of a tier table: the affine widths 2, 3, 4 and MXFP4.
+constexpr int kMx4 = MOE_MXFP4;
+__host__ __device__ constexpr bool valid_format(int f) {
+  return f == 2 || f == 3 || f == 4 || f == kMx4;
+}
+// Bytes of one block's code field and of its scale entry in the dm table.
+__host__ __device__ constexpr int field_bytes(int f) { return f == kMx4 ? 16 : 4 * f; }
+__host__ __device__ constexpr int scale_bytes(int f) { return f == kMx4 ? 1 : 4; }
+
 // One expert of a decode group together with the tokens that route to it.
 struct Item {
   int32_t expert;          // expert id, -1 for the shared expert
   int32_t tier;            // 0..2 quantised tier, kDenseTier, or -1 (skip)
   int32_t slot;            // slot inside the tier table
-  int32_t bits;            // code widths: gate/up | down << 8 (0 for dense)
+  int32_t bits;            // code formats: gate/up | down << 8 (0 for dense)
   int32_t route[kGroup];   // row of h for token t of the group, or -1
   float gw[kGroup];        // mixing weight of token t (0 when not routed)
 };
@@ -30,9 +39,9 @@ struct Item {
 // Kernel-side view of the expert tables of one layer.
 struct Tables {
   const uint8_t* codes[3][3];
-  const uint32_t* dm[3][3];
-  int32_t bits[3];         // gate / up code width of each tier
-  int32_t bits_dn[3];      // down code width of each tier
+  const uint32_t* dm[3][3];  // (d, m) words; uint8 E8M0 bytes for MXFP4
+  int32_t bits[3];         // gate / up code format of each tier
+  int32_t bits_dn[3];      // down code format of each tier
   int32_t n_slots[3];
   const void* dense[3];    // shared expert gate / up / down (act dtype)
 };
@@ -165,7 +174,10 @@ void launch_dense_shared_down(const void* h_s, int T, const void* w_down, float*
 
 // Quantise one block of 32 floats; returns MOE_OK or MOE_EINVAL.
 int quantise_block(const float* x, int bits, uint16_t* d, uint16_t* m, uint8_t* q);
-// Pack 32 codes (each <= 2^bits - 1) into a 4*bits-byte code field.
+// Quantise one block of 32 floats to MXFP4: E8M0 byte and E2M1 codes.
+int quantise_block_mx(const float* x, uint8_t* e, uint8_t* q);
+// Pack 32 codes (each <= 2^bits - 1, or E2M1 codes for kMx4) into a
+// field_bytes(bits)-byte code field.
 void encode_codes(const uint8_t* q, int bits, uint8_t* field);
 // Index of block (slot, row, block column) in a tier table of R x C matrices.
 inline size_t tile_block_index(size_t slot, int r, int j, int R, int C) {

@@ -42,9 +42,9 @@ struct Frag<bf16_t> {
   template <int BITS>
   __device__ __forceinline__ void load_quant(const uint8_t* codes, const uint32_t* dm, size_t idx) {
     uint32_t w[4];
-    load_field<BITS>(codes + idx * (4 * BITS), w);
+    load_field<BITS>(field_ptr<BITS>(codes, idx), w);
     SinkBf16 sink;
-    dequant_block<BITS>(w, dm[idx], sink);
+    dequant_block<BITS>(w, load_scale<BITS>(dm, idx), sink);
 #pragma unroll
     for (int i = 0; i < 16; i++) v[i] = sink.v[i];
   }
@@ -69,9 +69,9 @@ struct Frag<float> {
   template <int BITS>
   __device__ __forceinline__ void load_quant(const uint8_t* codes, const uint32_t* dm, size_t idx) {
     uint32_t w[4];
-    load_field<BITS>(codes + idx * (4 * BITS), w);
+    load_field<BITS>(field_ptr<BITS>(codes, idx), w);
     SinkF32 sink;
-    dequant_block<BITS>(w, dm[idx], sink);
+    dequant_block<BITS>(w, load_scale<BITS>(dm, idx), sink);
 #pragma unroll
     for (int i = 0; i < 32; i++) v[i] = sink.v[i];
   }
@@ -100,7 +100,8 @@ template <>
 __device__ __forceinline__ void store_act<float>(float* p, float v) { *p = v; }
 
 // Raw (not yet dequantised) B-operand data of one lane for one super-step:
-// a quantised block's code field and (d, m) word, or 32 dense act values.
+// a quantised block's code field and (d, m) word (MXFP4: scale byte), or 32
+// dense act values.
 template <typename A>
 struct Raw {
   uint32_t v[16 * sizeof(A) / 2];  // dense: 32 act values; quantised: w[0..3], dm in v[4]
@@ -109,8 +110,8 @@ struct Raw {
 template <typename A, int BITS>
 __device__ __forceinline__ void load_raw(Raw<A>& r, const uint8_t* codes, const uint32_t* dm,
                                          size_t idx) {
-  load_field<BITS>(codes + idx * (4 * BITS), r.v);
-  r.v[4] = dm[idx];
+  load_field<BITS>(field_ptr<BITS>(codes, idx), r.v);
+  r.v[4] = load_scale<BITS>(dm, idx);
 }
 
 template <typename A>
@@ -266,6 +267,8 @@ __device__ __forceinline__ void gateup_dispatch(float (*red)[8][64], const A* __
     gateup_item<A, 0, NC>(red, x, T, H, I, rg, 0, 0, tb, wave, NW, lane, rt, h);
   else if (bits == 4)
     gateup_item<A, 4, NC>(red, x, T, H, I, rg, tier, slot, tb, wave, NW, lane, rt, h);
+  else if (bits == kMx4)
+    gateup_item<A, kMx4, NC>(red, x, T, H, I, rg, tier, slot, tb, wave, NW, lane, rt, h);
   else if (bits == 3)
     gateup_item<A, 3, NC>(red, x, T, H, I, rg, tier, slot, tb, wave, NW, lane, rt, h);
   else
@@ -284,7 +287,7 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode_gateup(const Item*
   // the count and this item's header (always inside the items array) in one trip
   const int n = *n_items;
   const int tier = items[u].tier;
-  const int slot = items[u].slot, bits = items[u].bits & 0xFF;   // gate / up width
+  const int slot = items[u].slot, bits = items[u].bits & 0xFF;   // gate / up format
   const int4 routes = *reinterpret_cast<const int4*>(&items[u].route[4 * (lane >> 4)]);
   if (u >= n || tier < 0) return;
   const int rt[4] = {routes.x, routes.y, routes.z, routes.w};
@@ -586,6 +589,7 @@ __global__ __launch_bounds__(1024) void k_decode_down(const Item* __restrict__ i
                          (size_t)(rg * 16 + lm) * I + 128 * c + 32 * lg;
         if (t == kDenseTier) load_down<A, 0>(raw[j], tb, t, idx, dense);
         else if ((it.bits >> 8) == 4) load_down<A, 4>(raw[j], tb, t, idx, dense);
+        else if ((it.bits >> 8) == kMx4) load_down<A, kMx4>(raw[j], tb, t, idx, dense);
         else if ((it.bits >> 8) == 3) load_down<A, 3>(raw[j], tb, t, idx, dense);
         else load_down<A, 2>(raw[j], tb, t, idx, dense);
       }
@@ -612,6 +616,7 @@ __global__ __launch_bounds__(1024) void k_decode_down(const Item* __restrict__ i
       Frag<A> b;
       if (t == kDenseTier) to_frag<A, 0>(b, raw[j]);
       else if ((it.bits >> 8) == 4) to_frag<A, 4>(b, raw[j]);
+      else if ((it.bits >> 8) == kMx4) to_frag<A, kMx4>(b, raw[j]);
       else if ((it.bits >> 8) == 3) to_frag<A, 3>(b, raw[j]);
       else to_frag<A, 2>(b, raw[j]);
       const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
@@ -727,8 +732,9 @@ __global__ __launch_bounds__(1024) void k_decode1_down(const Item* __restrict__ 
                                            (size_t)row * I + 128 * c + 32 * lg);
       } else {
         const size_t idx = (((size_t)item.slot * nrg + rg) * nbg + c) * 64 + 16 * lg + half * 8 + (lm & 7);
-        const int dbits = item.bits >> 8;       // down width
+        const int dbits = item.bits >> 8;       // down format
         if (dbits == 4) load_raw<bf16_t, 4>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
+        else if (dbits == kMx4) load_raw<bf16_t, kMx4>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
         else if (dbits == 3) load_raw<bf16_t, 3>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
         else load_raw<bf16_t, 2>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
       }
@@ -747,6 +753,7 @@ __global__ __launch_bounds__(1024) void k_decode1_down(const Item* __restrict__ 
       Frag<bf16_t> b;
       if (hx.tier == kDenseTier) to_frag<bf16_t, 0>(b, raw[j]);
       else if ((hx.bits >> 8) == 4) to_frag<bf16_t, 4>(b, raw[j]);
+      else if ((hx.bits >> 8) == kMx4) to_frag<bf16_t, kMx4>(b, raw[j]);
       else if ((hx.bits >> 8) == 3) to_frag<bf16_t, 3>(b, raw[j]);
       else to_frag<bf16_t, 2>(b, raw[j]);
       const f32x4_t z = {0.f, 0.f, 0.f, 0.f};

@@ -106,8 +106,8 @@ __device__ __forceinline__ void load_braw(BRaw<A, BITS>& r, const Tables& tb, in
     }
   } else {
     const size_t idx = (((size_t)slot * (R / 16) + rg) * (C / 128) + c) * 64 + lane;
-    load_field<BITS>(tb.codes[tier][mat] + idx * (4 * BITS), r.v);
-    r.v[4] = tb.dm[tier][mat][idx];
+    load_field<BITS>(field_ptr<BITS>(tb.codes[tier][mat], idx), r.v);
+    r.v[4] = load_scale<BITS>(tb.dm[tier][mat], idx);
   }
 }
 
@@ -503,12 +503,13 @@ __device__ __forceinline__ void prefill_wg(const PArgs& a) {
     const int tm = a.tier_map[e];
     const int tier = tm >> 16, slot = tm & 0xFFFF;
     if (tier < 0 || tier > 2 || slot >= a.tb.n_slots[tier]) return;
-    // the tier's code width (of this matrix) is uniform over the workgroup
+    // the tier's code format (of this matrix) is uniform over the workgroup
     const int wbits = MODE == kRoutedDown ? a.tb.bits_dn[tier] : a.tb.bits[tier];
     if constexpr (sizeof(A) == 2 && NBG > 0) {
       __shared__ uint4 sL0[kStagePieces], sL1[kStagePieces], sL2[kStagePieces];
       switch (wbits) {
         case 4: prefill_body_lds<4, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2); break;
+        case kMx4: prefill_body_lds<kMx4, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2); break;
         case 3: prefill_body_lds<3, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2); break;
         default: prefill_body_lds<2, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2); break;
       }
@@ -516,6 +517,7 @@ __device__ __forceinline__ void prefill_wg(const PArgs& a) {
       __shared__ uint32_t sA[2 * ROWS * PT<A>::RU];
       switch (wbits) {
         case 4: prefill_body<A, 4, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
+        case kMx4: prefill_body<A, kMx4, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
         case 3: prefill_body<A, 3, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
         default: prefill_body<A, 2, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
       }

@@ -45,8 +45,7 @@ int check_tiers(const moe_dims* d, const int32_t n_slots[3], const int32_t tier_
   for (int t = 0; t < 3; t++) {
     if (n_slots[t] < 0) return MOE_EINVAL;
     sum += n_slots[t];
-    if (n_slots[t] > 0 && tier_bits[t] != 2 && tier_bits[t] != 3 && tier_bits[t] != 4)
-      return MOE_EINVAL;
+    if (n_slots[t] > 0 && !valid_format(tier_bits[t])) return MOE_EINVAL;
   }
   return sum == d->n_experts ? MOE_OK : MOE_EINVAL;
 }
@@ -58,8 +57,7 @@ int check_layer(const moe_dims* d, const moe_layer* L) {
   int rc = check_tiers(d, L->n_slots, L->tier_bits);
   if (rc) return rc;
   for (int t = 0; t < 3; t++)
-    if (L->down_bits[t] != 0 && L->down_bits[t] != 2 && L->down_bits[t] != 3 && L->down_bits[t] != 4)
-      return MOE_EINVAL;
+    if (L->down_bits[t] != 0 && !valid_format(L->down_bits[t])) return MOE_EINVAL;
   for (int t = 0; t < 3; t++) {
     if (L->n_slots[t] == 0) continue;
     for (int m = 0; m < 3; m++)
@@ -245,12 +243,12 @@ int moe_set_trace(hipEvent_t* events, int32_t* tags, int32_t capacity, int32_t* 
 size_t moe_tier_table_bytes(const moe_dims* dims, int32_t bits, int32_t n_slots, int32_t mat,
                             int32_t which) {
   if (check_dims(dims) != MOE_OK || n_slots < 0 || mat < 0 || mat > 2) return 0;
-  if (bits != 2 && bits != 3 && bits != 4) return 0;
+  if (!valid_format(bits)) return 0;
   int rows, cols;
   mat_shape(dims, mat, &rows, &cols);
   const size_t blocks = (size_t)n_slots * rows * (cols / 32);
-  if (which == MOE_CODES) return blocks * 4 * bits;
-  if (which == MOE_DM) return blocks * 4;
+  if (which == MOE_CODES) return blocks * field_bytes(bits);
+  if (which == MOE_DM) return blocks * scale_bytes(bits);
   return 0;
 }
 
@@ -370,7 +368,7 @@ int moe_build_tiers(const moe_dims* dims, const uint64_t* popularity, const int3
   if (src->kind != MOE_SRC_F32 && src->kind != MOE_SRC_CODES) return MOE_EINVAL;
   for (int m = 0; m < 3; m++) {
     if (src->kind == MOE_SRC_F32 && !src->w[m]) return MOE_EINVAL;
-    if (src->kind == MOE_SRC_CODES && (!src->q[m] || !src->d[m] || !src->m[m])) return MOE_EINVAL;
+    if (src->kind == MOE_SRC_CODES && (!src->q[m] || !src->d[m])) return MOE_EINVAL;
   }
   for (int t = 0; t < 3; t++)
     if (n_slots[t] > 0)
@@ -381,14 +379,21 @@ int moe_build_tiers(const moe_dims* dims, const uint64_t* popularity, const int3
   int32_t mbits[3][3];
   for (int t = 0; t < 3; t++) {
     const int dn = dst->down_bits[t];
-    if (dn != 0 && dn != 2 && dn != 3 && dn != 4) return MOE_EINVAL;
+    if (dn != 0 && !valid_format(dn)) return MOE_EINVAL;
     for (int m = 0; m < 3; m++) mbits[t][m] = m == MOE_DOWN && dn ? dn : tier_bits[t];
   }
+  // affine blocks given as codes need their min table
+  for (int t = 0; t < 3; t++)
+    for (int m = 0; m < 3; m++)
+      if (src->kind == MOE_SRC_CODES && n_slots[t] > 0 && mbits[t][m] != kMx4 && !src->m[m])
+        return MOE_EINVAL;
 
   std::atomic<int> status{MOE_OK};
   // pack one (tier, matrix, slot) expert matrix into `codes`/`dm`
   auto pack_one = [&](int t, int m, int slot, uint8_t* codes, uint32_t* dm) {
-    const int bits = mbits[t][m], L = (1 << bits) - 1;
+    const int bits = mbits[t][m];
+    const bool mx = bits == kMx4;
+    const int L = mx ? 15 : (1 << bits) - 1, fb = field_bytes(bits);
     const int e = order[start[t] + slot];
     int R, C;
     mat_shape(dims, m, &R, &C);
@@ -396,10 +401,13 @@ int moe_build_tiers(const moe_dims* dims, const uint64_t* popularity, const int3
     uint8_t q[32], field[16];
     for (int r = 0; r < R; r++) {
       for (int j = 0; j < nb; j++) {
-        uint16_t db, mb;
+        uint16_t db = 0, mb = 0;
+        uint8_t eb = 0;
         const size_t blk = ((size_t)e * R + r) * nb + j;
         if (src->kind == MOE_SRC_F32) {
-          if (quantise_block(src->w[m] + blk * 32, bits, &db, &mb, q) != MOE_OK) {
+          const int rc = mx ? quantise_block_mx(src->w[m] + blk * 32, &eb, q)
+                            : quantise_block(src->w[m] + blk * 32, bits, &db, &mb, q);
+          if (rc != MOE_OK) {
             status = MOE_EINVAL;
             return;
           }
@@ -412,17 +420,26 @@ int moe_build_tiers(const moe_dims* dims, const uint64_t* popularity, const int3
             }
             q[i] = qs[i];
           }
-          db = src->d[m][blk];
-          mb = src->m[m][blk];
-          if ((db & 0x7C00u) == 0x7C00u || (mb & 0x7C00u) == 0x7C00u) {
-            status = MOE_EINVAL;
-            return;
+          if (mx) {
+            eb = (uint8_t)src->d[m][blk];
+            if (eb < 2 || eb > 252) {
+              status = MOE_EINVAL;
+              return;
+            }
+          } else {
+            db = src->d[m][blk];
+            mb = src->m[m][blk];
+            if ((db & 0x7C00u) == 0x7C00u || (mb & 0x7C00u) == 0x7C00u) {
+              status = MOE_EINVAL;
+              return;
+            }
           }
         }
         encode_codes(q, bits, field);
         const size_t idx = tile_block_index(slot, r, j, R, C);
-        std::memcpy(codes + idx * 4 * bits, field, 4 * bits);
-        dm[idx] = (uint32_t)db | ((uint32_t)mb << 16);
+        std::memcpy(codes + idx * fb, field, fb);
+        if (mx) reinterpret_cast<uint8_t*>(dm)[idx] = eb;
+        else dm[idx] = (uint32_t)db | ((uint32_t)mb << 16);
       }
     }
   };

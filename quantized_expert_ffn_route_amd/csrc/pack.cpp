@@ -63,13 +63,58 @@ int quantise_block(const float* x, int bits, uint16_t* d_out, uint16_t* m_out, u
   return MOE_OK;
 }
 
+// MXFP4 block (OCP Microscaling v1.0; the pages' low down tier, P1 "step 4:
+// three shelves, all on the GPU"): 32 E2M1 codes sharing the scale 2^X with
+// X = floor(log2(max|x|)) - 2, clamped to [-125, 125] so that every element
+// is a normal float (X = -125 for an all-zero block).  Each code is the E2M1
+// value nearest to x / 2^X (exact in double), ties to the even mantissa,
+// magnitudes above 6 saturating to 6; zero is code 0.
+int quantise_block_mx(const float* x, uint8_t* e_out, uint8_t* q) {
+  float amax = 0.0f;
+  for (int i = 0; i < 32; i++) {
+    if (!std::isfinite(x[i])) return MOE_EINVAL;
+    amax = std::fabs(x[i]) > amax ? std::fabs(x[i]) : amax;
+  }
+  int X = -125;
+  if (amax > 0.0f) {
+    int ex;
+    std::frexp(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1): floor(log2) = ex - 1
+    X = ex - 1 - 2;
+  }
+  X = X < -125 ? -125 : (X > 125 ? 125 : X);
+  // E2M1 magnitudes by code; a magnitude moves up to code k past the midpoint
+  // of codes k-1 and k, or at it when k is even (the even mantissa)
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  for (int i = 0; i < 32; i++) {
+    const double t = std::ldexp((double)x[i], -X);
+    const double a = std::fabs(t);
+    int k = 0;
+    if (a > 6.0) {
+      k = 7;
+    } else {
+      for (int c = 1; c < 8; c++) {
+        const double mid = 0.5 * (mag[c - 1] + mag[c]);
+        if (a > mid || (a == mid && (c & 1) == 0)) k = c;
+      }
+    }
+    q[i] = (uint8_t)(k | (t < 0.0 && k > 0 ? 8 : 0));
+  }
+  *e_out = (uint8_t)(X + 127);
+  return MOE_OK;
+}
+
 // Code field of one block: `bits` little-endian 32-bit words.  In every word
 // the low half holds even-numbered codes and the high half the following odd
 // codes at the same offsets, packed from bit 0.  4 bits: word i holds codes
 // 8i..8i+7; 2 bits: word i holds codes 16i..16i+15; 3 bits: word i holds
 // codes 10i..10i+9 and the top bit of each half-word of words 0..2 carries
 // one bit of codes 30 (low halves) and 31 (high halves).
+// MXFP4: 16 bytes, code k in bits 4k..4k+3 (byte k/2, low nibble for even k).
 void encode_codes(const uint8_t* q, int bits, uint8_t* field) {
+  if (bits == kMx4) {
+    for (int j = 0; j < 16; j++) field[j] = (uint8_t)((q[2 * j] & 15u) | (q[2 * j + 1] & 15u) << 4);
+    return;
+  }
   uint32_t w[4] = {0, 0, 0, 0};
   if (bits == 4) {
     for (int k = 0; k < 32; k++) {

@@ -35,6 +35,11 @@ class TestLayer:
     popularity: np.ndarray
 
 
+def _quantise(w, fmt):
+    """The oracle's quantiser of the table format ``fmt`` (a width or MXFP4)."""
+    return O.quantise_rows_mx(w) if fmt == O.MXFP4 else O.quantise_rows(w, fmt)
+
+
 def popularity_from_calibration(spec, w_router, bias, seed, n=1024):
     """Route counts of ``n`` calibration tokens (oracle routing, host)."""
     xc = synth.tokens(spec, n, seed)
@@ -70,14 +75,15 @@ def make_layer(spec: synth.LayerSpec, seed: int = 0, source: str = "f32",
 
         def experts(e):
             if e not in cache:
-                cache[e] = O.ExpertBlocks(bits_of[e], O.quantise_rows(gate[e], bits_of[e]),
-                                          O.quantise_rows(up[e], bits_of[e]),
-                                          O.quantise_rows(down[e], dbits_of[e]))
+                cache[e] = O.ExpertBlocks(bits_of[e], _quantise(gate[e], bits_of[e]),
+                                          _quantise(up[e], bits_of[e]),
+                                          _quantise(down[e], dbits_of[e]))
             return cache[e]
         src_arrays = (gate, up, down)
         src = M.source_f32(*src_arrays)
     else:
         assert spec.down_bits is None, "pre-quantised sources use one width per tier"
+        assert O.MXFP4 not in spec.tier_bits, "pre-quantised sources hold affine blocks"
         per = [synth.expert_codes(spec, bits_of[e], seed + 2, e) for e in range(spec.n_experts)]
 
         def experts(e):

@@ -532,3 +532,35 @@ def test_per_matrix_ladder(down_bits):
     np.testing.assert_array_equal(ids, oids)
     ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
     check_y(y, ref["y"], "bf16", f"prefill T=300, down bits {down_bits}")
+
+
+# MXFP4 tables (the pages' low down tier): as a whole tier and as the down
+# ladder of the lower tiers, through decode (fp32 and bf16 activations) and
+# prefill
+MX = 0x14
+
+
+@pytest.mark.parametrize("tier_bits,down_bits,act", [
+    ((4, 3, MX), None, "bf16"),
+    ((4, 3, 2), (4, MX, MX), "bf16"),
+    ((MX, 3, 2), None, "f32"),
+])
+def test_mxfp4_tiers(tier_bits, down_bits, act):
+    spec = MID.with_(tier_bits=tier_bits, down_bits=down_bits, act=act)
+    tl = make_layer(spec, seed=14)
+    for T in (1, 6):
+        x = synth.tokens(spec, T, 100 + T)
+        y, ids, w = run_decode(tl, x)
+        _, oids, g = O.route(act_f64(x, act), tl.ol.w_router, tl.ol.bias, spec.top_k, exact=True)
+        np.testing.assert_array_equal(ids, oids)
+        ref = O.moe_layer(act_f64(x, act), tl.ol)
+        check_y(y, ref["y"], act, f"decode T={T}, {tier_bits}/{down_bits} {act}")
+        if act == "bf16":
+            yb, _, _ = run_decode(tl, x, M.MOE_BF16)
+            check_y(yb, O.output_cast(ref["y"], "bf16"), act, f"decode T={T} bf16 out")
+    x = synth.tokens(spec, 300, 105)
+    y, ids, w, _, _ = run_prefill(tl, x)
+    _, oids, g = O.route(act_f64(x, act), tl.ol.w_router, tl.ol.bias, spec.top_k, exact=True)
+    np.testing.assert_array_equal(ids, oids)
+    ref = O.moe_layer(act_f64(x, act), tl.ol)
+    check_y(y, ref["y"], act, f"prefill T=300, {tier_bits}/{down_bits} {act}")

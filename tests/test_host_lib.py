@@ -170,7 +170,9 @@ def _host_tables(d, n_slots, tier_bits, down_bits=None):
         for m in range(3):
             b = _mbits(tier_bits, down_bits, t, m)
             codes[t][m] = np.zeros(M.tier_table_bytes(d, b, n_slots[t], m, M.MOE_CODES), np.uint8)
-            dm[t][m] = np.zeros(M.tier_table_bytes(d, b, n_slots[t], m, M.MOE_DM) // 4, np.uint32)
+            nd = M.tier_table_bytes(d, b, n_slots[t], m, M.MOE_DM)
+            # MXFP4: one scale byte per block; otherwise (d, m) words
+            dm[t][m] = np.zeros(nd, np.uint8) if b == M.MOE_MXFP4 else np.zeros(nd // 4, np.uint32)
             L.codes[t][m] = codes[t][m].ctypes.data
             L.dm[t][m] = dm[t][m].ctypes.data
     return L, codes, dm
@@ -185,6 +187,10 @@ def _oracle_tables(blocks_by_expert, slot_expert, n_slots, tier_bits, down_bits=
             continue
         for m in range(3):
             experts = [slot_expert[start[t] + s] for s in range(n_slots[t])]
+            if _mbits(tier_bits, down_bits, t, m) == O.MXFP4:
+                out[(t, m)] = O.pack_tiles_mx(np.stack([blocks_by_expert[e][m].q for e in experts]),
+                                              np.stack([blocks_by_expert[e][m].e for e in experts]))
+                continue
             q = np.stack([blocks_by_expert[e][m][2] for e in experts])
             dd = np.stack([blocks_by_expert[e][m][0] for e in experts])
             mm = np.stack([blocks_by_expert[e][m][1] for e in experts])
@@ -203,8 +209,17 @@ def test_build_tiers_map_only_matches_oracle():
         np.testing.assert_array_equal(sexp, want_se)
 
 
+MX = 0x14     # the format code of MXFP4 tables, as the C header defines it
+
+
+def _quantise(w, fmt):
+    return O.quantise_rows_mx(w) if fmt == O.MXFP4 else O.quantise_rows(w, fmt)
+
+
 @pytest.mark.parametrize("tier_bits,down_bits", [((4, 3, 2), None), ((2, 4, 3), None),
-                                                  ((4, 3, 2), (4, 4, 3)), ((3, 3, 2), (0, 4, 0))])
+                                                  ((4, 3, 2), (4, 4, 3)), ((3, 3, 2), (0, 4, 0)),
+                                                  ((4, 3, MX), None), ((4, 3, 2), (4, MX, MX)),
+                                                  ((MX, 3, 2), (2, 0, 0))])
 def test_build_tiers_f32_bit_exact_vs_oracle(tier_bits, down_bits):
     spec = synth.TINY.with_(n_experts=12, n_slots=(3, 6, 3))
     d = M.dims(spec.hidden, spec.inter, spec.n_experts, spec.top_k, False, spec.act)
@@ -216,7 +231,7 @@ def test_build_tiers_f32_bit_exact_vs_oracle(tier_bits, down_bits):
     want_map, want_se = O.build_tiers(pop, spec.n_slots)
     np.testing.assert_array_equal(tmap, want_map)
     tier_of = {e: int(want_map[e]) >> 16 for e in range(spec.n_experts)}
-    blocks = {e: [O.quantise_rows(w[e], _mbits(tier_bits, down_bits, tier_of[e], m))
+    blocks = {e: [_quantise(w[e], _mbits(tier_bits, down_bits, tier_of[e], m))
                   for m, w in enumerate((gate, up, down))]
               for e in range(spec.n_experts)}
     want = _oracle_tables(blocks, want_se, spec.n_slots, tier_bits, down_bits)
@@ -246,6 +261,95 @@ def test_build_tiers_codes_source_bit_exact_vs_oracle():
     for (t, m), (wc, wd) in want.items():
         np.testing.assert_array_equal(codes[t][m], wc)
         np.testing.assert_array_equal(dm[t][m], wd)
+
+
+def test_build_tiers_mx_ties_saturation_and_range_vs_oracle():
+    # one expert whose blocks hit every rounding case of the MXFP4 quantiser:
+    # exact grid points, midpoints (ties to even), saturation above 6, zero
+    # blocks and blocks whose shared exponent is clamped at either end
+    H = I = 128
+    d = M.dims(H, I, 1, 1, False, "f32")
+    rng = np.random.default_rng(31)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 7.99])
+    mats = []
+    for m in range(3):
+        w = rng.standard_normal((I, H)) * np.exp(rng.uniform(-10, 3, (I, 1)))
+        for r in range(0, I, 3):
+            k = int(rng.integers(-20, 20))
+            sgn = rng.choice([-1.0, 1.0], size=10)
+            w[r, 32 * (r % 4):32 * (r % 4) + 10] = sgn * mids * 2.0 ** k
+        w[5, :32] = 0.0
+        w[6, 32:64] = 2.0 ** -140                  # exponent clamped at -125
+        w[7, 64:96] = 1.5 * 2.0 ** 127             # exponent at +125
+        mats.append(np.ascontiguousarray(w.astype(np.float32)[None]))
+    L, codes, dm = _host_tables(d, (1, 0, 0), (MX, 3, 2))
+    M.build_tiers(d, np.ones(1, np.uint64), (1, 0, 0), (MX, 3, 2), M.source_f32(*mats), L,
+                  dst_on_device=False)
+    for m in range(3):
+        b = O.quantise_rows_mx(mats[m][0])
+        wc, we = O.pack_tiles_mx(b.q[None], b.e[None])
+        np.testing.assert_array_equal(codes[0][m], wc, err_msg=f"codes mat {m}")
+        np.testing.assert_array_equal(dm[0][m], we, err_msg=f"scales mat {m}")
+
+
+def test_build_tiers_mx_codes_source_and_range_check():
+    spec = synth.TINY.with_(hidden=256, inter=128, n_experts=4, n_slots=(1, 2, 1))
+    tier_bits, down_bits = (4, 3, 2), (MX, 0, MX)
+    d = M.dims(spec.hidden, spec.inter, spec.n_experts, spec.top_k, False, spec.act)
+    pop = np.array([9, 7, 5, 3], np.uint64)
+    rng = np.random.default_rng(32)
+    shapes = ((128, 256), (128, 256), (256, 128))
+    tmap, sexp = M.build_tiers(d, pop, spec.n_slots, tier_bits)
+    tier_of = [int(v) >> 16 for v in tmap]
+    q, dd, mm = [], [], []
+    blocks = {e: [None] * 3 for e in range(4)}
+    for mi, (r, c) in enumerate(shapes):
+        qm = np.zeros((4, r, c), np.uint8)
+        dm_ = np.zeros((4, r, c // 32), np.uint16)
+        mn = np.zeros((4, r, c // 32), np.float16)
+        for e in range(4):
+            f = _mbits(tier_bits, down_bits, tier_of[e], mi)
+            if f == MX:
+                qm[e] = rng.integers(0, 16, (r, c))
+                dm_[e] = rng.integers(2, 253, (r, c // 32))
+                blocks[e][mi] = O.MxBlocks(dm_[e].astype(np.uint8), qm[e])
+            else:
+                qm[e] = rng.integers(0, 2 ** f, (r, c))
+                dv = rng.uniform(0.01, 1, (r, c // 32)).astype(np.float16)
+                mv = rng.uniform(-1, 1, (r, c // 32)).astype(np.float16)
+                dm_[e] = dv.view(np.uint16)
+                mn[e] = mv
+                blocks[e][mi] = (dv, mv, qm[e])
+        q.append(qm)
+        dd.append(dm_)
+        mm.append(mn)
+    L, codes, dm = _host_tables(d, spec.n_slots, tier_bits, down_bits)
+    M.build_tiers(d, pop, spec.n_slots, tier_bits, M.source_codes(q, dd, mm), L,
+                  dst_on_device=False)
+    want = _oracle_tables(blocks, sexp, spec.n_slots, tier_bits, down_bits)
+    for (t, m), (wc, wd) in want.items():
+        np.testing.assert_array_equal(codes[t][m], wc, err_msg=f"codes tier {t} mat {m}")
+        np.testing.assert_array_equal(dm[t][m], wd, err_msg=f"scales tier {t} mat {m}")
+    # an E8M0 byte outside [2, 252] is rejected
+    e_mx = [e for e in range(4) if tier_of[e] == 0][0]
+    for bad in (1, 253):
+        dd[2][e_mx, 0, 0] = bad
+        with pytest.raises(M.MoeError) as err:
+            M.build_tiers(d, pop, spec.n_slots, tier_bits, M.source_codes(q, dd, mm), L,
+                          dst_on_device=False)
+        assert err.value.status == M.MOE_EINVAL
+    dd[2][e_mx, 0, 0] = 100
+
+
+def test_mx_table_bytes_and_layer_checks():
+    d = M.dims(2048, 512, 512, 10, True, "bf16")
+    # 16 code bytes and one scale byte per block of 32
+    assert M.tier_table_bytes(d, MX, 128, M.MOE_DOWN, M.MOE_CODES) == 128 * 2048 * 512 // 32 * 16
+    assert M.tier_table_bytes(d, MX, 128, M.MOE_DOWN, M.MOE_DM) == 128 * 2048 * 512 // 32
+    assert M.tier_table_bytes(d, 5, 128, M.MOE_DOWN, M.MOE_DM) == 0
+    # the planner's error model has no MXFP4 weight
+    with pytest.raises(M.MoeError):
+        M.plan_tiers(d, np.ones(512, np.uint64), (4, 3, MX), 1 << 40)
 
 
 def test_build_tiers_rejects_bad_input():
