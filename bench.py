@@ -43,6 +43,20 @@ N_LAYERS = 48
 N_GRAPHS = 16
 
 
+MXFP4 = 0x14                   # format code of MXFP4 tables
+
+
+def _formats(text):
+    out = tuple(MXFP4 if v.strip().lower() == "mx" else int(v) for v in text.split(","))
+    if len(out) != 3:
+        raise argparse.ArgumentTypeError("three comma-separated formats")
+    return out
+
+
+def fmt_name(f):
+    return "MXFP4" if f == MXFP4 else f"{f}-bit"
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -55,6 +69,10 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
     ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--tier-bits", default="4,3,2", type=_formats,
+                    help="code format of each tier: 2, 3, 4 or mx (MXFP4)")
+    ap.add_argument("--down-bits", default=None, type=_formats,
+                    help="the down matrices' own format per tier (0: the tier's)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run an elementwise copy of 256 MiB (fp32 -> fp32) three times, the "
                          "known-size reference for HBM byte counters")
@@ -80,7 +98,8 @@ def make_stack(M, torch, spec, n_layers, seed):
     Tier tables: iid uniform code bytes (every byte pattern is a valid code
     field), scales d = sigma / std(q) * U(0.8, 1.2) and mins
     m = -d L / 2 + N(0, (0.05 sigma)^2), sigma = 1/sqrt(fan_in), so the
-    dequantised weights have std ~ 1/sqrt(fan_in).  Router N(0, 0.02^2) in
+    dequantised weights have std ~ 1/sqrt(fan_in); MXFP4 tables take the
+    scale 2^X with X = round(log2(sigma / 2.93)) - {0 or 1} per block.  Router N(0, 0.02^2) in
     bf16 with bias 0.27 * N(0, 1); shared expert N(0, 1/fan_in) in bf16.
     Popularity per layer: route counts of 4096 N(0,1) calibration tokens
     (moe_route), ranked into tiers by moe_build_tiers.
@@ -99,17 +118,24 @@ def make_stack(M, torch, spec, n_layers, seed):
         bias = (torch.randn(E, generator=gen, device="cuda") * synth.DEFAULT_BIAS_BETA).float()
         shared = [(torch.randn(shape, generator=gen, device="cuda") / np.sqrt(shape[1])).to(torch.bfloat16)
                   for shape in ((I, H), (I, H), (H, I))]
-        lay = M.DeviceLayer(d, spec.n_slots, spec.tier_bits, (w_r, bias), shared)
+        lay = M.DeviceLayer(d, spec.n_slots, spec.tier_bits, (w_r, bias), shared,
+                            down_bits=spec.down_bits)
         for t in range(3):
-            bits = spec.tier_bits[t]
-            L = (1 << bits) - 1
-            std_q = float(np.sqrt(((L + 1) ** 2 - 1) / 12.0))
             for m in range(3):
+                bits = lay.matrix_bits(t, m)
                 fan_in = H if m != M.MOE_DOWN else I
                 sigma = 1.0 / np.sqrt(fan_in)
                 c = lay.codes[t][m]
                 c.copy_(torch.randint(0, 256, c.shape, generator=gen, device="cuda", dtype=torch.uint8))
                 n = lay.dm[t][m].numel()
+                if bits == MXFP4:
+                    # uniform E2M1 codes have rms 2.93: scale 2^X ~ sigma / 2.93
+                    x0 = int(np.round(np.log2(sigma / 2.93)))
+                    e = 127 + x0 - torch.randint(0, 2, (n,), generator=gen, device="cuda")
+                    lay.dm[t][m].copy_(e.to(torch.uint8))
+                    continue
+                L = (1 << bits) - 1
+                std_q = float(np.sqrt(((L + 1) ** 2 - 1) / 12.0))
                 dd = (sigma / std_q) * (0.8 + 0.4 * torch.rand(n, generator=gen, device="cuda"))
                 mm = -dd * (L / 2.0) + 0.05 * sigma * torch.randn(n, generator=gen, device="cuda")
                 db = dd.half().view(torch.int16).to(torch.int32) & 0xFFFF
@@ -163,7 +189,11 @@ def measured_traffic(kernel):
 def table_bytes(spec, bits, mat):
     rows, cols = (spec.hidden, spec.inter) if mat == 2 else (spec.inter, spec.hidden)
     blocks = rows * cols // 32
-    return blocks * (4 * bits + 4)
+    return blocks * (17 if bits == MXFP4 else 4 * bits + 4)
+
+
+def down_format(spec, t):
+    return spec.down_bits[t] if spec.down_bits and spec.down_bits[t] else spec.tier_bits[t]
 
 
 def decode_kernel_bytes(spec, layer, ids_row):
@@ -176,9 +206,10 @@ def decode_kernel_bytes(spec, layer, ids_row):
     experts + shared bf16 down + h read + y written (bf16).
     """
     H, I, E, K = spec.hidden, spec.inter, spec.n_experts, spec.top_k
-    bits = [spec.tier_bits[int(layer.tmap_host[e]) >> 16] for e in ids_row]
-    gu = sum(table_bytes(spec, b, 0) + table_bytes(spec, b, 1) for b in bits) + 2 * I * H * 2
-    dn = sum(table_bytes(spec, b, 2) for b in bits) + H * I * 2
+    tiers = [int(layer.tmap_host[e]) >> 16 for e in ids_row]
+    gu = sum(table_bytes(spec, spec.tier_bits[t], 0) + table_bytes(spec, spec.tier_bits[t], 1)
+             for t in tiers) + 2 * I * H * 2
+    dn = sum(table_bytes(spec, down_format(spec, t), 2) for t in tiers) + H * I * 2
     return {
         "router_keys": E * H * 2 + E * 4 + H * 2 + E * 8,
         "topk_items": E * 8 + K * 8 + (K + 1) * 136,
@@ -384,8 +415,15 @@ def main():
     import quantized_expert_ffn_route_amd as M
 
     M.lib()                       # fail loudly if the HIP library is missing
-    spec = synth.FULL
+    spec = synth.FULL.with_(tier_bits=args.tier_bits,
+                            down_bits=None if args.down_bits is None or not any(args.down_bits)
+                            else args.down_bits)
     H, I, K = spec.hidden, spec.inter, spec.top_k
+    # the committed counter record was taken on the default formats
+    default_fmt = spec.tier_bits == (4, 3, 2) and not spec.down_bits
+    tiers_txt = "tiers 128/256/128 at " + "/".join(fmt_name(f) for f in spec.tier_bits)
+    if spec.down_bits:
+        tiers_txt += ", down at " + "/".join(fmt_name(down_format(spec, t)) for t in range(3))
     log("building the 48-layer stack")
     d, layers = make_stack(M, torch, spec, N_LAYERS, args.seed)
     gen = torch.Generator(device="cuda")
@@ -471,7 +509,7 @@ def main():
     if dom:
         roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic("decode_gateup"),
+                    "traffic": measured_traffic("decode_gateup") if default_fmt else None,
                     "kernel": "k_decode_gateup", "bytes_per_launch": dom["bytes"],
                     "avg_us": dom["avg_us"]}
     layer_bytes = sum(k["bytes"] for k in kernels.values()) if kernels else None
@@ -499,19 +537,22 @@ def main():
             pk.setdefault(name, []).append(ms)
         routed_gu_flops = 2.0 * T * K * 2 * I * H
         layer_flops = 2.0 * T * (K * 3 * I * H + 3 * I * H + spec.n_experts * H)
-        gu_us = 1e3 * float(np.mean(pk["prefill_gateup"]))
+        # per layer call: a matrix whose tiers mix affine and MXFP4 tables
+        # runs one launch per format family
+        steps = args.prefill_steps
+        gu_us = 1e3 * float(np.sum(pk["prefill_gateup"])) / steps
         prefill = {
             "workload": f"prefill {T} tokens, one full-size layer (rotating over the stack)",
             "tokens_per_s": round(T * args.prefill_steps / pwall, 1),
             "ms_per_layer": round(1e3 * pwall / args.prefill_steps, 3),
             "layer_tflops": round(layer_flops / (pwall / args.prefill_steps) / 1e12, 1),
-            "kernels_avg_us": {n: round(1e3 * float(np.mean(v)), 2) for n, v in pk.items()},
+            "kernels_avg_us": {n: round(1e3 * float(np.sum(v)) / steps, 2) for n, v in pk.items()},
             "roofline": {"bound": "mfma", "kernel": "k_prefill<routed gate/up>",
                          "achieved": round(routed_gu_flops / (gu_us * 1e-6) / 1e12, 1),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(routed_gu_flops / (gu_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
                          "flops_per_launch": routed_gu_flops, "avg_us": round(gu_us, 2),
-                         "traffic": measured_traffic("prefill_gateup")},
+                         "traffic": measured_traffic("prefill_gateup") if default_fmt else None},
         }
         log(f"prefill: {prefill['tokens_per_s']:.0f} tokens/s")
 
@@ -541,9 +582,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded random 4/3/2-bit blocks, bf16 router/shared, N(0,1) tokens)",
+        "data": "synthetic (seeded random quantised blocks, bf16 router/shared, N(0,1) tokens)",
         "config": {"workload": "one full-size MoE layer, batch-1 decode (hidden 2048, 512 experts, "
-                               "top-10 + 1 shared, intermediate 512, tiers 128/256/128 at 4/3/2 bits)"
+                               f"top-10 + 1 shared, intermediate 512, {tiers_txt})"
                                ", timed as one token through 48 distinct layers per step",
                    "layers_per_step": N_LAYERS, "tokens_per_step": 1,
                    "us_per_layer": round(1e6 * wall / (N_LAYERS * args.steps), 3),

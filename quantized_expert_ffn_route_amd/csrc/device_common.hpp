@@ -195,6 +195,15 @@ struct SinkBf16Step {
 template <int BITS>
 __device__ __forceinline__ void dequant_kstep(int k, const uint32_t* w, uint32_t dm,
                                               uint32_t (&out)[4]) {
+  if constexpr (BITS == kMx4) {
+    // k-step k is exactly field word k: four conversions
+    const float s = mx_scale(dm);
+    out[0] = mx_pair_bf16<0>(w[k], s);
+    out[1] = mx_pair_bf16<1>(w[k], s);
+    out[2] = mx_pair_bf16<2>(w[k], s);
+    out[3] = mx_pair_bf16<3>(w[k], s);
+    return;
+  }
   switch (k) {
     case 0: { SinkBf16Step<0> s; dequant_block<BITS>(w, dm, s); for (int i = 0; i < 4; i++) out[i] = s.v[i]; break; }
     case 1: { SinkBf16Step<1> s; dequant_block<BITS>(w, dm, s); for (int i = 0; i < 4; i++) out[i] = s.v[i]; break; }

@@ -480,7 +480,13 @@ __device__ __forceinline__ void prefill_body_lds(const PArgs& a, int grp, int ro
 // NBG > 0 (bf16 routed modes): the unrolled pipeline for NBG chunks; the
 // launcher picks it when the contraction has NBG chunks and the workgroup
 // rows divide the weight rows.  NBG == 0: the register-staged body.
-template <typename A, int MODE, int NBG>
+// FAM selects the table formats a kernel handles: 0 the affine widths, 1
+// MXFP4, -1 all.  Every body inlined into one kernel adds to the register
+// pressure of the others (at the bf16 kernels' 128-register budget the four
+// together spill, each family alone does not), so the bf16 launcher runs one
+// kernel per family present and a workgroup whose tier is of the other
+// family leaves at once.
+template <typename A, int MODE, int NBG, int FAM>
 __device__ __forceinline__ void prefill_wg(const PArgs& a) {
   using C = MC<MODE>;
   constexpr int ROWS = PR<A, MODE>::ROWS;
@@ -505,21 +511,37 @@ __device__ __forceinline__ void prefill_wg(const PArgs& a) {
     if (tier < 0 || tier > 2 || slot >= a.tb.n_slots[tier]) return;
     // the tier's code format (of this matrix) is uniform over the workgroup
     const int wbits = MODE == kRoutedDown ? a.tb.bits_dn[tier] : a.tb.bits[tier];
+    if constexpr (FAM >= 0) {
+      if ((wbits == kMx4) != (FAM == 1)) return;
+    }
     if constexpr (sizeof(A) == 2 && NBG > 0) {
       __shared__ uint4 sL0[kStagePieces], sL1[kStagePieces], sL2[kStagePieces];
-      switch (wbits) {
-        case 4: prefill_body_lds<4, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2); break;
-        case kMx4: prefill_body_lds<kMx4, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2); break;
-        case 3: prefill_body_lds<3, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2); break;
-        default: prefill_body_lds<2, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2); break;
+      if constexpr (FAM == 1) {
+        prefill_body_lds<kMx4, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2);
+      } else {
+        switch (wbits) {
+          case 4: prefill_body_lds<4, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2); break;
+          case 3: prefill_body_lds<3, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2); break;
+          case 2: prefill_body_lds<2, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2); break;
+          default:
+            if constexpr (FAM < 0)
+              prefill_body_lds<kMx4, MODE, NBG>(a, grp, row0, nrows, tier, slot, nt, sL0, sL1, sL2);
+            break;
+        }
       }
     } else {
       __shared__ uint32_t sA[2 * ROWS * PT<A>::RU];
-      switch (wbits) {
-        case 4: prefill_body<A, 4, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
-        case kMx4: prefill_body<A, kMx4, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
-        case 3: prefill_body<A, 3, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
-        default: prefill_body<A, 2, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
+      if constexpr (FAM == 1) {
+        prefill_body<A, kMx4, MODE>(a, grp, row0, nrows, tier, slot, nt, sA);
+      } else {
+        switch (wbits) {
+          case 4: prefill_body<A, 4, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
+          case 3: prefill_body<A, 3, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
+          case 2: prefill_body<A, 2, MODE>(a, grp, row0, nrows, tier, slot, nt, sA); break;
+          default:
+            if constexpr (FAM < 0) prefill_body<A, kMx4, MODE>(a, grp, row0, nrows, tier, slot, nt, sA);
+            break;
+        }
       }
     }
   } else {
@@ -533,13 +555,13 @@ __device__ __forceinline__ void prefill_wg(const PArgs& a) {
 
 // bf16: four waves per SIMD (two workgroups per CU); the fp32 variants keep
 // their registers (no spills) at lower occupancy.
-template <int MODE, int NBG>
+template <int MODE, int NBG, int FAM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_prefill_bf16(PArgs a) {
-  prefill_wg<bf16_t, MODE, NBG>(a);
+  prefill_wg<bf16_t, MODE, NBG, FAM>(a);
 }
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void k_prefill_f32(PArgs a) {
-  prefill_wg<float, MODE, 0>(a);
+  prefill_wg<float, MODE, 0, -1>(a);
 }
 
 template <typename A, int MODE>
@@ -557,15 +579,26 @@ void launch_mode(const PArgs& a, int n_groups, hipStream_t s) {
     int nbg = 0;
     const int k = (MODE == kRoutedDown ? a.I : a.H) / 128;
     if (Nr % C::NWG == 0 && (k & (k - 1)) == 0 && k <= 32) nbg = k;
-    switch (nbg) {
-      case 1: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 1>), grid, dim3(kThreads), 0, s, a); break;
-      case 2: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 2>), grid, dim3(kThreads), 0, s, a); break;
-      case 4: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 4>), grid, dim3(kThreads), 0, s, a); break;
-      case 8: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 8>), grid, dim3(kThreads), 0, s, a); break;
-      case 16: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 16>), grid, dim3(kThreads), 0, s, a); break;
-      case 32: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 32>), grid, dim3(kThreads), 0, s, a); break;
-      default: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 0>), grid, dim3(kThreads), 0, s, a); break;
+    // one launch per format family present in this matrix's tier tables
+    bool fam[2] = {false, false};
+    for (int t = 0; t < 3; t++) {
+      if (a.tb.n_slots[t] == 0) continue;
+      const int f = MODE == kRoutedDown ? a.tb.bits_dn[t] : a.tb.bits[t];
+      fam[f == kMx4] = true;
     }
+#define MOE_PREFILL_FAMILY(F)                                                                         \
+  switch (nbg) {                                                                                      \
+    case 1: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 1, F>), grid, dim3(kThreads), 0, s, a); break;   \
+    case 2: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 2, F>), grid, dim3(kThreads), 0, s, a); break;   \
+    case 4: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 4, F>), grid, dim3(kThreads), 0, s, a); break;   \
+    case 8: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 8, F>), grid, dim3(kThreads), 0, s, a); break;   \
+    case 16: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 16, F>), grid, dim3(kThreads), 0, s, a); break; \
+    case 32: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 32, F>), grid, dim3(kThreads), 0, s, a); break; \
+    default: MOE_LAUNCH(kid, (k_prefill_bf16<MODE, 0, F>), grid, dim3(kThreads), 0, s, a); break;  \
+  }
+    if (fam[0]) MOE_PREFILL_FAMILY(0)
+    if (fam[1]) MOE_PREFILL_FAMILY(1)
+#undef MOE_PREFILL_FAMILY
   } else {
     MOE_LAUNCH(kid, (k_prefill_f32<MODE>), grid, dim3(kThreads), 0, s, a);
   }
