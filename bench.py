@@ -345,7 +345,7 @@ TRAFFIC_KERNELS = [
     ("k_router_keys", "router_keys"), ("k_decode1_gateup", "decode_gateup"),
     ("k_decode_gateup", "decode_gateup"), ("k_decode_down", "decode_down"),
     ("k_prefill_bf16<0,", "prefill_gateup"), ("k_prefill_bf16<2,", "prefill_down"),
-    ("k_dense<0,", "router_approx"), ("k_dense<3,", "router_approx"),
+    ("k_dense<0,", "route_router_approx"), ("k_dense<3,", "router_approx"),
     ("k_dense<1,", "prefill_shared_gateup"),
     ("k_dense<2,", "prefill_shared_down"), ("k_topk_recheck", "topk_recheck"),
     ("k_combine", "combine"),
