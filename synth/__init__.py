@@ -77,8 +77,12 @@ FULL = LayerSpec(hidden=2048, inter=512, n_experts=512, top_k=10, has_shared=Tru
 DEFAULT_BIAS_BETA = 0.27
 
 
+#: Format code of MXFP4 tables (the C header's MOE_MXFP4).
+MXFP4 = 0x14
+
+
 def levels_of(bits: int) -> int:
-    return (1 << bits) - 1
+    return 15 if bits == MXFP4 else (1 << bits) - 1
 
 
 def to_bf16_bits(a) -> np.ndarray:
@@ -169,30 +173,42 @@ def expert_weights_f32(spec: LayerSpec, seed: int, experts: Optional[Sequence[in
     return gate, up, down
 
 
-def expert_codes(spec: LayerSpec, bits: int, seed: int, expert: int):
-    """Random already-quantised blocks of one expert at ``bits`` bits.
+def expert_codes(spec: LayerSpec, bits: int, seed: int, expert: int,
+                 down_bits: Optional[int] = None):
+    """Random already-quantised blocks of one expert at ``bits`` bits
+    (``down_bits`` for the down matrix, when given).
 
     For full-size layers, where quantising 1.6 G float32 weights on the host
     would dominate the run, the blocks are drawn directly: codes uniform on
     ``0..L`` (one byte per weight), scale ``d`` such that the dequantised
     weights have standard deviation ~1/sqrt(fan_in) (times U(0.8, 1.2)), and
     min ``m = -d*L/2 + N(0, (0.05/sqrt(fan_in))^2)``; d and m are rounded to
-    fp16 by NumPy.
+    fp16 by NumPy.  An MXFP4 matrix draws E2M1 codes uniform on 0..15 and the
+    scale byte ``127 + round(log2(sigma / 2.93)) - {0 or 1}`` (uniform E2M1
+    codes have rms 2.93), returned as ``(e, None, q)`` with ``e`` uint8.
 
     Returns ``{"gate": (d, m, q), "up": ..., "down": ...}`` with ``q`` uint8
     ``rows x cols`` and ``d``, ``m`` float16 ``rows x cols/32``.  Stream:
-    ``default_rng([seed, expert, bits])``, matrices drawn in the order gate,
-    up, down, each as q then d then m.
+    ``default_rng([seed, expert, bits])`` (``[seed, expert, bits, down_bits]``
+    when down_bits is given), matrices drawn in the order gate, up, down, each
+    as q then d then m (q then the scale-byte choice for MXFP4).
     """
     H, I = spec.hidden, spec.inter
-    L = levels_of(bits)
-    std_q = np.sqrt(((L + 1) ** 2 - 1) / 12.0)
-    rng = np.random.default_rng([seed, int(expert), int(bits)])
+    key = [seed, int(expert), int(bits)] + ([] if down_bits is None else [int(down_bits)])
+    rng = np.random.default_rng(key)
     out: Dict[str, tuple] = {}
     for name, (rows, cols) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        f = down_bits if (name == "down" and down_bits is not None) else bits
+        L = levels_of(f)
         sigma = 1.0 / np.sqrt(cols)
         q = rng.integers(0, L + 1, size=(rows, cols), dtype=np.uint8)
         nb = cols // 32
+        if f == MXFP4:
+            x0 = int(np.round(np.log2(sigma / 2.93)))
+            e = (127 + x0 - rng.integers(0, 2, size=(rows, nb))).astype(np.uint8)
+            out[name] = (e, None, q)
+            continue
+        std_q = np.sqrt(((L + 1) ** 2 - 1) / 12.0)
         d = (sigma / std_q) * rng.uniform(0.8, 1.2, size=(rows, nb))
         m = -d * (L / 2.0) + rng.normal(0.0, 0.05 * sigma, size=(rows, nb))
         out[name] = (d.astype(np.float16), m.astype(np.float16), q)

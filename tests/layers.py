@@ -82,17 +82,32 @@ def make_layer(spec: synth.LayerSpec, seed: int = 0, source: str = "f32",
         src_arrays = (gate, up, down)
         src = M.source_f32(*src_arrays)
     else:
-        assert spec.down_bits is None, "pre-quantised sources use one width per tier"
-        assert O.MXFP4 not in spec.tier_bits, "pre-quantised sources hold affine blocks"
-        per = [synth.expert_codes(spec, bits_of[e], seed + 2, e) for e in range(spec.n_experts)]
+        per = [synth.expert_codes(spec, bits_of[e], seed + 2, e,
+                                  None if spec.down_bits is None else dbits_of[e])
+               for e in range(spec.n_experts)]
+
+        def as_oracle(mat):
+            d, m, q = mat
+            return O.MxBlocks(d, q) if m is None else mat
 
         def experts(e):
             p = per[e]
-            return O.ExpertBlocks(bits_of[e], p["gate"], p["up"], p["down"])
+            return O.ExpertBlocks(bits_of[e], *[as_oracle(p[n]) for n in ("gate", "up", "down")])
+
+        def scale_word(mat):
+            # the library's code source: fp16 bits of d, or the E8M0 byte
+            d, m, q = mat
+            return d.astype(np.uint16) if m is None else d.view(np.uint16)
+
+        def min_word(mat, shape):
+            d, m, q = mat
+            return np.zeros(shape, np.float16) if m is None else m
         names = ("gate", "up", "down")
         q = [np.ascontiguousarray(np.stack([per[e][n][2] for e in range(spec.n_experts)])) for n in names]
-        dd = [np.ascontiguousarray(np.stack([per[e][n][0] for e in range(spec.n_experts)])) for n in names]
-        mm = [np.ascontiguousarray(np.stack([per[e][n][1] for e in range(spec.n_experts)])) for n in names]
+        dd = [np.ascontiguousarray(np.stack([scale_word(per[e][n]) for e in range(spec.n_experts)]))
+              for n in names]
+        mm = [np.ascontiguousarray(np.stack([min_word(per[e][n], per[e][n][0].shape)
+                                             for e in range(spec.n_experts)])) for n in names]
         src_arrays = (q, dd, mm)
         src = M.source_codes(q, dd, mm)
 

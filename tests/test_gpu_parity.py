@@ -564,3 +564,29 @@ def test_mxfp4_tiers(tier_bits, down_bits, act):
     np.testing.assert_array_equal(ids, oids)
     ref = O.moe_layer(act_f64(x, act), tl.ol)
     check_y(y, ref["y"], act, f"prefill T=300, {tier_bits}/{down_bits} {act}")
+
+
+def test_full_size_mixed_formats():
+    # full-size layer with both format families in gate/up (tier 0 MXFP4,
+    # tiers 1-2 affine) and in down (tier 0 affine, tiers 1-2 MXFP4), so each
+    # matrix runs both prefill kernels, in the launch configuration the
+    # benchmark times
+    spec = synth.FULL.with_(tier_bits=(MX, 3, 2), down_bits=(4, MX, MX))
+    print("\n[layer] full-size mixed formats", flush=True)
+    tl = make_layer(spec, seed=8, source="codes", n_calib=4096)
+    xs1 = synth.tokens(spec, 3, 120)
+    for i in range(3):
+        x = xs1[i:i + 1]
+        y, ids, w = run_decode(tl, x, M.MOE_BF16)
+        ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+        np.testing.assert_array_equal(ids, ref["ids"])
+        check_y(y, O.output_cast(ref["y"], "bf16"), "bf16", f"decode full mixed token {i}")
+    T = 4096
+    x = synth.tokens(spec, T, 121)
+    y, ids, w, off, srt = run_prefill(tl, x, M.MOE_BF16)
+    xs = act_f64(x, "bf16")
+    keys, oids, g = O.route(xs, tl.ol.w_router, tl.ol.bias, spec.top_k)
+    np.testing.assert_array_equal(ids, oids)
+    sample = [0, 5, 1023, 2049, 4095]
+    ref = O.moe_layer(xs, tl.ol, tokens=sample, routing=(keys, oids, g))
+    check_y(y[sample], O.output_cast(ref["y"], "bf16"), "bf16", "prefill full mixed T=4096 (sampled)")
