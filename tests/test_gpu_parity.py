@@ -193,6 +193,50 @@ def test_decode_full_single_tokens(full):
         y, ids, w = run_decode(full, xs[t:t + 1])
         np.testing.assert_array_equal(ids, ref["ids"][t:t + 1])
         check_y(y, ref["y"][t:t + 1], "bf16", f"decode full T=1 token {t}")
+        # the benchmark's configuration: bf16 output
+        yb, idb, _ = run_decode(full, xs[t:t + 1], M.MOE_BF16)
+        np.testing.assert_array_equal(idb, ref["ids"][t:t + 1])
+        check_y(yb, O.output_cast(ref["y"][t:t + 1], "bf16"), "bf16", f"decode full token {t} bf16 out")
+
+
+def test_decode_graph_replays_match_eager(mid, full):
+    # the benchmark replays captured decode calls: every replay, with new
+    # inputs copied in and other eager calls in between, must give the eager
+    # results bit for bit
+    for tl in (mid, full):
+        spec, d, L = tl.spec, tl.dl.d, tl.dl.c_struct()
+        H, K = spec.hidden, spec.top_k
+        X = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
+        Y = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
+        IDS = torch.empty((1, K), dtype=torch.int32, device="cuda")
+        W = torch.empty((1, K), dtype=torch.float32, device="cuda")
+        ws = torch.empty(M.workspace_bytes("decode", d, L, 1, M.MOE_BF16), dtype=torch.uint8,
+                         device="cuda")
+        xs = synth.tokens(spec, 4, 130)
+        eager = []
+        for i in range(4):
+            X.copy_(dev(xs[i:i + 1], "bf16"))
+            M.forward_decode(d, L, X, Y, M.MOE_BF16, IDS, W, ws=ws)
+            torch.cuda.synchronize()
+            eager.append((Y.clone(), IDS.clone(), W.clone()))
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            M.forward_decode(d, L, X, Y, M.MOE_BF16, IDS, W, ws=ws)
+        torch.cuda.synchronize()
+        other = synth.tokens(spec, 3, 131)
+        for rep in range(3):
+            for i in range(4):
+                X.copy_(dev(xs[i:i + 1], "bf16"))
+                graph.replay()
+                torch.cuda.synchronize()
+                assert torch.equal(Y, eager[i][0]), (spec.hidden, rep, i)
+                assert torch.equal(IDS, eager[i][1]) and torch.equal(W, eager[i][2])
+                # eager work on the same workspace between replays
+                run_decode(tl, other[rep:rep + 1], M.MOE_BF16)
+                M.forward_decode(d, L, dev(other[rep:rep + 1], "bf16"), torch.empty_like(Y),
+                                 M.MOE_BF16, ws=ws)
+                torch.cuda.synchronize()
+        del graph
 
 
 @pytest.mark.parametrize("T", [4, 8, 16])
