@@ -642,10 +642,14 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ share
     float g[KB];
 #pragma unroll
     for (int j = 0; j < KB; j++) {
-      const int k = k0 + j < K ? k0 + j : K - 1;
+      if (k0 + j >= K) break;
+      const int k = k0 + j;
       const int pos = route_pos[(size_t)t * K + k];
       g[j] = topk_w[(size_t)t * K + k];
-      v[j] = *reinterpret_cast<const float4*>(route_rows + (size_t)pos * H + c);
+      // each route row is read exactly once: keep it out of the caches
+      typedef float f4v __attribute__((ext_vector_type(4)));
+      const f4v r = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(route_rows + (size_t)pos * H + c));
+      v[j] = make_float4(r.x, r.y, r.z, r.w);
     }
 #pragma unroll
     for (int j = 0; j < KB; j++) {
