@@ -222,17 +222,22 @@ struct SinkF32 {
   }
 };
 
-// Loads the code field of a block: `BITS` dwords (4 for MXFP4).
+// Loads the code field of a block: `BITS` dwords (4 for MXFP4).  A kernel
+// reads each weight block once, so the loads carry the non-temporal hint.
 template <int BITS>
 __device__ __forceinline__ void load_field(const uint8_t* p, uint32_t* w) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   if constexpr (BITS == 4 || BITS == kMx4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   } else if constexpr (BITS == 3) {
     const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-    w[0] = q[0]; w[1] = q[1]; w[2] = q[2];
+    w[0] = __builtin_nontemporal_load(q);
+    w[1] = __builtin_nontemporal_load(q + 1);
+    w[2] = __builtin_nontemporal_load(q + 2);
   } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
     w[0] = v.x; w[1] = v.y;
   }
 }
