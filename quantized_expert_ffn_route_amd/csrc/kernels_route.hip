@@ -455,8 +455,9 @@ __global__ __launch_bounds__(512) void k_topk_recheck(const bf16_t* __restrict__
   const double gamma = 1.1 * (double)(H + 64) * 0x1.0p-23;
   const double delta =
       gamma * sqrt(xx) * sqrt((double)wm * 1.001) + 0x1.0p-21 * ((double)am + 1.0);
-  // a value th <= the K-th largest approximate key: bisect until between K
-  // and K + 8 keys reach it (or keep the smallest key)
+  // a value th <= the K-th largest approximate key: bisect until K or K + 1
+  // keys reach it (or the interval cannot shrink; th keeps the smallest key
+  // when the bisection is skipped)
   float th = -nmn;
   if (!bad && E > K + 8) {
     float lo = -nmn, hi = amx;
@@ -467,7 +468,7 @@ __global__ __launch_bounds__(512) void k_topk_recheck(const bf16_t* __restrict__
 #pragma unroll
       for (int j = 0; j < KPL; j++) c += __popcll(__ballot(ap[j] >= mid));
       if (c < K) hi = mid;
-      else if (c > K + 8) lo = mid;
+      else if (c > K + 1) lo = mid;
       else { lo = mid; break; }
     }
     th = lo;
@@ -501,6 +502,12 @@ __global__ __launch_bounds__(512) void k_topk_recheck(const bf16_t* __restrict__
     double part[8];
 #pragma unroll
     for (int b = 0; b < 8; b += CB) {
+      // slots past the last candidate are not computed (their sums are unused)
+      if (r0 + b >= ncand) {
+#pragma unroll
+        for (int c = 0; c < CB; c++) part[b + c] = 0.0;
+        continue;
+      }
       uint4 wr[CB][MAXC];
 #pragma unroll
       for (int c = 0; c < CB; c++) {
