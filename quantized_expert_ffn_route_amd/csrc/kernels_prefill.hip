@@ -298,6 +298,8 @@ __device__ __forceinline__ void prefill_body(const PArgs& a, int grp, int row0, 
 // ---------------------------------------------------------------------------
 
 constexpr int kStages = 3;
+// Consecutive tiles (or token chunks) that one XCD takes together.
+constexpr int kXcdRun = 4;
 // Routed bf16 tiles: 96 token rows, so that one tile holds a whole expert
 // bucket at the usual prefill load (about 80 routes per expert at 4096 tokens,
 // top-10 of 512) and each weight block is dequantised once per expert.
@@ -497,8 +499,11 @@ __device__ __forceinline__ void prefill_wg(const PArgs& a) {
   const int NT = (Nr + C::NWG - 1) / C::NWG;
   // XCD-aware mapping: the workgroups that share one expert's (or one token
   // chunk's) rows land on the same XCD, whose L2 then serves the re-reads.
-  const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
-  const int grp = (j / NT) * 8 + xcd, nt = j % NT;
+  // Groups of kXcdRun consecutive tiles go to one XCD: the sort lists an
+  // expert's full tiles next to each other, so they share that XCD's L2 and
+  // its table lines are fetched once (the grid covers whole groups).
+  const int b = blockIdx.x, xcd = b & 7, j = b >> 3, g8 = j / NT;
+  const int grp = ((g8 / kXcdRun) * 8 + xcd) * kXcdRun + g8 % kXcdRun, nt = j % NT;
   if constexpr (C::ROUTED) {
     if (grp >= *a.n_tiles) return;
     const int2 tile = a.tiles[grp];
@@ -569,7 +574,7 @@ void launch_mode(const PArgs& a, int n_groups, hipStream_t s) {
   using C = MC<MODE>;
   const int Nr = C::GATEUP ? a.I : a.H;
   const int NT = (Nr + C::NWG - 1) / C::NWG;
-  dim3 grid(((n_groups + 7) / 8) * 8 * NT);
+  dim3 grid(((n_groups + 8 * kXcdRun - 1) / (8 * kXcdRun)) * 8 * kXcdRun * NT);
   constexpr int kid = MODE == kRoutedGateUp   ? MOE_K_PREFILL_GATEUP
                       : MODE == kSharedGateUp ? MOE_K_PREFILL_SHARED_GATEUP
                       : MODE == kSharedDown   ? MOE_K_PREFILL_SHARED_DOWN
