@@ -303,6 +303,31 @@ def prof_summary(out_dir, command, title):
             print(f"| `{n}` | {a[0]} | {a[1] / a[0]:.2f} | {a[2]:.2f} | {a[3]:.2f} | {a[4]} | {a[5]} "
                   f"| {a[6]} | {a[7]} |")
         print()
+        # the decode kernels by phase of the bench run: eager warm-up passes
+        # before capture, graph replays, and the traced eager pass (the last
+        # N_GRAPHS x N_LAYERS launches) whose events give the bench line's
+        # per-kernel averages
+        n_pass = N_GRAPHS * N_LAYERS
+        phase = {}
+        for r in trace:
+            n = short(r.get("Kernel_Name", ""))
+            if "moe::k_decode" in n or "moe::k_router_keys_dec" in n:
+                phase.setdefault(n, []).append((int(r["Start_Timestamp"]),
+                                                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+        if phase:
+            print("Decode kernels by phase of the run (average us): warm-up passes before graph "
+                  "capture, graph replays, and the last traced eager pass that the bench line's "
+                  "per-kernel figures time:\n")
+            print("| kernel | warm-up | replays | traced eager pass |")
+            print("|---|---|---|---|")
+            for n, v in sorted(phase.items()):
+                d = [x for _, x in sorted(v)]
+                if len(d) <= 2 * n_pass:
+                    continue
+                warm, rep, last = d[:n_pass], d[n_pass:len(d) - n_pass], d[len(d) - n_pass:]
+                print(f"| `{n}` | {sum(warm) / len(warm):.2f} | {sum(rep) / max(1, len(rep)):.2f} "
+                      f"| {sum(last) / len(last):.2f} |")
+            print()
     ctr = rows("*counter_collection.csv")
     if ctr:
         agg = {}
