@@ -234,9 +234,12 @@ int moe_build_tiers(const moe_dims* dims, const uint64_t* popularity,
  * from tier 0 to tier 2, no assignment of widths to experts does better.
  * Host only, exact integer arithmetic.
  *
- *   popularity   host [E] usage counts.   tier_bits  each in {2, 3, 4}.
+ *   popularity   host [E] usage counts.   tier_bits  each in {2, 3, 4}
+ *                (MOE_MXFP4 is rejected: its error is not a function of a
+ *                width, so the model above does not cover it).
  *   n_slots_out  host [3] (out).
- * Returns MOE_EINVAL for invalid arguments or when no plan fits the budget. */
+ * Returns MOE_EINVAL for invalid arguments or when no plan fits the budget.
+ * The plan sizes every matrix at its tier's width (no down ladder). */
 int moe_plan_tiers(const moe_dims* dims, const uint64_t* popularity,
                    const int32_t tier_bits[3], uint64_t budget_bytes,
                    int32_t n_slots_out[3]);
