@@ -634,3 +634,24 @@ def test_full_size_mixed_formats():
     sample = [0, 5, 1023, 2049, 4095]
     ref = O.moe_layer(xs, tl.ol, tokens=sample, routing=(keys, oids, g))
     check_y(y[sample], O.output_cast(ref["y"], "bf16"), "bf16", "prefill full mixed T=4096 (sampled)")
+
+
+@pytest.mark.parametrize("spec_name", ["odd", "i640"])
+def test_mxfp4_register_staged_paths(spec_name):
+    # contraction lengths that are not a power-of-two number of 128-chunks
+    # (3 chunks; down K = 640, five chunks) run the register-staged prefill
+    # body; here with MXFP4 and affine tiers mixed in both matrices
+    base = ODD if spec_name == "odd" else I640
+    spec = base.with_(tier_bits=(4, MX, 2), down_bits=(MX, 3, MX))
+    tl = make_layer(spec, seed=15)
+    for T in (1, 4):
+        x = synth.tokens(spec, T, 140 + T)
+        y, ids, w = run_decode(tl, x)
+        ref = O.moe_layer(act_f64(x, "bf16"), tl.ol, exact_keys=True)
+        np.testing.assert_array_equal(ids, ref["ids"])
+        check_y(y, ref["y"], "bf16", f"decode T={T}, {spec_name} mixed formats")
+    x = synth.tokens(spec, 200, 145)
+    y, ids, w, _, _ = run_prefill(tl, x)
+    ref = O.moe_layer(act_f64(x, "bf16"), tl.ol, exact_keys=True)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    check_y(y, ref["y"], "bf16", f"prefill T=200, {spec_name} mixed formats")
