@@ -244,6 +244,19 @@ int moe_plan_tiers(const moe_dims* dims, const uint64_t* popularity,
                    const int32_t tier_bits[3], uint64_t budget_bytes,
                    int32_t n_slots_out[3]);
 
+/* moe_plan_tiers with the down matrices on their own ladder, as the pages'
+ * re-packer plans with separate gate/up and down format lists ([P1] "step 4:
+ * three shelves, all on the GPU" and its command line).  down_bits[t] in
+ * {2, 3, 4}, or 0 for tier_bits[t]; NULL: no ladder (moe_plan_tiers).  An
+ * expert of tier t costs two matrices at tier_bits[t] and one at its down
+ * width (each H*I/32 blocks of 4*bits + 4 bytes), and its error is the sum
+ * of the three matrices' errors under the model above.  Same ranking, search,
+ * tie rule and errors as moe_plan_tiers; MOE_MXFP4 is rejected in either
+ * list. */
+int moe_plan_tiers_ladder(const moe_dims* dims, const uint64_t* popularity,
+                          const int32_t tier_bits[3], const int32_t down_bits[3],
+                          uint64_t budget_bytes, int32_t n_slots_out[3]);
+
 /* A1-A2 -- router scores, top-K and mixing weights for T tokens.
  *
  * key[t][e] = x[t] . w_router[e] + b[e] accumulated in float64 (all inputs

@@ -471,7 +471,7 @@ ERR_WEIGHT = {4: 49, 3: 225, 2: 1225}
 
 
 def plan_tiers(popularity, tier_bits: Sequence[int], hidden: int, inter: int,
-               budget_bytes: int):
+               budget_bytes: int, down_bits: Optional[Sequence[int]] = None):
     """Tier sizes (n0, n1, n2) that fit the expert tables in a byte budget.
 
     The pages' re-packer fills a memory budget with a planner that gives each
@@ -495,14 +495,24 @@ def plan_tiers(popularity, tier_bits: Sequence[int], hidden: int, inter: int,
     first at every width step, so its result is itself a band plan, and the
     exhaustive search over bands below never does worse.  Raises ValueError
     when no plan fits, or for an MXFP4 tier (outside the error model).
+
+    ``down_bits`` (0: the tier's width) gives the down matrices their own
+    ladder, as the pages' re-packer plans with separate gate/up and down
+    format lists [P1, "step 4: three shelves, all on the GPU"].  An expert of
+    tier t then costs two matrices at tier_bits[t] and one at its down width,
+    and its error is the sum over its three equally sized matrices.
     """
-    if any(b not in ERR_WEIGHT for b in tier_bits):
+    dn = [d if d else b for b, d in zip(tier_bits, down_bits or (0, 0, 0))]
+    if any(b not in ERR_WEIGHT for b in list(tier_bits) + dn):
         raise ValueError("the error model covers the 2-, 3- and 4-bit affine widths only")
     pop = [int(v) for v in np.asarray(popularity, dtype=np.uint64)]
     E = len(pop)
     order = sorted(range(E), key=lambda e: (-pop[e], e))
-    cost_b = [expert_table_bytes(hidden, inter, b) for b in tier_bits]
-    w = [ERR_WEIGHT[b] for b in tier_bits]
+    # per expert: 2/3 of a whole expert at the gate/up width plus 1/3 at the
+    # down width (each term is an integer: a matrix is a third of the tables)
+    cost_b = [2 * expert_table_bytes(hidden, inter, b) // 3 + expert_table_bytes(hidden, inter, d) // 3
+              for b, d in zip(tier_bits, dn)]
+    w = [2 * ERR_WEIGHT[b] + ERR_WEIGHT[d] for b, d in zip(tier_bits, dn)]
     best = None
     for n0 in range(E, -1, -1):
         for n1 in range(E - n0, -1, -1):

@@ -102,6 +102,9 @@ def lib():
         L.moe_plan_tiers.restype = ctypes.c_int
         L.moe_plan_tiers.argtypes = [POINTER(MoeDims), c_void_p, POINTER(c_int32), ctypes.c_uint64,
                                      POINTER(c_int32)]
+        L.moe_plan_tiers_ladder.restype = ctypes.c_int
+        L.moe_plan_tiers_ladder.argtypes = [POINTER(MoeDims), c_void_p, POINTER(c_int32),
+                                            POINTER(c_int32), ctypes.c_uint64, POINTER(c_int32)]
         L.moe_route.restype = ctypes.c_int
         L.moe_route.argtypes = [POINTER(MoeDims), POINTER(MoeLayer), c_void_p, c_int32, c_void_p,
                                 c_void_p, c_void_p, POINTER(c_size_t), c_void_p]
@@ -180,14 +183,19 @@ def build_tiers(d: MoeDims, popularity, n_slots, tier_bits, source: Optional[Moe
     return tmap, sexp
 
 
-def plan_tiers(d: MoeDims, popularity, tier_bits, budget_bytes: int):
-    """``moe_plan_tiers``: tier sizes ``(n0, n1, n2)`` for a byte budget."""
+def plan_tiers(d: MoeDims, popularity, tier_bits, budget_bytes: int, down_bits=None):
+    """``moe_plan_tiers`` (``moe_plan_tiers_ladder`` when ``down_bits`` is
+    given): tier sizes ``(n0, n1, n2)`` for a byte budget."""
     pop = np.ascontiguousarray(popularity, dtype=np.uint64)
     if pop.shape != (d.n_experts,):
         raise ValueError("popularity must hold one count per expert")
     out = (c_int32 * 3)()
-    rc = lib().moe_plan_tiers(ctypes.byref(d), pop.ctypes.data, _i32x3(tier_bits),
-                              ctypes.c_uint64(int(budget_bytes)), out)
+    if down_bits is None:
+        rc = lib().moe_plan_tiers(ctypes.byref(d), pop.ctypes.data, _i32x3(tier_bits),
+                                  ctypes.c_uint64(int(budget_bytes)), out)
+    else:
+        rc = lib().moe_plan_tiers_ladder(ctypes.byref(d), pop.ctypes.data, _i32x3(tier_bits),
+                                         _i32x3(down_bits), ctypes.c_uint64(int(budget_bytes)), out)
     _check(rc, "moe_plan_tiers")
     return tuple(int(v) for v in out)
 

@@ -263,11 +263,24 @@ size_t moe_tier_table_bytes(const moe_dims* dims, int32_t bits, int32_t n_slots,
 // best n1 is an end of its feasible interval: O(E log E) in all.
 int moe_plan_tiers(const moe_dims* dims, const uint64_t* popularity, const int32_t tier_bits[3],
                    uint64_t budget_bytes, int32_t n_slots_out[3]) {
+  return moe_plan_tiers_ladder(dims, popularity, tier_bits, nullptr, budget_bytes, n_slots_out);
+}
+
+// With a down ladder an expert of tier t stores gate and up at tier_bits[t]
+// and down at its own width: bytes and error add up over the three matrices
+// (equal sizes), so the band search is the same with per-tier totals.
+int moe_plan_tiers_ladder(const moe_dims* dims, const uint64_t* popularity,
+                          const int32_t tier_bits[3], const int32_t down_bits[3],
+                          uint64_t budget_bytes, int32_t n_slots_out[3]) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if (!popularity || !tier_bits || !n_slots_out) return MOE_EINVAL;
-  for (int t = 0; t < 3; t++)
+  int32_t dn[3];
+  for (int t = 0; t < 3; t++) {
+    dn[t] = down_bits && down_bits[t] ? down_bits[t] : tier_bits[t];
     if (tier_bits[t] != 2 && tier_bits[t] != 3 && tier_bits[t] != 4) return MOE_EINVAL;
+    if (dn[t] != 2 && dn[t] != 3 && dn[t] != 4) return MOE_EINVAL;
+  }
   const int E = dims->n_experts;
   std::vector<int32_t> order(E);
   std::iota(order.begin(), order.end(), 0);
@@ -279,11 +292,12 @@ int moe_plan_tiers(const moe_dims* dims, const uint64_t* popularity, const int32
   std::vector<u128> P(E + 1, 0);
   for (int r = 0; r < E; r++) P[r + 1] = P[r] + popularity[order[r]];
   auto werr = [](int b) -> u128 { return b == 4 ? 49 : (b == 3 ? 225 : 1225); };
-  const u128 w0 = werr(tier_bits[0]), w1 = werr(tier_bits[1]), w2 = werr(tier_bits[2]);
-  // bytes of one expert's three matrices at b bits
-  const int64_t blocks = 3 * (int64_t)dims->hidden * dims->inter / 32;
-  const int64_t c0 = blocks * (4 * tier_bits[0] + 4), c1 = blocks * (4 * tier_bits[1] + 4),
-                c2 = blocks * (4 * tier_bits[2] + 4);
+  // error weight and bytes of one expert of tier t (gate, up, down)
+  auto wt = [&](int t) { return 2 * werr(tier_bits[t]) + werr(dn[t]); };
+  const u128 w0 = wt(0), w1 = wt(1), w2 = wt(2);
+  const int64_t blocks = (int64_t)dims->hidden * dims->inter / 32;   // per matrix
+  auto ct = [&](int t) { return blocks * (2 * (4 * tier_bits[t] + 4) + (4 * dn[t] + 4)); };
+  const int64_t c0 = ct(0), c1 = ct(1), c2 = ct(2);
   const __int128 budget = (__int128)budget_bytes;
   bool found = false;
   u128 best = 0;

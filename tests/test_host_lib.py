@@ -431,3 +431,28 @@ def test_plan_tiers_rejects_bad_input():
         M.plan_tiers(d, pop, (4, 5, 2), 10**9)
     with pytest.raises(M.MoeError):
         M.plan_tiers(d, pop, (4, 3, 2), 8 * O.expert_table_bytes(256, 128, 2) - 1)
+
+
+@pytest.mark.parametrize("tier_bits,down_bits", [((4, 3, 2), (4, 4, 3)), ((3, 3, 2), (4, 2, 4)),
+                                                  ((4, 3, 2), (0, 4, 0)), ((2, 3, 4), (3, 0, 2))])
+def test_plan_tiers_ladder_matches_oracle(tier_bits, down_bits):
+    rng = np.random.default_rng(sum(tier_bits) + 10 * sum(down_bits))
+    H, I = 256, 128
+    dn = [d if d else b for b, d in zip(tier_bits, down_bits)]
+    c = [2 * O.expert_table_bytes(H, I, b) // 3 + O.expert_table_bytes(H, I, d) // 3
+         for b, d in zip(tier_bits, dn)]
+    for trial in range(25):
+        E = int(rng.integers(1, 40))
+        d = M.dims(H, I, E, 1, False, "bf16")
+        pop = (rng.zipf(1.5, size=E) if trial % 2 else rng.integers(0, 4, size=E)).astype(np.uint64)
+        budget = int(rng.integers(E * min(c) - c[0], E * max(c) + c[0]))
+        try:
+            want = O.plan_tiers(pop, tier_bits, H, I, budget, down_bits=down_bits)
+        except ValueError:
+            with pytest.raises(M.MoeError):
+                M.plan_tiers(d, pop, tier_bits, budget, down_bits=down_bits)
+            continue
+        assert M.plan_tiers(d, pop, tier_bits, budget, down_bits=down_bits) == want
+    d = M.dims(H, I, 4, 1, False, "bf16")
+    with pytest.raises(M.MoeError):
+        M.plan_tiers(d, np.ones(4, np.uint64), (4, 3, 2), 1 << 40, down_bits=(4, 0x14, 2))

@@ -513,6 +513,42 @@ def test_plan_brute_force_every_assignment(bits):
             assert _plan_cost([pop[e] for e in order], bands, bits) == best_any
 
 
+@pytest.mark.parametrize("bits,down", [((4, 3, 2), (4, 4, 3)), ((3, 3, 2), (4, 2, 4)),
+                                       ((4, 3, 2), (0, 4, 0))])
+def test_plan_ladder_brute_force_every_assignment(bits, down):
+    # with a down ladder an expert of tier t stores gate and up at bits[t] and
+    # down at its own width: costs and errors are counted per matrix here, by
+    # a search over every assignment restricted to band plans
+    import itertools
+    rng = np.random.default_rng(8)
+    H, I = 128, 256
+    dn = [d if d else b for b, d in zip(bits, down)]
+    # bytes of one matrix (H*I/32 blocks) at b bits, from the block size
+    mat = {b: H * I // 32 * (4 * b + 4) for b in (2, 3, 4)}
+    c = [2 * mat[b] + mat[d] for b, d in zip(bits, dn)]
+    for trial in range(12):
+        E = int(rng.integers(1, 7))
+        pop = rng.integers(0, 6, size=E).astype(np.uint64)
+        budget = int(rng.integers(E * min(c), E * max(c) + 1))
+        n = O.plan_tiers(pop, bits, H, I, budget, down_bits=down)
+        assert sum(n) == E and n[0] * c[0] + n[1] * c[1] + n[2] * c[2] <= budget
+        order = sorted(range(E), key=lambda e: (-int(pop[e]), e))
+        best_band = None
+        for assign in itertools.product(range(3), repeat=E):
+            ranked = [assign[e] for e in order]
+            if sum(c[t] for t in assign) > budget or any(ranked[i] > ranked[i + 1] for i in range(E - 1)):
+                continue
+            err = sum(int(pop[e]) * (2 * _werr(bits[t]) + _werr(dn[t])) for e, t in enumerate(assign))
+            key = (err, -ranked.count(0), -ranked.count(1))
+            if best_band is None or key < best_band[0]:
+                best_band = (key, (ranked.count(0), ranked.count(1), ranked.count(2)))
+        assert tuple(n) == best_band[1]
+    # without a ladder the plan is the single-width plan
+    pop = rng.integers(0, 9, size=9).astype(np.uint64)
+    budget = 9 * O.expert_table_bytes(H, I, 3)
+    assert O.plan_tiers(pop, bits, H, I, budget, down_bits=(0, 0, 0)) == O.plan_tiers(pop, bits, H, I, budget)
+
+
 def _greedy(pop, bits, H, I, budget):
     # the pages' planner: start every expert at the cheapest width, then keep
     # spending bytes on the single upgrade (one expert, next wider width) that
