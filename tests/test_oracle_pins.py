@@ -104,6 +104,91 @@ def test_quantiser_hand_blocks(case):
         np.testing.assert_array_equal(v[0], x)
 
 
+def _derivation():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "derive_quant_rounding", os.path.join(GOLDEN, "derive_quant_rounding.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+_ROUNDING = _load("quant_rounding_blocks.json")["cases"]
+
+
+def _block(case):
+    return np.asarray([float.fromhex(h) for h in case["x_hex"]], dtype=np.float32)[None, :]
+
+
+@pytest.mark.parametrize("case", _ROUNDING, ids=lambda c: c["name"])
+def test_quantiser_rounding_blocks(case):
+    # blocks where m, d or a code depends on the rounding of one step; the
+    # expected values come from exact rational arithmetic (Fraction), not from
+    # NumPy's float16/float32 conversions
+    d, m, q = O.quantise_rows(_block(case), case["bits"])
+    assert int(d.view(np.uint16)[0, 0]) == case["d_bits"]
+    assert int(m.view(np.uint16)[0, 0]) == case["m_bits"]
+    np.testing.assert_array_equal(q[0], case["q"])
+
+
+def test_rounding_blocks_follow_from_exact_arithmetic():
+    # the stored values are what the Fraction derivation gives, and each block
+    # separates the stated rounding from the wrong variant it names
+    der = _derivation()
+    fresh = der.derive()
+    assert fresh == _ROUNDING
+    for case in _ROUNDING:
+        xs = [Fraction(float.fromhex(h)) for h in case["x_hex"]]
+        wrong = (der.quantise_trunc16 if case["catches"] == "trunc16" else der.quantise_f64_steps)(
+            xs, case["bits"])
+        assert (der.f16_bits(wrong[0]), der.f16_bits(wrong[1]), wrong[2]) != (
+            case["d_bits"], case["m_bits"], case["q"])
+
+
+def test_rounding_blocks_catch_planted_oracle_mistakes(monkeypatch):
+    # plant each mistake in the oracle (CPU only) and check a block fails
+    def trunc_f16(a):
+        a = np.asarray(a, dtype=np.float64)
+        r = a.astype(np.float16)
+        # step toward zero where RNE went away from zero
+        away = np.abs(r.astype(np.float64)) > np.abs(a)
+        r = np.where(away, np.nextafter(r, np.float16(0)), r)
+        return r.astype(np.float16)
+
+    def run_all():
+        bad = 0
+        for case in _ROUNDING:
+            d, m, q = O.quantise_rows(_block(case), case["bits"])
+            got = (int(d.view(np.uint16)[0, 0]), int(m.view(np.uint16)[0, 0]), list(q[0]))
+            bad += got != (case["d_bits"], case["m_bits"], case["q"])
+        return bad
+
+    assert run_all() == 0
+    with monkeypatch.context() as mp:
+        mp.setattr(O.moe_oracle, "f16_round", trunc_f16)
+        assert run_all() >= 2
+    # fp64 intermediates: quantise with the float32 casts removed
+    src = O.moe_oracle.quantise_rows
+
+    def quantise_f64(w, bits):
+        w = np.asarray(w, dtype=np.float64)
+        L = O.LEVELS[bits]
+        blk = w.reshape(w.shape[0], -1, 32)
+        lo, hi = blk.min(-1), blk.max(-1)
+        m16 = (lo).astype(np.float16)
+        d16 = ((hi - lo) / L).astype(np.float16)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = np.clip(np.rint((blk - m16.astype(np.float64)[..., None]) /
+                                d16.astype(np.float64)[..., None]), 0, L)
+        q = np.where(d16[..., None] == 0, 0, q).astype(np.uint8)
+        return d16, m16, q.reshape(w.shape)
+
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "quantise_rows", quantise_f64)
+        assert run_all() >= 2
+    assert O.moe_oracle.quantise_rows is src
+
+
 @pytest.mark.parametrize("bits", [4, 3, 2])
 def test_quantiser_reconstruction_bound(bits):
     rng = np.random.default_rng(bits)
