@@ -297,7 +297,10 @@ int moe_forward_decode(const moe_dims* dims, const moe_layer* layer, const void*
 
 /* A1-A2, A4, A7-A8 -- the layer for many tokens (prefill).
  *
- * Same function as moe_forward_decode.  Routes r = t*K + k are grouped by
+ * Same function as moe_forward_decode.  T * H and T * K * I must each stay
+ * below 2^31 (the routed GEMMs gather token rows with 32-bit element
+ * offsets): MOE_EUNSUPPORTED otherwise, before any launch or workspace
+ * query.  Routes r = t*K + k are grouped by
  * expert with a stable counting sort (expert_offsets[E+1] exclusive prefix
  * of per-expert counts; sorted_routes[T*K] the routes of expert e at
  * offsets[e]..offsets[e+1] in ascending r), the grouping the batched path

@@ -618,6 +618,11 @@ int moe_forward_prefill(const moe_dims* dims, const moe_layer* layer, const void
   if ((rc = check_layer(dims, layer))) return rc;
   if (dims->n_experts > 4096) return MOE_EUNSUPPORTED;
   if (T < 0 || (int64_t)T * dims->top_k > INT32_MAX) return MOE_EINVAL;
+  // the routed GEMMs gather token rows (x, and h per route) with 32-bit
+  // element offsets
+  if ((int64_t)T * dims->hidden > INT32_MAX ||
+      (int64_t)T * dims->top_k * dims->inter > INT32_MAX)
+    return MOE_EUNSUPPORTED;
   if (y_dt != MOE_F32 && y_dt != dims->act) return MOE_EINVAL;
   const PrefillWs w = prefill_ws(dims, T);
   bool size_only;

@@ -150,6 +150,27 @@ def test_forward_argument_checks_without_gpu():
                                    None, None, None, None, None, ctypes.byref(s1), None) == M.MOE_EUNSUPPORTED
 
 
+def test_prefill_rejects_gathers_beyond_32_bit_offsets():
+    # the routed GEMMs gather x rows (T * H elements) and h rows (T * K * I
+    # elements) with 32-bit element offsets: at or above 2^31 the call is
+    # refused before any launch, also for a workspace-size query
+    lib = M.lib()
+    n = ctypes.c_size_t(0)
+
+    def query(d, T):
+        L = _fake_layer(d, (d.n_experts, 0, 0))
+        return lib.moe_forward_prefill(ctypes.byref(d), ctypes.byref(L), None, T, None, M.MOE_F32,
+                                       None, None, None, None, None, ctypes.byref(n), None)
+    full = M.dims(2048, 512, 512, 10, True, "bf16")
+    # T * K * I: 419430 * 10 * 512 = 2147481600 < 2^31 <= 419431 * 5120
+    assert query(full, 419430) == M.MOE_OK
+    assert query(full, 419431) == M.MOE_EUNSUPPORTED
+    # T * H: with K = 1 and a narrow I, the x gather is the binding limit
+    wide = M.dims(8192, 128, 64, 1, False, "bf16")
+    assert query(wide, (1 << 31) // 8192 - 1) == M.MOE_OK
+    assert query(wide, (1 << 31) // 8192) == M.MOE_EUNSUPPORTED
+
+
 # ------------------------------------------------------------ host tier build
 
 def _mbits(tier_bits, down_bits, t, m):
@@ -238,6 +259,29 @@ def test_build_tiers_f32_bit_exact_vs_oracle(tier_bits, down_bits):
     for (t, m), (wc, wd) in want.items():
         np.testing.assert_array_equal(codes[t][m], wc, err_msg=f"codes tier {t} mat {m}")
         np.testing.assert_array_equal(dm[t][m], wd, err_msg=f"dm tier {t} mat {m}")
+
+
+def test_build_tiers_rounding_blocks_match_exact_derivation():
+    # the library's quantiser on the golden blocks whose d, m or codes depend
+    # on the rounding of one step (exact Fraction derivation): block (row 0,
+    # block 0) of the gate matrix of a one-expert layer sits at table index 0
+    import json
+    from conftest import GOLDEN
+    with open(os.path.join(GOLDEN, "quant_rounding_blocks.json")) as fh:
+        cases = json.load(fh)["cases"]
+    H = I = 128
+    d = M.dims(H, I, 1, 1, False, "f32")
+    for case in cases:
+        b = case["bits"]
+        rng = np.random.default_rng(40)
+        mats = [rng.standard_normal((1,) + shape).astype(np.float32) for shape in ((I, H), (I, H), (H, I))]
+        mats[0][0, 0, :32] = [float.fromhex(h) for h in case["x_hex"]]
+        L, codes, dm = _host_tables(d, (1, 0, 0), (b, b, b))
+        M.build_tiers(d, np.ones(1, np.uint64), (1, 0, 0), (b, b, b), M.source_f32(*mats), L,
+                      dst_on_device=False)
+        assert int(dm[0][0][0]) == case["d_bits"] | (case["m_bits"] << 16), case["name"]
+        np.testing.assert_array_equal(O.decode_codes(codes[0][0][:4 * b], b), case["q"],
+                                      err_msg=case["name"])
 
 
 def test_build_tiers_codes_source_bit_exact_vs_oracle():
