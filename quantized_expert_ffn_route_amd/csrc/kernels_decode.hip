@@ -349,7 +349,8 @@ __device__ __forceinline__ void topk_block(const double* __restrict__ keys, int 
   float mx = ok && !bad ? kf : -INFINITY, mn = ok && !bad ? kf : INFINITY;
   wave_maxmin_f32(mx, mn);
   const bool wbad = __ballot(bad) != 0;
-  if (t < 256) S.hist[t] = 0u;
+  // every bin is cleared, whatever the workgroup size (128 to 512 threads)
+  for (int i = t; i < 256; i += blockDim.x) S.hist[i] = 0u;
   if (ok) s_tm[t] = tm;
   if (lane == 0) {
     S.mx[wave] = mx;
@@ -403,6 +404,9 @@ __device__ __forceinline__ void topk_block(const double* __restrict__ keys, int 
       S.cand[pos].id = (uint32_t)t;
     }
     __syncthreads();
+    // fewer than K candidates cannot happen with a consistent histogram; if
+    // it ever did, the wave-level selection below still gives the exact ids
+    if (S.cnt < K) mode = 2;
   }
   if (wave != 0) return;
   if (mode == 2) {
