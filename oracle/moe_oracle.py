@@ -739,7 +739,7 @@ def expert_ffn(x, gate_w, up_w, down_w, act: str):
 
 
 def moe_layer(x, layer: OracleLayer, tokens: Optional[Sequence[int]] = None,
-              routing=None, exact_keys: bool = False):
+              routing=None, exact_keys: bool = False, drop_experts: bool = False):
     """Output of the layer for the rows ``tokens`` of ``x`` (all rows if None).
 
     Each token runs through its K chosen experts plus the one shared expert
@@ -749,8 +749,10 @@ def moe_layer(x, layer: OracleLayer, tokens: Optional[Sequence[int]] = None,
         y[t] = sum_k g[t,k] * out_{ids[t,k]}(x[t]) + out_shared(x[t])
 
     in float64.  ``routing`` may pass precomputed ``(keys, ids, g)`` for all
-    rows of ``x``.  Returns a dict with keys, ids, g (for all rows) and ``y``
-    (float64, one row per requested token).
+    rows of ``x``.  ``drop_experts`` forgets each expert's dequantised weights
+    once its bucket is done (memory only; the arithmetic is the same).
+    Returns a dict with keys, ids, g (for all rows) and ``y`` (float64, one
+    row per requested token).
     """
     x = np.asarray(x, dtype=np.float64)
     if routing is None:
@@ -770,6 +772,8 @@ def moe_layer(x, layer: OracleLayer, tokens: Optional[Sequence[int]] = None,
         _, out = expert_ffn(x[[t for _, t, _ in lst]], gw, uw, dw, layer.act)
         for j, (i, t, k) in enumerate(lst):
             y[i] += g[t, k] * out[j]
+        if drop_experts:
+            layer._cache.pop(e, None)
     if layer.shared is not None:
         _, out_s = expert_ffn(x[rows], *layer.shared, act=layer.act)
         y += out_s

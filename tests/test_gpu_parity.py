@@ -347,7 +347,11 @@ def test_odd_shapes_decode_and_prefill(odd, T):
     check_y(yp, ref["y"], "bf16", f"prefill odd T={T}")
 
 
-def test_prefill_full_4096_sampled(full):
+def test_prefill_full_4096_every_row(full):
+    # every one of the 4096 x 2048 outputs against the oracle, which runs
+    # expert by expert (each expert's dequantised weights dropped after its
+    # bucket); then a second call on the same inputs must repeat the first
+    # bit for bit (no atomics anywhere in the prefill path)
     T = 4096
     x = synth.tokens(full.spec, T, 21)
     y, ids, w, off, srt = run_prefill(full, x, M.MOE_BF16)
@@ -358,9 +362,14 @@ def test_prefill_full_4096_sampled(full):
     o_off, o_srt = O.sort_routes(ids, full.spec.n_experts)
     np.testing.assert_array_equal(off, o_off)
     np.testing.assert_array_equal(srt, o_srt)
-    sample = [0, 1, 777, 2048, 3000, 4095]
-    ref = O.moe_layer(xs, full.ol, tokens=sample, routing=(keys, oids, g))
-    check_y(y[sample], O.output_cast(ref["y"], "bf16"), "bf16", "prefill full T=4096 (sampled rows)")
+    y2, ids2, w2, off2, srt2 = run_prefill(full, x, M.MOE_BF16)
+    assert torch.equal(y, y2)
+    np.testing.assert_array_equal(ids, ids2)
+    np.testing.assert_array_equal(w.view(np.uint32), w2.view(np.uint32))
+    np.testing.assert_array_equal(srt, srt2)
+    print("  oracle over all 4096 rows ...", flush=True)
+    ref = O.moe_layer(xs, full.ol, routing=(keys, oids, g), drop_experts=True)
+    check_y(y, O.output_cast(ref["y"], "bf16"), "bf16", "prefill full T=4096 (every row)")
 
 
 def test_prefill_router_ties_take_lower_id():
@@ -631,9 +640,9 @@ def test_full_size_mixed_formats():
     xs = act_f64(x, "bf16")
     keys, oids, g = O.route(xs, tl.ol.w_router, tl.ol.bias, spec.top_k)
     np.testing.assert_array_equal(ids, oids)
-    sample = [0, 5, 1023, 2049, 4095]
-    ref = O.moe_layer(xs, tl.ol, tokens=sample, routing=(keys, oids, g))
-    check_y(y[sample], O.output_cast(ref["y"], "bf16"), "bf16", "prefill full mixed T=4096 (sampled)")
+    print("  oracle over all 4096 rows ...", flush=True)
+    ref = O.moe_layer(xs, tl.ol, routing=(keys, oids, g), drop_experts=True)
+    check_y(y, O.output_cast(ref["y"], "bf16"), "bf16", "prefill full mixed T=4096 (every row)")
 
 
 @pytest.mark.parametrize("spec_name", ["odd", "i640"])
@@ -655,3 +664,92 @@ def test_mxfp4_register_staged_paths(spec_name):
     ref = O.moe_layer(act_f64(x, "bf16"), tl.ol, exact_keys=True)
     np.testing.assert_array_equal(ids, ref["ids"])
     check_y(y, ref["y"], "bf16", f"prefill T=200, {spec_name} mixed formats")
+
+
+def test_decode_wide_default_router_128_threads():
+    # hidden 256: the one-token gate/up workgroups have 128 threads, each
+    # holding one of the 128 keys; the whole 256-bin histogram must start
+    # cleared.  T = 17 ends with a one-token group after a full group of 16.
+    tl = make_layer(WIDE, seed=18)
+    for T in (1, 17):
+        for seed in (150, 151, 152):
+            x = synth.tokens(WIDE, T, seed + T)
+            y, ids, w = run_decode(tl, x)
+            _, oids, g = O.route(act_f64(x, "bf16"), tl.ol.w_router, tl.ol.bias, WIDE.top_k,
+                                 exact=True)
+            np.testing.assert_array_equal(ids, oids)
+            assert np.max(np.abs(w - g)) <= 1e-6
+            ref = O.moe_layer(act_f64(x, "bf16"), tl.ol, exact_keys=True)
+            check_y(y, ref["y"], "bf16", f"decode T={T} seed {seed}, H=256 E=128")
+
+
+# top-1 (every mixing weight exactly 1) and top-E (every expert chosen)
+K1 = synth.LayerSpec(hidden=256, inter=128, n_experts=16, top_k=1, has_shared=True, act="bf16",
+                     n_slots=(4, 8, 4))
+KE = synth.LayerSpec(hidden=256, inter=128, n_experts=8, top_k=8, has_shared=False, act="bf16",
+                     n_slots=(2, 4, 2))
+
+
+@pytest.mark.parametrize("spec_name", ["k1", "ke"])
+def test_top_one_and_top_all(spec_name):
+    spec = K1 if spec_name == "k1" else KE
+    tl = make_layer(spec, seed=19)
+    xs = act_f64
+    for T in (1, 5):
+        x = synth.tokens(spec, T, 160 + T)
+        y, ids, w = run_decode(tl, x)
+        ref = O.moe_layer(xs(x, "bf16"), tl.ol, exact_keys=True)
+        np.testing.assert_array_equal(ids, ref["ids"])
+        check_y(y, ref["y"], "bf16", f"decode T={T}, {spec_name}")
+        if spec.top_k == 1:
+            assert np.all(w == np.float32(1.0))
+        else:
+            assert np.all(np.sort(ids, axis=1) == np.arange(spec.n_experts))
+            assert np.max(np.abs(w.sum(axis=1) - 1.0)) <= 1e-6
+    x = synth.tokens(spec, 100, 170)
+    y, ids, w, off, srt = run_prefill(tl, x)
+    ref = O.moe_layer(xs(x, "bf16"), tl.ol, exact_keys=True)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    o_off, o_srt = O.sort_routes(ids, spec.n_experts)
+    np.testing.assert_array_equal(off, o_off)
+    np.testing.assert_array_equal(srt, o_srt)
+    check_y(y, ref["y"], "bf16", f"prefill T=100, {spec_name}")
+    if spec.top_k == 1:
+        assert np.all(w == np.float32(1.0))
+    else:
+        assert np.all(np.diff(off) == 100)
+
+
+def test_planned_tiers_through_decode_and_prefill():
+    # the byte-budget planner's split drives the forward path: plan with a
+    # down ladder for a budget that leaves the 2-bit tier empty and the other
+    # two uneven, check the oracle's planner agrees, then build the tables at
+    # that split and run decode and prefill against the oracle
+    import layers
+    spec = MID.with_(down_bits=(4, 4, 3))
+    w_router, bias = synth.router(spec, 21)
+    pop = layers.popularity_from_calibration(spec, w_router, bias, 22)
+    per = {b: O.expert_table_bytes(spec.hidden, spec.inter, b) for b in (4, 3, 2)}
+    # room for 28 experts at 4 bits and 4 at 3 bits (down at 4 bits): the
+    # least-error plan spends it exactly so, with no 2-bit expert
+    budget = 28 * per[4] + 4 * (2 * per[3] // 3 + per[4] // 3)
+    d = M.dims(spec.hidden, spec.inter, spec.n_experts, spec.top_k, spec.has_shared, spec.act)
+    plan = M.plan_tiers(d, pop, spec.tier_bits, budget, down_bits=spec.down_bits)
+    want = O.plan_tiers(pop, spec.tier_bits, spec.hidden, spec.inter, budget, spec.down_bits)
+    assert tuple(plan) == tuple(want)
+    print(f"  planned split {tuple(plan)} for {budget} bytes", flush=True)
+    assert plan[2] == 0 and plan[0] != plan[1] and sum(plan) == spec.n_experts
+    tl = make_layer(spec.with_(n_slots=tuple(int(v) for v in plan)), seed=21)
+    want_map, _ = O.build_tiers(tl.popularity, tuple(int(v) for v in plan))
+    np.testing.assert_array_equal(tl.tier_map, want_map)
+    for T in (1, 5):
+        x = synth.tokens(spec, T, 180 + T)
+        y, ids, w = run_decode(tl, x)
+        ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+        np.testing.assert_array_equal(ids, ref["ids"])
+        check_y(y, ref["y"], "bf16", f"decode T={T}, planned split {tuple(plan)}")
+    x = synth.tokens(spec, 300, 186)
+    y, ids, w, _, _ = run_prefill(tl, x)
+    ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    check_y(y, ref["y"], "bf16", f"prefill T=300, planned split {tuple(plan)}")
