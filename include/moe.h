@@ -295,6 +295,26 @@ int moe_forward_decode(const moe_dims* dims, const moe_layer* layer, const void*
                        int32_t T, void* y, int32_t y_dt, int32_t* topk_ids,
                        float* topk_w, void* ws, size_t* ws_bytes, hipStream_t stream);
 
+/* moe_forward_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, result and launches as
+ * moe_forward_decode, which it shares its kernels with; the workspace is a
+ * library-owned device array of MOE_NOALLOC_SCRATCH_BYTES bytes per GPU,
+ * created with the library's code object on each GPU it runs on and held
+ * until the process ends.  The call itself allocates nothing.
+ *
+ * Returns MOE_ENOSPC (nothing launched) when the layer's decode workspace
+ * (moe_forward_decode with ws == NULL reports its size) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES; about 0.27 MB for the full-size layer of 512
+ * experts, top-10, intermediate 512.  Every call on one GPU uses the same
+ * array and leaves its contents behind (no call needs them cleared): calls
+ * that may overlap on one GPU -- concurrent streams, or host threads -- race
+ * and must be ordered by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+int moe_forward_decode_noalloc(const moe_dims* dims, const moe_layer* layer, const void* x,
+                               int32_t T, void* y, int32_t y_dt, int32_t* topk_ids,
+                               float* topk_w, hipStream_t stream);
+
 /* A1-A2, A4, A7-A8 -- the layer for many tokens (prefill).
  *
  * Same function as moe_forward_decode.  T * H and T * K * I must each stay

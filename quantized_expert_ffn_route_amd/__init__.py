@@ -25,7 +25,8 @@ __all__ = [
     "MOE_SRC_F32", "MOE_SRC_CODES", "MOE_MXFP4",
     "MoeError", "MoeLibraryMissing", "MoeDims", "MoeLayer", "MoeExpertSource",
     "lib", "library_path", "status_string", "dims", "tier_table_bytes",
-    "build_tiers", "plan_tiers", "route", "forward_decode", "forward_prefill", "workspace_bytes",
+    "build_tiers", "plan_tiers", "route", "forward_decode", "forward_decode_noalloc",
+    "forward_prefill", "workspace_bytes",
     "DeviceLayer", "Trace", "KERNEL_NAMES",
 ]
 
@@ -112,6 +113,10 @@ def lib():
         L.moe_forward_decode.argtypes = [POINTER(MoeDims), POINTER(MoeLayer), c_void_p, c_int32,
                                          c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                                          POINTER(c_size_t), c_void_p]
+        L.moe_forward_decode_noalloc.restype = ctypes.c_int
+        L.moe_forward_decode_noalloc.argtypes = [POINTER(MoeDims), POINTER(MoeLayer), c_void_p,
+                                                 c_int32, c_void_p, c_int32, c_void_p, c_void_p,
+                                                 c_void_p]
         L.moe_set_trace.restype = ctypes.c_int
         L.moe_set_trace.argtypes = [c_void_p, c_void_p, c_int32, c_void_p]
         L.moe_forward_prefill.restype = ctypes.c_int
@@ -248,6 +253,16 @@ def forward_decode(d: MoeDims, layer: MoeLayer, x, y, y_dt: int, topk_ids=None, 
                                   _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ctypes.byref(n),
                                   _stream(stream))
     _check(rc, "moe_forward_decode")
+
+
+def forward_decode_noalloc(d: MoeDims, layer: MoeLayer, x, y, y_dt: int, topk_ids=None,
+                           topk_w=None, stream=None) -> None:
+    """``moe_forward_decode_noalloc`` on torch tensors (no workspace: the
+    library's own device scratch)."""
+    rc = lib().moe_forward_decode_noalloc(ctypes.byref(d), ctypes.byref(layer), _ptr(x),
+                                          int(x.shape[0]), _ptr(y), y_dt, _ptr(topk_ids),
+                                          _ptr(topk_w), _stream(stream))
+    _check(rc, "moe_forward_decode_noalloc")
 
 
 def forward_prefill(d: MoeDims, layer: MoeLayer, x, y, y_dt: int, topk_ids=None, topk_w=None,

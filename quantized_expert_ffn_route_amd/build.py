@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 
 ARCH = "gfx950"
 DEVICE_SOURCES = ["kernels_route.hip", "kernels_decode.hip", "kernels_prefill.hip",
-                  "kernels_dense.hip"]
+                  "kernels_dense.hip", "scratch.hip"]
 HOST_SOURCES = ["moe_abi.cpp", "pack.cpp"]
 
 

@@ -46,6 +46,15 @@ struct Tables {
   const void* dense[3];    // shared expert gate / up / down (act dtype)
 };
 
+// Bytes of the library-owned device scratch of moe_forward_decode_noalloc
+// (one array per GPU, held until the process ends).
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+
+// Device address of that scratch on the current device (scratch.hip): the
+// symbol's address is looked up once per device and kept.  MOE_OK or
+// MOE_EHIP / MOE_EUNSUPPORTED.
+int scratch_for_current_device(void** out);
+
 // ---- launch trace (moe_set_trace); defined in moe_abi.cpp ----
 // Returns the start/stop events of the next trace slot for a kernel launched
 // on `s`, or leaves them null (no trace installed, slots used up, or `s` is

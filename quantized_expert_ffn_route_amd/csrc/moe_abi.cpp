@@ -556,21 +556,67 @@ int moe_route(const moe_dims* dims, const moe_layer* layer, const void* x, int32
 // Decode: groups of up to 16 tokens, four launches per group.
 // ---------------------------------------------------------------------------
 
-int moe_forward_decode(const moe_dims* dims, const moe_layer* layer, const void* x, int32_t T,
-                       void* y, int32_t y_dt, int32_t* topk_ids, float* topk_w, void* ws,
-                       size_t* ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode launch sequence on a checked workspace `base` of the decode
+// layout (arguments already validated).
+int decode_launches(const moe_dims* dims, const moe_layer* layer, const void* x, int32_t T,
+                    void* y, int32_t y_dt, int32_t* topk_ids, float* topk_w, char* base,
+                    const DecodeWs& w, hipStream_t stream);
+
+int check_decode_args(const moe_dims* dims, const moe_layer* layer, int32_t T, int32_t y_dt) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if ((rc = check_layer(dims, layer))) return rc;
   if (T < 0 || (int64_t)T * dims->top_k > INT32_MAX) return MOE_EINVAL;
   if (y_dt != MOE_F32 && y_dt != dims->act) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_decode(const moe_dims* dims, const moe_layer* layer, const void* x, int32_t T,
+                       void* y, int32_t y_dt, int32_t* topk_ids, float* topk_w, void* ws,
+                       size_t* ws_bytes, hipStream_t stream) {
+  int rc = check_decode_args(dims, layer, T, y_dt);
+  if (rc) return rc;
   const DecodeWs w = decode_ws(dims);
   bool size_only;
   if ((rc = check_ws(ws, ws_bytes, w.total, &size_only)) || size_only) return rc;
   if (T == 0) return MOE_OK;
   if (!x || !aligned(x, 16) || !y || !aligned(y, 16)) return MOE_EINVAL;
+  return decode_launches(dims, layer, x, T, y, y_dt, topk_ids, topk_w, static_cast<char*>(ws), w,
+                         stream);
+}
+
+int moe_forward_decode_noalloc(const moe_dims* dims, const moe_layer* layer, const void* x,
+                               int32_t T, void* y, int32_t y_dt, int32_t* topk_ids,
+                               float* topk_w, hipStream_t stream) {
+  int rc = check_decode_args(dims, layer, T, y_dt);
+  if (rc) return rc;
+  const DecodeWs w = decode_ws(dims);
+  static_assert(kScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "scratch size");
+  if (w.total > kScratchBytes) return MOE_ENOSPC;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16) || !y || !aligned(y, 16)) return MOE_EINVAL;
+  void* scratch = nullptr;
+  if ((rc = scratch_for_current_device(&scratch))) return rc;
+  return decode_launches(dims, layer, x, T, y, y_dt, topk_ids, topk_w,
+                         static_cast<char*>(scratch), w, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_launches(const moe_dims* dims, const moe_layer* layer, const void* x, int32_t T,
+                    void* y, int32_t y_dt, int32_t* topk_ids, float* topk_w, char* base,
+                    const DecodeWs& w, hipStream_t stream) {
   clear_hip_error();
-  char* base = static_cast<char*>(ws);
   const int H = dims->hidden, K = dims->top_k, E = dims->n_experts;
   const Tables tb = make_tables(dims, layer);
   const size_t xb = act_bytes(dims->act), yb = y_dt == MOE_BF16 ? 2 : 4;
@@ -604,6 +650,10 @@ int moe_forward_decode(const moe_dims* dims, const moe_layer* layer, const void*
   }
   return hip_status();
 }
+
+}  // namespace
+
+extern "C" {
 
 // ---------------------------------------------------------------------------
 // Prefill: route, counting sort, grouped GEMMs, weighted scatter-combine.

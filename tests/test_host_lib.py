@@ -500,3 +500,31 @@ def test_plan_tiers_ladder_matches_oracle(tier_bits, down_bits):
     d = M.dims(H, I, 4, 1, False, "bf16")
     with pytest.raises(M.MoeError):
         M.plan_tiers(d, np.ones(4, np.uint64), (4, 3, 2), 1 << 40, down_bits=(4, 0x14, 2))
+
+
+def test_decode_noalloc_refuses_workspaces_beyond_its_scratch():
+    # a decode workspace larger than the library's scratch is refused before
+    # any HIP call (MOE_ENOSPC); the header states the scratch size
+    lib = M.lib()
+    with open(os.path.join(ROOT, "include", "moe.h")) as fh:
+        m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", fh.read())
+    limit = int(m.group(1)) << int(m.group(2))
+    n = ctypes.c_size_t(0)
+    d = M.dims(256, 128, 40000, 4, False, "bf16")
+    L = _fake_layer(d, (40000, 0, 0))
+    assert lib.moe_forward_decode(ctypes.byref(d), ctypes.byref(L), None, 1, None, M.MOE_F32, None,
+                                  None, None, ctypes.byref(n), None) == M.MOE_OK
+    assert n.value > limit
+    fake = 1 << 22
+    assert lib.moe_forward_decode_noalloc(ctypes.byref(d), ctypes.byref(L), fake, 1, fake,
+                                          M.MOE_F32, None, None, None) == M.MOE_ENOSPC
+    # invalid arguments are refused the same way as by moe_forward_decode
+    bad = M.dims(256, 128, 64, 65, False, "f32")
+    assert lib.moe_forward_decode_noalloc(ctypes.byref(bad), ctypes.byref(L), fake, 1, fake,
+                                          M.MOE_F32, None, None, None) == M.MOE_EINVAL
+    # the full-size layer fits
+    full = M.dims(2048, 512, 512, 10, True, "bf16")
+    Lf = _fake_layer(full, (128, 256, 128))
+    assert lib.moe_forward_decode(ctypes.byref(full), ctypes.byref(Lf), None, 1, None, M.MOE_BF16,
+                                  None, None, None, ctypes.byref(n), None) == M.MOE_OK
+    assert n.value <= limit
