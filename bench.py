@@ -65,6 +65,12 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=8)
     ap.add_argument("--prefill-tokens", type=int, default=4096)
     ap.add_argument("--cpu-tokens", type=int, default=320)
+    ap.add_argument("--cpu-tokens-1t", type=int, default=96,
+                    help="tokens of the one-thread oracle figure (0: skip)")
+    ap.add_argument("--no-verify", action="store_true",
+                    help="skip the verify-batch leg (T = 4, 8, 16 correlated tokens)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-ceiling leg (torch GEMV over 48 x 25.8 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
@@ -222,7 +228,21 @@ def decode_kernel_bytes(spec, layer, ids_row):
 # CPU baseline: the oracle on a bounded sample
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(n_tokens, seed):
+def cpu_model():
+    """Model name of the host CPU (first entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(n_tokens, seed, n_tokens_1t=0):
+    """The oracle on batch-1 decode tokens through one full-size layer, with
+    BLAS on every host thread, and (n_tokens_1t > 0) again on one thread."""
     import oracle as O
     import synth
     from threadpoolctl import threadpool_limits
@@ -252,10 +272,24 @@ def cpu_baseline(n_tokens, seed):
         for t in range(n_tokens):       # batch-1 decode: one token per call
             O.moe_layer(x[t:t + 1], layer)
         dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "MoE-layer tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_tokens} batch-1 decode tokens through one full-size layer (host-generated "
-                      f"seeded blocks of the same shapes and tiers); NumPy fp64, BLAS on {cores} "
-                      f"threads, element-wise dequantisation single-threaded; {dt:.1f} s"}
+    out = {"value": n_tokens / dt, "unit": "MoE-layer tokens/s", "cores": cores, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"{n_tokens} batch-1 decode tokens through one full-size layer (host-generated "
+                     f"seeded blocks of the same shapes and tiers); NumPy fp64, BLAS on {cores} "
+                     f"threads, element-wise dequantisation single-threaded; {dt:.1f} s"}
+    if n_tokens_1t > 0:
+        # the same tokens again on one thread; the touched experts' dequantised
+        # weights are dropped first so that the rate includes them, as above
+        layer._cache.clear()
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            for t in range(n_tokens_1t):
+                O.moe_layer(x[t:t + 1], layer)
+            dt1 = time.perf_counter() - t0
+        out["one_thread"] = {"value": n_tokens_1t / dt1, "cores": 1,
+                             "sample": f"the first {n_tokens_1t} of the same tokens, BLAS on one "
+                                       f"thread; {dt1:.1f} s"}
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -365,10 +399,125 @@ def prof_summary(out_dir, command, title):
         print()
 
 
+# the kernel that runs gate/up in batch-1 decode (the dominant decode kernel)
+DECODE_GATEUP_KERNEL = "k_decode1_gateup"
+
+
+def verify_batches(M, torch, spec, d, layers, args, sizes=(4, 8, 16), n_graphs=4):
+    """Small-batch verify decode: T correlated tokens (x_t = sqrt(0.6) z_0 +
+    sqrt(0.4) z_t, mean pairwise cosine ~0.6, so their experts overlap)
+    through the 48-layer stack, one HIP graph per batch of 48 layer calls,
+    n_graphs batches replayed round-robin.  Reports MoE-layer tokens/s, the
+    mean union of experts per layer call, the union's algorithmic bytes and
+    their HBM fraction."""
+    H = spec.hidden
+    out = {}
+    gen = torch.Generator(device="cuda")
+    for T in sizes:
+        gen.manual_seed(args.seed + 100 + T)
+        z0 = torch.randn((n_graphs, N_LAYERS, 1, H), generator=gen, device="cuda")
+        zt = torch.randn((n_graphs, N_LAYERS, T, H), generator=gen, device="cuda")
+        X = (np.sqrt(0.6) * z0 + np.sqrt(0.4) * zt).to(torch.bfloat16)
+        Y = torch.empty((N_LAYERS, T, H), dtype=torch.bfloat16, device="cuda")
+        IDS = torch.empty((n_graphs, N_LAYERS, T, spec.top_k), dtype=torch.int32, device="cuda")
+        WTS = torch.empty((n_graphs, N_LAYERS, T, spec.top_k), dtype=torch.float32, device="cuda")
+        ws = torch.empty(M.workspace_bytes("decode", d, layers[0].cs, T, M.MOE_BF16),
+                         dtype=torch.uint8, device="cuda")
+
+        def batch_pass(g):
+            for l in range(N_LAYERS):
+                M.forward_decode(d, layers[l].cs, X[g, l], Y[l], M.MOE_BF16, IDS[g, l], WTS[g, l],
+                                 ws=ws)
+
+        graphs = []
+        for g in range(n_graphs):
+            batch_pass(g)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                batch_pass(g)
+            graphs.append(graph)
+        for k in range(args.warmup):
+            graphs[k % n_graphs].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            graphs[k % n_graphs].replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ids = IDS.cpu().numpy()
+        unions, nbytes = [], []
+        for g in range(n_graphs):
+            for l in range(N_LAYERS):
+                u = np.unique(ids[g, l])
+                unions.append(len(u))
+                tiers = [int(layers[l].tmap_host[e]) >> 16 for e in u]
+                routed = sum(table_bytes(spec, spec.tier_bits[t], 0) + table_bytes(spec, spec.tier_bits[t], 1)
+                             + table_bytes(spec, down_format(spec, t), 2) for t in tiers)
+                nbytes.append(routed + 3 * spec.inter * H * 2 + spec.n_experts * (H * 2 + 4)
+                              + 2 * T * H * 2)
+        us_layer = 1e6 * wall / (args.steps * N_LAYERS)
+        mean_bytes = float(np.mean(nbytes))
+        gbs = mean_bytes / (us_layer * 1e-6) / 1e9
+        out[f"T{T}"] = {"tokens_per_s": round(T * N_LAYERS * args.steps / wall, 1),
+                        "us_per_layer": round(us_layer, 3),
+                        "mean_union": round(float(np.mean(unions)), 2),
+                        "bytes_per_layer": int(mean_bytes),
+                        "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"verify T={T}: {out[f'T{T}']}")
+        del graphs, X, zt, z0
+    return {"workload": "verify decode: T correlated tokens (cosine ~0.6) per layer call through "
+                        "the 48-layer stack, one graph per batch of 48 layer calls",
+            "unit": "MoE-layer tokens/s", **out}
+
+
+def streaming_ceiling(torch, layer_bytes, args):
+    """Measured ceiling for one layer's bytes: torch's own bf16 GEMV (one
+    launch streaming a [rows x 2048] matrix of the layer's size) over 48
+    distinct matrices (1.24 GB, so reads come from HBM), captured in one HIP
+    graph per step like the decode step and replayed the same number of
+    times.  It reads the same number of bytes per layer as the MoE layer's
+    kernels but has no data-dependent step in between."""
+    H = 2048
+    rows = -(-layer_bytes // (2 * H))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(args.seed + 11)
+    mats = [torch.randn((rows, H), generator=gen, device="cuda").to(torch.bfloat16)
+            for _ in range(N_LAYERS)]
+    vec = torch.randn(H, generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.empty((N_LAYERS, rows), dtype=torch.bfloat16, device="cuda")
+
+    def one_pass():
+        for l in range(N_LAYERS):
+            torch.mv(mats[l], vec, out=out[l])
+
+    one_pass()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_pass()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    us = 1e6 * (time.perf_counter() - t0) / (N_LAYERS * args.steps)
+    del mats
+    nbytes = rows * H * 2
+    return {"op": "torch.mv, bf16 [%d x %d] (one layer's bytes), 48 distinct matrices per graph"
+                  % (rows, H),
+            "us_per_layer": round(us, 3), "bytes": nbytes,
+            "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 # kernel symbol fragment -> name used by the launch trace and the bench line
 TRAFFIC_KERNELS = [
     ("k_router_keys", "router_keys"), ("k_decode1_gateup", "decode_gateup"),
-    ("k_decode_gateup", "decode_gateup"), ("k_decode_down", "decode_down"),
+    ("k_decode_gateup", "decode_gateup"), ("k_decode1_down", "decode_down"),
+    ("k_decode_down", "decode_down"),
     ("k_prefill_bf16<0,", "prefill_gateup"), ("k_prefill_bf16<2,", "prefill_down"),
     ("k_dense<0,", "route_router_approx"), ("k_dense<3,", "router_approx"),
     ("k_dense<1,", "prefill_shared_gateup"),
@@ -535,10 +684,22 @@ def main():
         roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4),
                     "traffic": measured_traffic("decode_gateup") if default_fmt else None,
-                    "kernel": "k_decode_gateup", "bytes_per_launch": dom["bytes"],
+                    "kernel": DECODE_GATEUP_KERNEL, "bytes_per_launch": dom["bytes"],
                     "avg_us": dom["avg_us"]}
     layer_bytes = sum(k["bytes"] for k in kernels.values()) if kernels else None
-    log(f"decode: {value:.0f} layer-tokens/s, {1e6 * wall / (N_LAYERS * args.steps):.2f} us/layer")
+    us_layer = 1e6 * wall / (N_LAYERS * args.steps)
+    # the whole layer against the HBM roofline: algorithmic bytes of its
+    # kernels over the graph-timed time per layer
+    layer_roofline = None
+    if layer_bytes:
+        gbs = layer_bytes / (us_layer * 1e-6) / 1e9
+        layer_roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                          "bytes_per_layer": layer_bytes, "us_per_layer": round(us_layer, 3)}
+    log(f"decode: {value:.0f} layer-tokens/s, {us_layer:.2f} us/layer")
+
+    ceiling = None if args.no_ceiling else streaming_ceiling(torch, layer_bytes or 25_838_079, args)
+    verify = None if args.no_verify else verify_batches(M, torch, spec, d, layers, args)
 
     prefill = None
     if not args.no_prefill:
@@ -593,7 +754,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(args.cpu_tokens, args.seed)
+        cpu = cpu_baseline(args.cpu_tokens, args.seed, args.cpu_tokens_1t)
 
     line = {
         "metric": "MoE-layer tokens/s (batch-1 decode, 4k prefill) + % HBM/MFMA roofline",
@@ -616,6 +777,9 @@ def main():
                    "gpu_event_s": round(gpu_s, 6), "graphs": not args.eager,
                    "layer_bytes": layer_bytes},
         "roofline": roofline,
+        "layer_roofline": layer_roofline,
+        "streaming_ceiling": ceiling,
+        "verify": verify,
         "kernels": kernels,
         "prefill": prefill,
         "cpu_baseline": cpu,
