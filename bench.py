@@ -362,6 +362,33 @@ def prof_summary(out_dir, command, title):
                 print(f"| `{n}` | {sum(warm) / len(warm):.2f} | {sum(rep) / max(1, len(rep)):.2f} "
                       f"| {sum(last) / len(last):.2f} |")
             print()
+        # per-layer timeline of the replayed decode graphs: each layer is the
+        # chain router keys -> gate/up -> down; durations of the three kernels
+        # and the gaps between one kernel's end and the next one's start
+        seq = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), short(r.get("Kernel_Name", "")))
+                     for r in trace if "moe::k_decode1" in short(r.get("Kernel_Name", ""))
+                     or "moe::k_router_keys_dec" in short(r.get("Kernel_Name", "")))
+        order = ("k_router_keys_dec", "k_decode1_gateup", "k_decode1_down")
+        layers_t = []
+        for i in range(len(seq) - 3):
+            a, b, c, nxt = seq[i], seq[i + 1], seq[i + 2], seq[i + 3]
+            if all(o in x[2] for o, x in zip(order, (a, b, c))) and order[0] in nxt[2] \
+                    and "true" in a[2] and nxt[0] - c[1] < 20000:
+                layers_t.append((a[1] - a[0], b[0] - a[1], b[1] - b[0], c[0] - b[1], c[1] - c[0],
+                                 nxt[0] - c[1], nxt[0] - a[0]))
+        # drop the eager passes: keep layers whose chain gaps look like graph replays
+        if layers_t:
+            arr = np.array(layers_t, dtype=np.float64) / 1e3
+            med_gap = np.median(arr[:, 5])
+            rep = arr[arr[:, 5] <= 4 * max(med_gap, 0.5)]
+            print(f"Per-layer timeline of batch-1 decode ({len(rep)} consecutive layer chains "
+                  "router -> gate/up -> down whose next layer starts within a few us, i.e. graph "
+                  "replays; us, median [10th-90th percentile]):\n")
+            print("| router | gap | gate/up | gap | down | gap to next layer | layer start to next |")
+            print("|---|---|---|---|---|---|---|")
+            print("| " + " | ".join(f"{np.median(rep[:, k]):.2f} [{np.percentile(rep[:, k], 10):.2f}-"
+                                     f"{np.percentile(rep[:, k], 90):.2f}]" for k in range(7)) + " |")
+            print()
     ctr = rows("*counter_collection.csv")
     if ctr:
         agg = {}
@@ -388,15 +415,39 @@ def prof_summary(out_dir, command, title):
         for c, f in sorted(factor.items()):
             print(f"- {c}: reference copy counted {calib[c][1]:.0f} KiB -> factor {f:.4f}")
         print()
-        print("| kernel | counter | dispatches | avg KiB | scaled bytes per dispatch |")
+        print("| kernel | counter | dispatches | avg (KiB for byte counters) | scaled bytes per dispatch |")
         print("|---|---|---|---|---|")
         for (n, c), a in sorted(agg.items()):
             if "moe::" not in n:
                 continue
             v = a[1] / a[0]
             scaled = f"{v * 1024 * factor[c]:.0f}" if c in factor else "-"
-            print(f"| `{n}` | {c} | {a[0]} | {v:.1f} | {scaled} |")
+            print(f"| `{n}` | {c} | {a[0]} | {v:.4g} | {scaled} |")
         print()
+        # derived figures when the instruction and busy counters are present:
+        # GRBM_GUI_ACTIVE is summed over the 8 XCDs, so one XCD's active
+        # cycles are a eighth of it; 256 CUs x 4 SIMDs; a wave64 VALU
+        # instruction occupies its SIMD for 4 cycles
+        names = sorted({n for (n, c) in agg if "moe::" in n})
+        avg = {(n, c): a[1] / a[0] for (n, c), a in agg.items()}
+        if any((n, "SQ_VALU_MFMA_BUSY_CYCLES") in avg for n in names):
+            print("Derived per dispatch (GUI = GRBM_GUI_ACTIVE / 8, one XCD's active cycles; "
+                  "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GUI x 1024 SIMDs); VALU issue = 4 x "
+                  "SQ_INSTS_VALU / (GUI x 1024); bf16 MFMA flops = 512 x "
+                  "SQ_INSTS_VALU_MFMA_MOPS_BF16):\n")
+            print("| kernel | GUI cycles | MFMA busy | VALU issue | VALU / MFMA instructions | bf16 MFMA GFLOP |")
+            print("|---|---|---|---|---|---|")
+            for n in names:
+                g = avg.get((n, "GRBM_GUI_ACTIVE"), 0.0) / 8
+                if not g:
+                    continue
+                mb = avg.get((n, "SQ_VALU_MFMA_BUSY_CYCLES"), 0.0) / (g * 1024)
+                vi = 4 * avg.get((n, "SQ_INSTS_VALU"), 0.0) / (g * 1024)
+                nm = avg.get((n, "SQ_INSTS_MFMA"), 0.0)
+                ratio = f"{avg.get((n, 'SQ_INSTS_VALU'), 0.0) / nm:.2f}" if nm else "-"
+                gf = 512 * avg.get((n, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), 0.0) / 1e9
+                print(f"| `{n}` | {g:.0f} | {100 * mb:.1f}% | {100 * vi:.1f}% | {ratio} | {gf:.1f} |")
+            print()
 
 
 # the kernel that runs gate/up in batch-1 decode (the dominant decode kernel)
@@ -445,6 +496,15 @@ def verify_batches(M, torch, spec, d, layers, args, sizes=(4, 8, 16), n_graphs=4
             graphs[k % n_graphs].replay()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        # per-kernel durations: one eager pass of each batch with the launch trace
+        trace = M.Trace(n_graphs * N_LAYERS * 8)
+        with trace:
+            for g in range(n_graphs):
+                batch_pass(g)
+        torch.cuda.synchronize()
+        kd = {}
+        for name, ms in trace.durations_ms():
+            kd.setdefault(name, []).append(1e3 * ms)
         ids = IDS.cpu().numpy()
         unions, nbytes = [], []
         for g in range(n_graphs):
@@ -463,7 +523,8 @@ def verify_batches(M, torch, spec, d, layers, args, sizes=(4, 8, 16), n_graphs=4
                         "us_per_layer": round(us_layer, 3),
                         "mean_union": round(float(np.mean(unions)), 2),
                         "bytes_per_layer": int(mean_bytes),
-                        "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+                        "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "kernels_avg_us": {n: round(float(np.mean(v)), 2) for n, v in kd.items()}}
         log(f"verify T={T}: {out[f'T{T}']}")
         del graphs, X, zt, z0
     return {"workload": "verify decode: T correlated tokens (cosine ~0.6) per layer call through "
