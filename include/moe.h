@@ -338,6 +338,18 @@ int moe_forward_prefill(const moe_dims* dims, const moe_layer* layer, const void
                         float* topk_w, int32_t* expert_offsets, int32_t* sorted_routes,
                         void* ws, size_t* ws_bytes, hipStream_t stream);
 
+/* Checks a layer before use: the arguments as the forward calls check them,
+ * then the device tier map (copied on `stream`, which is synchronised): every
+ * entry must name a slot of its tier (tier in 0..2, slot < n_slots[tier]) and
+ * no slot may be named twice.  The forward calls read the tier map on the
+ * device and cannot report a bad entry: an expert whose entry is out of range
+ * contributes nothing to the output (it is skipped; no table is read out of
+ * bounds).  moe_build_tiers always writes a valid map; callers that fill
+ * tier_map themselves run this check once after loading.  Returns MOE_OK,
+ * MOE_EINVAL (bad map or argument) or MOE_EHIP.  Synchronous; not
+ * capturable. */
+int moe_check_layer(const moe_dims* dims, const moe_layer* layer, hipStream_t stream);
+
 /* Kernels of the library, as reported by the launch trace. */
 typedef enum {
   MOE_K_ROUTER_KEYS = 1,           /* A1: float64 router GEMV                   */

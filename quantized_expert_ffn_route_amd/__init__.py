@@ -25,7 +25,7 @@ __all__ = [
     "MOE_SRC_F32", "MOE_SRC_CODES", "MOE_MXFP4",
     "MoeError", "MoeLibraryMissing", "MoeDims", "MoeLayer", "MoeExpertSource",
     "lib", "library_path", "status_string", "dims", "tier_table_bytes",
-    "build_tiers", "plan_tiers", "route", "forward_decode", "forward_decode_noalloc",
+    "build_tiers", "plan_tiers", "check_layer", "route", "forward_decode", "forward_decode_noalloc",
     "forward_prefill", "workspace_bytes",
     "DeviceLayer", "Trace", "KERNEL_NAMES",
 ]
@@ -117,6 +117,8 @@ def lib():
         L.moe_forward_decode_noalloc.argtypes = [POINTER(MoeDims), POINTER(MoeLayer), c_void_p,
                                                  c_int32, c_void_p, c_int32, c_void_p, c_void_p,
                                                  c_void_p]
+        L.moe_check_layer.restype = ctypes.c_int
+        L.moe_check_layer.argtypes = [POINTER(MoeDims), POINTER(MoeLayer), c_void_p]
         L.moe_set_trace.restype = ctypes.c_int
         L.moe_set_trace.argtypes = [c_void_p, c_void_p, c_int32, c_void_p]
         L.moe_forward_prefill.restype = ctypes.c_int
@@ -253,6 +255,12 @@ def forward_decode(d: MoeDims, layer: MoeLayer, x, y, y_dt: int, topk_ids=None, 
                                   _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ctypes.byref(n),
                                   _stream(stream))
     _check(rc, "moe_forward_decode")
+
+
+def check_layer(d: MoeDims, layer: MoeLayer, stream=None) -> int:
+    """``moe_check_layer``: the status (MOE_OK, or MOE_EINVAL for a bad tier
+    map) rather than an exception."""
+    return int(lib().moe_check_layer(ctypes.byref(d), ctypes.byref(layer), _stream(stream)))
 
 
 def forward_decode_noalloc(d: MoeDims, layer: MoeLayer, x, y, y_dt: int, topk_ids=None,

@@ -231,6 +231,28 @@ const char* moe_status_string(int status) {
   }
 }
 
+int moe_check_layer(const moe_dims* dims, const moe_layer* layer, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_layer(dims, layer))) return rc;
+  const int E = dims->n_experts;
+  std::vector<int32_t> tmap(E);
+  clear_hip_error();
+  if (hipMemcpyAsync(tmap.data(), layer->tier_map, (size_t)E * sizeof(int32_t),
+                     hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return MOE_EHIP;
+  // every entry names a slot of a non-empty tier, and no slot twice
+  std::vector<uint8_t> used[3];
+  for (int t = 0; t < 3; t++) used[t].assign((size_t)layer->n_slots[t], 0);
+  for (int e = 0; e < E; e++) {
+    const int t = tmap[e] >> 16, sl = tmap[e] & 0xFFFF;
+    if (t < 0 || t > 2 || sl >= layer->n_slots[t] || used[t][sl]) return MOE_EINVAL;
+    used[t][sl] = 1;
+  }
+  return MOE_OK;
+}
+
 int moe_set_trace(hipEvent_t* events, int32_t* tags, int32_t capacity, int32_t* n_used) {
   if (events && (capacity < 0 || !tags || !n_used)) return MOE_EINVAL;
   g_trace.events = events;

@@ -753,3 +753,23 @@ def test_planned_tiers_through_decode_and_prefill():
     ref = O.moe_layer(act_f64(x, "bf16"), tl.ol)
     np.testing.assert_array_equal(ids, ref["ids"])
     check_y(y, ref["y"], "bf16", f"prefill T=300, planned split {tuple(plan)}")
+
+
+def test_check_layer_flags_bad_tier_maps(mid):
+    # a valid map passes; an entry past its tier, an unknown tier or a slot
+    # named twice is refused (the forward calls would skip such an expert)
+    d, L = mid.dl.d, mid.dl.c_struct()
+    assert M.check_layer(d, L) == M.MOE_OK
+    good = mid.dl.tier_map.clone()
+    try:
+        for bad in ((0, (3 << 16) | 0), (1, (0 << 16) | mid.spec.n_slots[0]),
+                    (2, int(good[3].item()))):
+            e, v = bad
+            mid.dl.tier_map.copy_(good)
+            mid.dl.tier_map[e] = v
+            torch.cuda.synchronize()
+            assert M.check_layer(d, L) == M.MOE_EINVAL, bad
+    finally:
+        mid.dl.tier_map.copy_(good)
+        torch.cuda.synchronize()
+    assert M.check_layer(d, L) == M.MOE_OK

@@ -528,3 +528,15 @@ def test_decode_noalloc_refuses_workspaces_beyond_its_scratch():
     assert lib.moe_forward_decode(ctypes.byref(full), ctypes.byref(Lf), None, 1, None, M.MOE_BF16,
                                   None, None, None, ctypes.byref(n), None) == M.MOE_OK
     assert n.value <= limit
+
+
+def test_check_layer_argument_errors_without_gpu():
+    # argument errors are found before the tier map is read from the device
+    lib = M.lib()
+    d = M.dims(256, 128, 64, 4, False, "f32")
+    L = _fake_layer(d, (32, 0, 0))            # counts do not sum to E
+    assert lib.moe_check_layer(ctypes.byref(d), ctypes.byref(L), None) == M.MOE_EINVAL
+    L = _fake_layer(d, (64, 0, 0))
+    L.tier_map = None
+    assert lib.moe_check_layer(ctypes.byref(d), ctypes.byref(L), None) == M.MOE_EINVAL
+    assert lib.moe_check_layer(None, ctypes.byref(L), None) == M.MOE_EINVAL
