@@ -254,6 +254,28 @@ __device__ __forceinline__ uint32_t load_scale(const uint32_t* dm, size_t idx) {
   else return dm[idx];
 }
 
+// Copies n uint4 from global memory into LDS with the whole workgroup,
+// eight loads per thread in flight before their stores (a plain strided loop
+// would wait for each load before the next).  `src_at(i)` gives the address
+// of element i.
+template <typename SrcAt>
+__device__ __forceinline__ void copy_to_lds(uint4* __restrict__ dst, int n, SrcAt src_at) {
+  const int nt = blockDim.x;
+  for (int i0 = threadIdx.x; i0 < n; i0 += 8 * nt) {
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int i = i0 + j * nt;
+      if (i < n) v[j] = *src_at(i);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int i = i0 + j * nt;
+      if (i < n) dst[i] = v[j];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // MFMA wrappers.  Lane l of a 16x16 tile: operand row/column l % 16, k-group
 // l / 16; accumulator element i is C[4*(l/16) + i][l % 16].
@@ -280,6 +302,32 @@ __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Wave sums of 8 candidates at once: p[c] is this lane's partial of
+// candidate c.  Each exchange hands the half of the candidates this lane does
+// not keep to its partner, so candidate c's total ends in lanes 8c .. 8c + 7
+// after 10 fp64 exchanges instead of 48.  Every addition pairs the same two
+// partial sums as wave_sum_f64 (partners at distance 32, 16, 8, 4, 2, 1), so
+// each total is bit-identical to wave_sum_f64 of that candidate's partials.
+__device__ __forceinline__ double wave_sum8_f64(const double (&p)[8], int lane) {
+  double q4[4], q2[2];
+  const bool h32 = (lane >> 5) & 1, h16 = (lane >> 4) & 1, h8 = (lane >> 3) & 1;
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    const double keep = h32 ? p[c + 4] : p[c], send = h32 ? p[c] : p[c + 4];
+    q4[c] = keep + __shfl_xor(send, 32, 64);
+  }
+#pragma unroll
+  for (int c = 0; c < 2; c++) {
+    const double keep = h16 ? q4[c + 2] : q4[c], send = h16 ? q4[c] : q4[c + 2];
+    q2[c] = keep + __shfl_xor(send, 16, 64);
+  }
+  double v = (h8 ? q2[1] : q2[0]) + __shfl_xor(h8 ? q2[0] : q2[1], 8, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 1, 64);
   return v;
 }
 

@@ -97,24 +97,29 @@ __global__ __launch_bounds__(256) void k_router_keys(const A* __restrict__ x, co
   }
 }
 
-// Decode variant (T <= 16, tokens fit in 64 KiB of LDS): two experts per
-// workgroup (one wave each), so the router rows spread over every CU.  Each
-// lane issues all loads of its router row first, then the group's tokens are
-// staged in LDS; both round trips overlap.  A single token (ONE) skips the
-// staging: each lane loads its own chunks of x next to its router chunks, so
-// no barrier sits between the loads and the arithmetic.  Same per-lane order
-// and butterfly as k_router_keys, so the keys are bit-identical.
+// Decode variant (T <= 16, tokens fit in 64 KiB of LDS), one expert per
+// wave.  A single token (ONE): two experts per workgroup, so the router rows
+// spread over every CU, and each lane loads its own chunks of x next to its
+// router chunks, so no barrier sits between the loads and the arithmetic.
+// Several tokens: eight experts per workgroup; each lane issues all loads of
+// its router row first, then the group's tokens are staged in LDS (both round
+// trips overlap) and eight tokens' partials are summed over the wave at once.
+// Same per-lane order and the same pairing of partial sums as k_router_keys,
+// so the keys are bit-identical.
 constexpr int kRouterDecWaves = 2;
+// Group tokens: eight experts per workgroup, so that each copy of the group's
+// tokens into LDS serves eight router rows.
+constexpr int kRouterGrpWaves = 8;
 
 template <typename A, int MAXC, bool ONE>
-__global__ __launch_bounds__(64 * kRouterDecWaves) void k_router_keys_dec(const A* __restrict__ x,
+__global__ __launch_bounds__(64 * kRouterGrpWaves) void k_router_keys_dec(const A* __restrict__ x,
                                                                           const A* __restrict__ w,
                                                                           const float* __restrict__ bias,
                                                                           double* __restrict__ keys,
                                                                           int T, int H, int E) {
   extern __shared__ uint4 s_x[];
   const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * kRouterDecWaves + (threadIdx.x >> 6);
+  const int e = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int nchunk = H / 8;
   constexpr int U4 = (int)sizeof(A) / 2;     // uint4 per 8-element chunk
   uint4 wraw[MAXC][U4];
@@ -153,30 +158,44 @@ __global__ __launch_bounds__(64 * kRouterDecWaves) void k_router_keys_dec(const 
     if (lane == 0) keys[e] = sum + b;
     return;
   }
-  const int n16 = T * H * (int)sizeof(A) / 16;
-  for (int i = threadIdx.x; i < n16; i += blockDim.x) s_x[i] = reinterpret_cast<const uint4*>(x)[i];
+  const uint4* xs = reinterpret_cast<const uint4*>(x);
+  copy_to_lds(s_x, T * H * (int)sizeof(A) / 16, [&](int i) { return xs + i; });
   __syncthreads();
   if (e >= E) return;
   const double b = bias ? (double)bias[e] : 0.0;
   const A* sxa = reinterpret_cast<const A*>(s_x);
-  for (int t = 0; t < T; t++) {
-    double acc = 0.0;
+  // eight tokens' partials at a time, summed over the wave together
+  // (wave_sum8_f64 pairs the same partial sums as wave_sum_f64, so every key
+  // is bit-identical to the one-token path's); token t0 + c ends in lanes
+  // 8c .. 8c + 7
+  for (int t0 = 0; t0 < T; t0 += 8) {
+    double p[8];
 #pragma unroll
-    for (int j = 0; j < MAXC; j++) {
-      const int q = lane + 64 * j;
-      if (q < nchunk) {
-        double wv[8], xv[8];
-        uint4 xr[U4];
+    for (int c = 0; c < 8; c++) {
+      const int t = t0 + c;
+      double acc = 0.0;
+      if (t < T) {
 #pragma unroll
-        for (int u = 0; u < U4; u++) xr[u] = reinterpret_cast<const uint4*>(sxa + (size_t)t * H + 8 * q)[u];
-        cvt8_f64<A>(wraw[j], wv);
-        cvt8_f64<A>(xr, xv);
+        for (int j = 0; j < MAXC; j++) {
+          const int q = lane + 64 * j;
+          if (q < nchunk) {
+            double wv[8], xv[8];
+            uint4 xr[U4];
 #pragma unroll
-        for (int k = 0; k < 8; k++) acc = __builtin_fma(xv[k], wv[k], acc);
+            for (int u = 0; u < U4; u++)
+              xr[u] = reinterpret_cast<const uint4*>(sxa + (size_t)t * H + 8 * q)[u];
+            cvt8_f64<A>(wraw[j], wv);
+            cvt8_f64<A>(xr, xv);
+#pragma unroll
+            for (int k = 0; k < 8; k++) acc = __builtin_fma(xv[k], wv[k], acc);
+          }
+        }
       }
+      p[c] = acc;
     }
-    const double sum = wave_sum_f64(acc);
-    if (lane == 0) keys[(size_t)t * E + e] = sum + b;
+    const double sum = wave_sum8_f64(p, lane);
+    const int c = lane >> 3;
+    if ((lane & 7) == 0 && t0 + c < T) keys[(size_t)(t0 + c) * E + e] = sum + b;
   }
 }
 
@@ -184,16 +203,17 @@ void launch_router_keys(int act, const void* x, const void* w, const float* b, d
                         int T, int H, int E, hipStream_t s) {
   const size_t xbytes = (size_t)T * H * (act == MOE_BF16 ? 2 : 4);
   if (T <= kGroup && xbytes <= 65536 && H <= 4096) {
-    dim3 grid((E + kRouterDecWaves - 1) / kRouterDecWaves);
     const int maxc = (H / 8 + 63) / 64;
+    const dim3 grid1((E + kRouterDecWaves - 1) / kRouterDecWaves);
+    const dim3 gridg((E + kRouterGrpWaves - 1) / kRouterGrpWaves);
 #define MOE_RK(AT, MC)                                                                          \
   do {                                                                                          \
     if (T == 1)                                                                                 \
-      MOE_LAUNCH(MOE_K_ROUTER_KEYS, (k_router_keys_dec<AT, MC, true>), grid,                    \
+      MOE_LAUNCH(MOE_K_ROUTER_KEYS, (k_router_keys_dec<AT, MC, true>), grid1,                   \
                  dim3(64 * kRouterDecWaves), 0, s, (const AT*)x, (const AT*)w, b, keys, T, H, E); \
     else                                                                                        \
-      MOE_LAUNCH(MOE_K_ROUTER_KEYS, (k_router_keys_dec<AT, MC, false>), grid,                   \
-                 dim3(64 * kRouterDecWaves), xbytes, s, (const AT*)x, (const AT*)w, b, keys, T, \
+      MOE_LAUNCH(MOE_K_ROUTER_KEYS, (k_router_keys_dec<AT, MC, false>), gridg,                  \
+                 dim3(64 * kRouterGrpWaves), xbytes, s, (const AT*)x, (const AT*)w, b, keys, T, \
                  H, E);                                                                         \
   } while (0)
     if (act == MOE_BF16) {
@@ -344,32 +364,6 @@ __device__ __forceinline__ float wave_max_f32(float v) {
                      __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 16))),
                fmaxf(__uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 32)),
                      __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 48))));
-}
-
-// Wave sums of 8 candidates at once: p[c] is this lane's partial of
-// candidate c.  Each exchange hands the half of the candidates this lane does
-// not keep to its partner, so candidate c's total ends in lanes 8c .. 8c + 7
-// after 10 fp64 exchanges instead of 48.  Every addition pairs the same two
-// partial sums as wave_sum_f64 (partners at distance 32, 16, 8, 4, 2, 1), so
-// each total is bit-identical to wave_sum_f64 of that candidate's partials.
-__device__ __forceinline__ double wave_sum8_f64(const double (&p)[8], int lane) {
-  double q4[4], q2[2];
-  const bool h32 = (lane >> 5) & 1, h16 = (lane >> 4) & 1, h8 = (lane >> 3) & 1;
-#pragma unroll
-  for (int c = 0; c < 4; c++) {
-    const double keep = h32 ? p[c + 4] : p[c], send = h32 ? p[c] : p[c + 4];
-    q4[c] = keep + __shfl_xor(send, 32, 64);
-  }
-#pragma unroll
-  for (int c = 0; c < 2; c++) {
-    const double keep = h16 ? q4[c + 2] : q4[c], send = h16 ? q4[c] : q4[c + 2];
-    q2[c] = keep + __shfl_xor(send, 16, 64);
-  }
-  double v = (h8 ? q2[1] : q2[0]) + __shfl_xor(h8 ? q2[0] : q2[1], 8, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 1, 64);
-  return v;
 }
 
 // The float64 key partial of this lane for a token held as raw bf16 pairs
