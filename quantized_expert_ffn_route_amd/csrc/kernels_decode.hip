@@ -312,10 +312,14 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode_gateup(const Item*
 // bin holding the K-th key.  The keys in that bin and above -- each larger
 // than every key outside -- are gathered in LDS and ranked exactly by (key
 // desc, id asc) in wave 0.  NaN or infinite keys, or more than 64 candidates,
-// hand over to the wave-level selection.  Wave 0's lanes r < K end with the
-// r-th id and its order key.
+// hand over to the wave-level selection.  S.sel[r], r < K, holds the r-th id
+// and its order key once the caller's next barrier has passed.  (Every wave
+// scanning the histogram itself, or every candidate ranking itself against
+// the gathered keys, saves barriers but was measured slower: the eight waves
+// share four SIMDs, so extra per-wave work costs more than a barrier.)
 struct TopkBlockLds {
   TopkSlot cand[64];
+  TopkSlot sel[64];
   uint32_t hist[256];
   float mx[kGateUpWaves], mn[kGateUpWaves];
   int bad[kGateUpWaves];
@@ -339,7 +343,7 @@ __device__ __forceinline__ void wave_maxmin_f32(float& mx, float& mn) {
 __device__ __forceinline__ void topk_block(const double* __restrict__ keys, int E, int K,
                                            const int32_t* __restrict__ tier_map,
                                            int32_t* __restrict__ s_tm, TopkBlockLds& S, int lane,
-                                           int wave, int NW, int* sel_id, uint64_t* sel_u) {
+                                           int wave, int NW) {
   const int t = threadIdx.x;
   const bool ok = t < E;
   const double k = keys[ok ? t : E - 1];
@@ -409,19 +413,25 @@ __device__ __forceinline__ void topk_block(const double* __restrict__ keys, int 
     if (S.cnt < K) mode = 2;
   }
   if (wave != 0) return;
+  int sid;
+  uint64_t su;
   if (mode == 2) {
-    topk_threshold<8>(keys, E, K, lane, S.cand, sel_id, sel_u);
-    return;
+    topk_threshold<8>(keys, E, K, lane, S.sel, &sid, &su);
+  } else {
+    const int nc = S.cnt;
+    uint64_t mu = 0;
+    uint32_t mid_ = 0xFFFFFFFFu;
+    if (lane < nc) {
+      mu = S.cand[lane].u;
+      mid_ = S.cand[lane].id;
+    }
+    wave_sync_lds();
+    rank_select(mu, mid_, nc, K, lane, S.sel, &sid, &su);
   }
-  const int nc = S.cnt;
-  uint64_t mu = 0;
-  uint32_t mid_ = 0xFFFFFFFFu;
-  if (lane < nc) {
-    mu = S.cand[lane].u;
-    mid_ = S.cand[lane].id;
+  if (lane < K) {
+    S.sel[lane].u = su;
+    S.sel[lane].id = (uint32_t)sid;
   }
-  wave_sync_lds();
-  rank_select(mu, mid_, nc, K, lane, S.cand, sel_id, sel_u);
 }
 
 template <typename A, int NC, int KPL>
@@ -436,7 +446,6 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode1_gateup(const doub
                                                          int32_t* __restrict__ n_items) {
   __shared__ float red[kGateUpWaves][8][64];
   __shared__ int32_t s_tm[4096];
-  __shared__ int32_t s_sel;
   __shared__ TopkBlockLds s_tk;
   const int nrg = I / 16;
   const int u = blockIdx.x / nrg, rg = blockIdx.x % nrg;
@@ -444,12 +453,17 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode1_gateup(const doub
   int tier = kDenseTier, slot = 0, bits = 0;
   if (u < K) {
     const bool writer = u == K - 1 && rg == 0;
-    int sid = -1;
-    uint64_t su = 0;
     if (E <= (int)blockDim.x) {
-      topk_block(keys, E, K, tier_map, s_tm, s_tk, lane, wave, NW, &sid, &su);
+      topk_block(keys, E, K, tier_map, s_tm, s_tk, lane, wave, NW);
     } else if (wave == 0) {
-      topk_threshold<KPL>(keys, E, writer ? K : u + 1, lane, s_tk.cand, &sid, &su);
+      const int rounds = writer ? K : u + 1;
+      int sid;
+      uint64_t su;
+      topk_threshold<KPL>(keys, E, rounds, lane, s_tk.cand, &sid, &su);
+      if (lane < rounds) {
+        s_tk.sel[lane].u = su;
+        s_tk.sel[lane].id = (uint32_t)sid;
+      }
     } else {
       // tier map into LDS; four clamped loads in flight per thread per pass
       const int nt = blockDim.x - 64;
@@ -465,52 +479,52 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode1_gateup(const doub
           if (e0 + j * nt < E) s_tm[e0 + j * nt] = v[j];
       }
     }
-    if (wave == 0) {
-      if (lane == u) s_sel = sid;
-      if (writer) {
-        const double key = lane < K ? key_of_order(su) : 0.0;
-        const float g = topk_weight(key, lane, K);
-        if (lane < K) {
-          ids[lane] = sid;
-          wts[lane] = g;
-          const int tm = tier_map[sid];
-          const int t = tm >> 16, sl = tm & 0xFFFF;
-          const int ns = t == 0 ? n_slots.x : (t == 1 ? n_slots.y : n_slots.z);
-          const bool ok = t >= 0 && t < 3 && sl < ns;
-          Item& it = items[lane];
-          it.expert = sid;
-          it.tier = ok ? t : -1;
-          it.slot = ok ? sl : 0;
-          it.bits = ok ? (t == 0 ? tier_bits.x : (t == 1 ? tier_bits.y : tier_bits.z)) : 0;
-          it.route[0] = lane;
-          it.gw[0] = g;
+    __syncthreads();
+    if (writer && wave == 0) {
+      // ids, weights and the down kernel's work items, after this
+      // workgroup's own loads are on their way (it is one of K * I / 16)
+      const int sid = lane < K ? (int)s_tk.sel[lane].id : -1;
+      const double key = lane < K ? key_of_order(s_tk.sel[lane].u) : 0.0;
+      const float g = topk_weight(key, lane, K);
+      if (lane < K) {
+        ids[lane] = sid;
+        wts[lane] = g;
+        const int tm = s_tm[sid];
+        const int t = tm >> 16, sl = tm & 0xFFFF;
+        const int ns = t == 0 ? n_slots.x : (t == 1 ? n_slots.y : n_slots.z);
+        const bool ok = t >= 0 && t < 3 && sl < ns;
+        Item& it = items[lane];
+        it.expert = sid;
+        it.tier = ok ? t : -1;
+        it.slot = ok ? sl : 0;
+        it.bits = ok ? (t == 0 ? tier_bits.x : (t == 1 ? tier_bits.y : tier_bits.z)) : 0;
+        it.route[0] = lane;
+        it.gw[0] = g;
+#pragma unroll
+        for (int j = 1; j < kGroup; j++) {
+          it.route[j] = -1;
+          it.gw[j] = 0.0f;
+        }
+      }
+      if (lane == 0) {
+        if (has_shared) {
+          Item& it = items[K];
+          it.expert = -1;
+          it.tier = kDenseTier;
+          it.slot = 0;
+          it.bits = 0;
+          it.route[0] = K;
+          it.gw[0] = 1.0f;
 #pragma unroll
           for (int j = 1; j < kGroup; j++) {
             it.route[j] = -1;
             it.gw[j] = 0.0f;
           }
         }
-        if (lane == 0) {
-          if (has_shared) {
-            Item& it = items[K];
-            it.expert = -1;
-            it.tier = kDenseTier;
-            it.slot = 0;
-            it.bits = 0;
-            it.route[0] = K;
-            it.gw[0] = 1.0f;
-#pragma unroll
-            for (int j = 1; j < kGroup; j++) {
-              it.route[j] = -1;
-              it.gw[j] = 0.0f;
-            }
-          }
-          *n_items = K + (has_shared ? 1 : 0);
-        }
+        *n_items = K + (has_shared ? 1 : 0);
       }
     }
-    __syncthreads();
-    const int tm = s_tm[s_sel];
+    const int tm = s_tm[s_tk.sel[u].id];
     const int t = tm >> 16, sl = tm & 0xFFFF;
     const int ns = t == 0 ? n_slots.x : (t == 1 ? n_slots.y : n_slots.z);
     if (t < 0 || t > 2 || sl >= ns) return;
@@ -660,40 +674,66 @@ __global__ __launch_bounds__(1024) void k_decode_down(const Item* __restrict__ i
 // this workgroup's eight rows of X, lanes 8-15 the same rows of Y, so every
 // lane loads and dequantises a real block (the general kernel leaves half
 // the lanes at zero).  C[0][n < 8] and C[1][n >= 8] are the two items'
-// partial rows; the cross terms are not used.  X and Y always share a tier
-// (the pairing below), so the dequantisation path is uniform per wave.
+// partial rows; the other products are never read, so the lanes that feed
+// only those (A rows 2-15, and Y's lanes of a pair without Y) load X's data
+// again instead of branching around their loads.  X and Y always share a
+// tier (the pairing below), so the dequantisation path is uniform per wave.
+//
+// Nothing is staged in LDS: each lane reads its item's 16-byte header, h row
+// index and weight straight from global memory, every wave pairs the items
+// itself, and the few h values a unit needs come from global memory (L2)
+// next to its weights.  Wave w takes the (pair, super-step) units 2w and
+// 2w + 1 of each batch of 32: with an even number of super-steps (the
+// launcher's condition) both are consecutive super-steps of one pair, so one
+// format branch loads, dequantises and multiplies both, and the only barrier
+// is the one before the final sum over the waves.
+
+template <int BITS>
+__device__ __forceinline__ void down1_unit2(const Tables& tb, int tier, size_t idx,
+                                            const bf16_t* dn, const Frag<bf16_t>& a0,
+                                            const Frag<bf16_t>& a1, f32x4_t& p0, f32x4_t& p1) {
+  // super-steps c and c + 1: 64 blocks, or 128 dense columns, apart
+  Raw<bf16_t> r0, r1;
+  if constexpr (BITS == 0) {
+    load_raw_dense<bf16_t>(r0, dn);
+    load_raw_dense<bf16_t>(r1, dn + 128);
+  } else {
+    load_raw<bf16_t, BITS>(r0, tb.codes[tier][MOE_DOWN], tb.dm[tier][MOE_DOWN], idx);
+    load_raw<bf16_t, BITS>(r1, tb.codes[tier][MOE_DOWN], tb.dm[tier][MOE_DOWN], idx + 64);
+  }
+  const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+  Frag<bf16_t> b;
+  to_frag<bf16_t, BITS>(b, r0);
+  p0 = mma_step(a0, b, z);
+  to_frag<bf16_t, BITS>(b, r1);
+  p1 = mma_step(a1, b, z);
+}
+
 template <typename Y>
 __global__ __launch_bounds__(1024) void k_decode1_down(const Item* __restrict__ items,
                                                        const int32_t* __restrict__ n_items,
                                                        int max_items, const bf16_t* __restrict__ h,
-                                                       int h_rows, Tables tb, Y* __restrict__ y,
-                                                       int H, int I) {
+                                                       Tables tb, Y* __restrict__ y, int H, int I) {
   __shared__ float red[16][16];
-  __shared__ int8_t s_pair[64][2];
-  __shared__ int s_npairs;
-  extern __shared__ uint4 s_dyn[];
-  Item* s_items = reinterpret_cast<Item*>(s_dyn);
-  const bf16_t* s_h = reinterpret_cast<const bf16_t*>(s_dyn + (size_t)max_items * (sizeof(Item) / 16));
+  __shared__ int8_t s_pair[16][64][2];     // one copy per wave
   // the two row halves of a tile sit 8 apart in the grid, on one XCD, so its
   // lines are fetched from HBM once (the grid is a multiple of 16)
   const int rg = ((blockIdx.x >> 4) << 3) | (blockIdx.x & 7), half = (blockIdx.x >> 3) & 1;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, NW = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lm = lane & 15, lg = lane >> 4;
   const int nbg = I / 128, nrg = H / 16;
+  // count and lane i's item (clamped: every load unconditional, all in flight together)
+  const int n_raw = *n_items;
+  const Item* me = items + min(lane, max_items - 1);
+  const int4 hd = *reinterpret_cast<const int4*>(me);   // expert, tier, slot, bits
+  const int hrow = me->route[0];
+  const int gwb = __float_as_int(me->gw[0]);
+  const int n = min(n_raw, min(max_items, 64));
+  int npairs;
   {
-    const int nh = max_items * (int)(sizeof(Item) / 16);
-    const int n16 = h_rows * I * (int)sizeof(bf16_t) / 16;
-    const uint4* si = reinterpret_cast<const uint4*>(items);
-    const uint4* sh = reinterpret_cast<const uint4*>(h);
-    for (int i = threadIdx.x; i < nh + n16; i += blockDim.x)
-      s_dyn[i] = i < nh ? si[i] : sh[i - nh];
-  }
-  const int n = min(*n_items, 64);
-  __syncthreads();
-  if (wave == 0) {
     // pair the items of each tier (dense last) in item order; an odd one out
-    // pairs with nothing.  Lane i holds item i (n <= 64).
-    const int t = lane < n ? s_items[lane].tier : -1;
+    // pairs with nothing.  Lane i holds item i.
+    const int t = lane < n ? hd.y : -1;
     const int cls = t == kDenseTier ? 3 : (t >= 0 && t < 3 ? t : -1);
     const uint64_t below = (1ull << lane) - 1ull;
     int base = 0, my_pair = -1, my_side = 0;
@@ -707,74 +747,66 @@ __global__ __launch_bounds__(1024) void k_decode1_down(const Item* __restrict__ 
       }
       base += (__popcll(m) + 1) >> 1;
     }
+    // one wave's stores to LDS land in program order: a partner's id
+    // overwrites the -1 its pair's first item wrote
     if (my_pair >= 0 && my_side == 0) {
-      s_pair[my_pair][0] = (int8_t)lane;
-      s_pair[my_pair][1] = (int8_t)-1;
+      s_pair[wave][my_pair][0] = (int8_t)lane;
+      s_pair[wave][my_pair][1] = (int8_t)-1;
     }
-    if (my_pair >= 0 && my_side == 1) s_pair[my_pair][1] = (int8_t)lane;
-    if (lane == 0) s_npairs = base;
+    if (my_pair >= 0 && my_side == 1) s_pair[wave][my_pair][1] = (int8_t)lane;
+    wave_sync_lds();
+    npairs = base;
   }
-  __syncthreads();
-  const int units = s_npairs * nbg;
+  const int units = npairs * nbg;
+  const int row = rg * 16 + half * 8 + (lm & 7);
   float acc = 0.f;
-  constexpr int PB = 2;
-  for (int p0 = wave; p0 < units; p0 += NW * PB) {
-    Raw<bf16_t> raw[PB];
+  for (int p0 = 2 * wave; p0 < units; p0 += 32) {
+    const int q = p0 / nbg, c = p0 % nbg;
+    // the pair's tier and format are X's, kept in scalar registers so the
+    // table pointers come from the kernel arguments without a vector load
+    const int ix = s_pair[wave][q][0] & 63, iy = s_pair[wave][q][1];
+    const int tier = __builtin_amdgcn_readlane(hd.y, ix);
+    const int fmt = tier == kDenseTier ? 0 : __builtin_amdgcn_readlane(hd.w, ix) >> 8;  // down format
+    // weight columns: X's item for lanes 0-7, Y's (if any) for lanes 8-15
+    const int it = lm < 8 || iy < 0 ? ix : iy;
+    const int slot = __shfl(hd.z, it, 64);
+    const size_t idx = (((size_t)slot * nrg + rg) * nbg + c) * 64 + 16 * lg + half * 8 + (lm & 7);
+    const bf16_t* dn = reinterpret_cast<const bf16_t*>(tb.dense[MOE_DOWN]) + (size_t)row * I + 128 * c + 32 * lg;
+    // A rows: row 1 is Y's h row when there is a Y, every other row X's
+    const int hr = __shfl(hrow, lm == 1 && iy >= 0 ? iy : ix, 64);
+    const uint4* ap = reinterpret_cast<const uint4*>(h + (size_t)hr * I + 128 * c + 32 * lg);
+    Frag<bf16_t> a0, a1;
 #pragma unroll
-    for (int j = 0; j < PB; j++) {
-      const int p = p0 + NW * j;
-      if (p >= units) continue;
-      const int c = p % nbg;
-      const int it = s_pair[p / nbg][lm >> 3];
-#pragma unroll
-      for (int i = 0; i < 16; i++) raw[j].v[i] = 0u;
-      if (it < 0) continue;
-      const Item& item = s_items[it];
-      const int row = rg * 16 + half * 8 + (lm & 7);
-      if (item.tier == kDenseTier) {
-        load_raw_dense<bf16_t>(raw[j], reinterpret_cast<const bf16_t*>(tb.dense[MOE_DOWN]) +
-                                           (size_t)row * I + 128 * c + 32 * lg);
-      } else {
-        const size_t idx = (((size_t)item.slot * nrg + rg) * nbg + c) * 64 + 16 * lg + half * 8 + (lm & 7);
-        const int dbits = item.bits >> 8;       // down format
-        if (dbits == 4) load_raw<bf16_t, 4>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
-        else if (dbits == kMx4) load_raw<bf16_t, kMx4>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
-        else if (dbits == 3) load_raw<bf16_t, 3>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
-        else load_raw<bf16_t, 2>(raw[j], tb.codes[item.tier][MOE_DOWN], tb.dm[item.tier][MOE_DOWN], idx);
-      }
+    for (int i = 0; i < 4; i++) {
+      const uint4 u0 = ap[i], u1 = ap[16 + i];    // +16 uint4 = +128 columns
+      a0.v[4 * i] = u0.x; a0.v[4 * i + 1] = u0.y; a0.v[4 * i + 2] = u0.z; a0.v[4 * i + 3] = u0.w;
+      a1.v[4 * i] = u1.x; a1.v[4 * i + 1] = u1.y; a1.v[4 * i + 2] = u1.z; a1.v[4 * i + 3] = u1.w;
     }
-#pragma unroll
-    for (int j = 0; j < PB; j++) {
-      const int p = p0 + NW * j;
-      if (p >= units) continue;
-      const int c = p % nbg;
-      const int ix = s_pair[p / nbg][0], iy = s_pair[p / nbg][1];
-      // A: row 0 = h of X, row 1 = h of Y (lanes with lm >= 2 carry zeros)
-      const int ia = lm == 0 ? ix : (lm == 1 ? iy : -1);
-      Frag<bf16_t> ha;
-      ha.load_act(s_h + (size_t)(ia >= 0 ? s_items[ia].route[0] : 0) * I + 128 * c + 32 * lg, ia >= 0);
-      const Item& hx = s_items[ix];           // the pair's tier (X always exists)
-      Frag<bf16_t> b;
-      if (hx.tier == kDenseTier) to_frag<bf16_t, 0>(b, raw[j]);
-      else if ((hx.bits >> 8) == 4) to_frag<bf16_t, 4>(b, raw[j]);
-      else if ((hx.bits >> 8) == kMx4) to_frag<bf16_t, kMx4>(b, raw[j]);
-      else if ((hx.bits >> 8) == 3) to_frag<bf16_t, 3>(b, raw[j]);
-      else to_frag<bf16_t, 2>(b, raw[j]);
-      const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-      const f32x4_t part = mma_step(ha, b, z);
-      // lanes 0-7: C[0][lane] (item X); lanes 8-15: C[1][lane] (item Y)
-      const int mine = lm < 8 ? ix : iy;
-      if (lg == 0 && mine >= 0) acc += s_items[mine].gw[0] * (lm < 8 ? part[0] : part[1]);
+    f32x4_t pa, pb;
+    if (fmt == 0) down1_unit2<0>(tb, tier, idx, dn, a0, a1, pa, pb);
+    else if (fmt == 4) down1_unit2<4>(tb, tier, idx, dn, a0, a1, pa, pb);
+    else if (fmt == kMx4) down1_unit2<kMx4>(tb, tier, idx, dn, a0, a1, pa, pb);
+    else if (fmt == 3) down1_unit2<3>(tb, tier, idx, dn, a0, a1, pa, pb);
+    else down1_unit2<2>(tb, tier, idx, dn, a0, a1, pa, pb);
+    // lanes 0-7: C[0][lane] (item X); lanes 8-15: C[1][lane] (item Y)
+    const float gx = __int_as_float(__builtin_amdgcn_readlane(gwb, ix));
+    const float gy = __int_as_float(__builtin_amdgcn_readlane(gwb, iy & 63));
+    if (lg == 0 && (lm < 8 || iy >= 0)) {
+      const float g = lm < 8 ? gx : gy;
+      acc += g * (lm < 8 ? pa[0] : pa[1]);
+      acc += g * (lm < 8 ? pb[0] : pb[1]);
     }
   }
   if (lane < 16) red[wave][lane] = acc;
   __syncthreads();
   if (wave != 0 || lane >= 8) return;
+  // all sixteen waves' partials read at once, then summed in wave order
+  float pr[16];
+#pragma unroll
+  for (int w = 0; w < 16; w++) pr[w] = red[w][lane] + red[w][lane + 8];
   float sum = 0.f;
 #pragma unroll
-  for (int w = 0; w < 16; w++) {
-    if (w < NW) sum += red[w][lane] + red[w][lane + 8];
-  }
+  for (int w = 0; w < 16; w++) sum += pr[w];
   Y* out = y + rg * 16 + half * 8 + lane;
   if constexpr (sizeof(Y) == 4) *out = sum; else *out = to_bf16(sum);
 }
@@ -855,14 +887,14 @@ void launch_decode_down(int act, int y_dt, const Item* items, const int32_t* n_i
   const size_t stage_bytes = (size_t)h_rows * I * (act == MOE_BF16 ? 2 : 4);
   const bool stage = act == MOE_BF16 && item_bytes + stage_bytes <= 48 * 1024;
   const size_t lds = item_bytes + (stage ? stage_bytes : 0);
-  if (T == 1 && act == MOE_BF16 && stage && max_items <= 64) {
-    // one token: two items per MFMA, no zero lanes
+  if (T == 1 && act == MOE_BF16 && max_items <= 64 && (I / 128) % 2 == 0) {
+    // one token: two items per MFMA, no zero lanes; two super-steps per wave
     if (y_dt == MOE_BF16)
-      MOE_LAUNCH(MOE_K_DECODE_DOWN, k_decode1_down<bf16_t>, grid, dim3(1024), lds, s, items,
-                 n_items, max_items, (const bf16_t*)h, h_rows, tb, (bf16_t*)y, H, I);
+      MOE_LAUNCH(MOE_K_DECODE_DOWN, k_decode1_down<bf16_t>, grid, dim3(1024), 0, s, items,
+                 n_items, max_items, (const bf16_t*)h, tb, (bf16_t*)y, H, I);
     else
-      MOE_LAUNCH(MOE_K_DECODE_DOWN, k_decode1_down<float>, grid, dim3(1024), lds, s, items,
-                 n_items, max_items, (const bf16_t*)h, h_rows, tb, (float*)y, H, I);
+      MOE_LAUNCH(MOE_K_DECODE_DOWN, k_decode1_down<float>, grid, dim3(1024), 0, s, items,
+                 n_items, max_items, (const bf16_t*)h, tb, (float*)y, H, I);
     return;
   }
 #define MOE_DN(AT, YT, PB, ST)                                                                 \
