@@ -262,17 +262,17 @@ template <typename SrcAt>
 __device__ __forceinline__ void copy_to_lds(uint4* __restrict__ dst, int n, SrcAt src_at) {
   const int nt = blockDim.x;
   for (int i0 = threadIdx.x; i0 < n; i0 += 8 * nt) {
-    uint4 v[8];
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
+    // unconditional loads from clamped indices, no branch between them; the
+    // eight words are named values, not an array, so they stay in registers
+    const auto ld = [&](int j) { return *src_at(min(i0 + j * nt, n - 1)); };
+    const uint4 v0 = ld(0), v1 = ld(1), v2 = ld(2), v3 = ld(3);
+    const uint4 v4 = ld(4), v5 = ld(5), v6 = ld(6), v7 = ld(7);
+    const auto st = [&](int j, const uint4& v) {
       const int i = i0 + j * nt;
-      if (i < n) v[j] = *src_at(i);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const int i = i0 + j * nt;
-      if (i < n) dst[i] = v[j];
-    }
+      if (i < n) dst[i] = v;
+    };
+    st(0, v0); st(1, v1); st(2, v2); st(3, v3);
+    st(4, v4); st(5, v5); st(6, v6); st(7, v7);
   }
 }
 
@@ -312,19 +312,19 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 // partial sums as wave_sum_f64 (partners at distance 32, 16, 8, 4, 2, 1), so
 // each total is bit-identical to wave_sum_f64 of that candidate's partials.
 __device__ __forceinline__ double wave_sum8_f64(const double (&p)[8], int lane) {
-  double q4[4], q2[2];
+  // every element read at a constant index, and every choice made between
+  // values: a select between two elements of p would otherwise be folded into
+  // one load at a lane-dependent index, which keeps p in scratch memory
+  const double p0 = p[0], p1 = p[1], p2 = p[2], p3 = p[3];
+  const double p4 = p[4], p5 = p[5], p6 = p[6], p7 = p[7];
   const bool h32 = (lane >> 5) & 1, h16 = (lane >> 4) & 1, h8 = (lane >> 3) & 1;
-#pragma unroll
-  for (int c = 0; c < 4; c++) {
-    const double keep = h32 ? p[c + 4] : p[c], send = h32 ? p[c] : p[c + 4];
-    q4[c] = keep + __shfl_xor(send, 32, 64);
-  }
-#pragma unroll
-  for (int c = 0; c < 2; c++) {
-    const double keep = h16 ? q4[c + 2] : q4[c], send = h16 ? q4[c] : q4[c + 2];
-    q2[c] = keep + __shfl_xor(send, 16, 64);
-  }
-  double v = (h8 ? q2[1] : q2[0]) + __shfl_xor(h8 ? q2[0] : q2[1], 8, 64);
+  const double q0 = (h32 ? p4 : p0) + __shfl_xor(h32 ? p0 : p4, 32, 64);
+  const double q1 = (h32 ? p5 : p1) + __shfl_xor(h32 ? p1 : p5, 32, 64);
+  const double q2 = (h32 ? p6 : p2) + __shfl_xor(h32 ? p2 : p6, 32, 64);
+  const double q3 = (h32 ? p7 : p3) + __shfl_xor(h32 ? p3 : p7, 32, 64);
+  const double r0 = (h16 ? q2 : q0) + __shfl_xor(h16 ? q0 : q2, 16, 64);
+  const double r1 = (h16 ? q3 : q1) + __shfl_xor(h16 ? q1 : q3, 16, 64);
+  double v = (h8 ? r1 : r0) + __shfl_xor(h8 ? r0 : r1, 8, 64);
   v += __shfl_xor(v, 4, 64);
   v += __shfl_xor(v, 2, 64);
   v += __shfl_xor(v, 1, 64);

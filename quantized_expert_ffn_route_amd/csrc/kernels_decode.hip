@@ -598,17 +598,25 @@ __global__ __launch_bounds__(1024) void k_decode_down(const Item* __restrict__ i
       const int p = p0 + NW * j;
       if (p >= npairs) continue;
       const Item& it = s_items[p / nbg];
-      const int c = p % nbg, t = it.tier;
-#pragma unroll
-      for (int i = 0; i < (int)(16 * sizeof(A) / 2); i++) raw[j].v[i] = 0u;
-      if (mine && t >= 0) {
-        const size_t idx = (((size_t)it.slot * nrg + rg) * nbg + c) * 64 + lane;
+      const int c = p % nbg;
+      // the item is the same for the whole wave: tier, format and slot in
+      // scalar registers, so the table pointers come from the kernel
+      // arguments without a vector load (which would wait for every load
+      // before it)
+      const int t = __builtin_amdgcn_readfirstlane(it.tier);
+      const int fmt = __builtin_amdgcn_readfirstlane(it.bits) >> 8;
+      const int slot = __builtin_amdgcn_readfirstlane(it.slot);
+      if (t >= 0) {
+        // the other half's lanes load this half's rows again (their
+        // columns are never stored), so no lane branches around a load
+        const int ml = mine ? lane : lane ^ 8;
+        const size_t idx = (((size_t)slot * nrg + rg) * nbg + c) * 64 + ml;
         const A* dense = reinterpret_cast<const A*>(tb.dense[MOE_DOWN]) +
-                         (size_t)(rg * 16 + lm) * I + 128 * c + 32 * lg;
+                         (size_t)(rg * 16 + (ml & 15)) * I + 128 * c + 32 * lg;
         if (t == kDenseTier) load_down<A, 0>(raw[j], tb, t, idx, dense);
-        else if ((it.bits >> 8) == 4) load_down<A, 4>(raw[j], tb, t, idx, dense);
-        else if ((it.bits >> 8) == kMx4) load_down<A, kMx4>(raw[j], tb, t, idx, dense);
-        else if ((it.bits >> 8) == 3) load_down<A, 3>(raw[j], tb, t, idx, dense);
+        else if (fmt == 4) load_down<A, 4>(raw[j], tb, t, idx, dense);
+        else if (fmt == kMx4) load_down<A, kMx4>(raw[j], tb, t, idx, dense);
+        else if (fmt == 3) load_down<A, 3>(raw[j], tb, t, idx, dense);
         else load_down<A, 2>(raw[j], tb, t, idx, dense);
       }
       if constexpr (!STAGE) {
@@ -621,7 +629,8 @@ __global__ __launch_bounds__(1024) void k_decode_down(const Item* __restrict__ i
       const int p = p0 + NW * j;
       if (p >= npairs) continue;
       const Item& it = s_items[p / nbg];
-      const int c = p % nbg, t = it.tier;
+      const int c = p % nbg, t = __builtin_amdgcn_readfirstlane(it.tier);
+      const int fmt = __builtin_amdgcn_readfirstlane(it.bits) >> 8;
       if (t < 0) continue;
       Frag<A>* hf;
       if constexpr (STAGE) {
@@ -633,9 +642,9 @@ __global__ __launch_bounds__(1024) void k_decode_down(const Item* __restrict__ i
       }
       Frag<A> b;
       if (t == kDenseTier) to_frag<A, 0>(b, raw[j]);
-      else if ((it.bits >> 8) == 4) to_frag<A, 4>(b, raw[j]);
-      else if ((it.bits >> 8) == kMx4) to_frag<A, kMx4>(b, raw[j]);
-      else if ((it.bits >> 8) == 3) to_frag<A, 3>(b, raw[j]);
+      else if (fmt == 4) to_frag<A, 4>(b, raw[j]);
+      else if (fmt == kMx4) to_frag<A, kMx4>(b, raw[j]);
+      else if (fmt == 3) to_frag<A, 3>(b, raw[j]);
       else to_frag<A, 2>(b, raw[j]);
       const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
       const f32x4_t part = mma_step(*hf, b, z);

@@ -101,15 +101,18 @@ __global__ __launch_bounds__(256) void k_router_keys(const A* __restrict__ x, co
 // wave.  A single token (ONE): two experts per workgroup, so the router rows
 // spread over every CU, and each lane loads its own chunks of x next to its
 // router chunks, so no barrier sits between the loads and the arithmetic.
-// Several tokens: eight experts per workgroup; each lane issues all loads of
-// its router row first, then the group's tokens are staged in LDS (both round
-// trips overlap) and eight tokens' partials are summed over the wave at once.
+// Several tokens: kRouterGrpWaves experts per workgroup; each lane issues all
+// loads of its router row first, then the group's tokens are staged in LDS
+// (both round trips overlap), its row is converted to fp64 once for all the
+// tokens (up to 2048 columns), and eight tokens' partials are summed over the
+// wave at once.
 // Same per-lane order and the same pairing of partial sums as k_router_keys,
 // so the keys are bit-identical.
 constexpr int kRouterDecWaves = 2;
-// Group tokens: eight experts per workgroup, so that each copy of the group's
-// tokens into LDS serves eight router rows.
-constexpr int kRouterGrpWaves = 8;
+// Group tokens: two experts per workgroup, so that the E / 2 workgroups
+// spread the fp64 arithmetic (T dot products per router row) over every CU;
+// each workgroup copies the group's tokens into LDS from L2.
+constexpr int kRouterGrpWaves = 2;
 
 template <typename A, int MAXC, bool ONE>
 __global__ __launch_bounds__(64 * kRouterGrpWaves) void k_router_keys_dec(const A* __restrict__ x,
@@ -164,6 +167,14 @@ __global__ __launch_bounds__(64 * kRouterGrpWaves) void k_router_keys_dec(const 
   if (e >= E) return;
   const double b = bias ? (double)bias[e] : 0.0;
   const A* sxa = reinterpret_cast<const A*>(s_x);
+  // the router row in fp64 once, for every token (64 registers at 2048
+  // columns; wider rows convert per token)
+  constexpr bool kHoist = MAXC <= 4;
+  double wv[kHoist ? MAXC : 1][8];
+  if constexpr (kHoist) {
+#pragma unroll
+    for (int j = 0; j < MAXC; j++) cvt8_f64<A>(wraw[j], wv[j]);
+  }
   // eight tokens' partials at a time, summed over the wave together
   // (wave_sum8_f64 pairs the same partial sums as wave_sum_f64, so every key
   // is bit-identical to the one-token path's); token t0 + c ends in lanes
@@ -179,15 +190,21 @@ __global__ __launch_bounds__(64 * kRouterGrpWaves) void k_router_keys_dec(const 
         for (int j = 0; j < MAXC; j++) {
           const int q = lane + 64 * j;
           if (q < nchunk) {
-            double wv[8], xv[8];
+            double xv[8];
             uint4 xr[U4];
 #pragma unroll
             for (int u = 0; u < U4; u++)
               xr[u] = reinterpret_cast<const uint4*>(sxa + (size_t)t * H + 8 * q)[u];
-            cvt8_f64<A>(wraw[j], wv);
             cvt8_f64<A>(xr, xv);
+            if constexpr (kHoist) {
 #pragma unroll
-            for (int k = 0; k < 8; k++) acc = __builtin_fma(xv[k], wv[k], acc);
+              for (int k = 0; k < 8; k++) acc = __builtin_fma(xv[k], wv[j][k], acc);
+            } else {
+              double wt[8];
+              cvt8_f64<A>(wraw[j], wt);
+#pragma unroll
+              for (int k = 0; k < 8; k++) acc = __builtin_fma(xv[k], wt[k], acc);
+            }
           }
         }
       }
