@@ -297,142 +297,14 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode_gateup(const Item*
 // ---- A2 + A3 + A5 for one token ----------------------------------------------
 //
 // Batch-1 decode.  Work item u < K is the token's rank-u expert, item K the
-// shared expert; the shared-expert workgroups skip routing.  When every
-// thread can hold one key (E <= threads), the workgroup selects the top-K
-// together (topk_block); otherwise wave 0 selects the first u + 1 ranks while
-// the other waves prefetch the tier map into LDS.  Workgroup (K - 1, 0)
-// publishes ids, weights and the work items for the down kernel.
-
-// Workgroup-wide exact top-K of one token's keys, one key per thread
-// (E <= blockDim.x), with the tier map copied into LDS in the same round
-// trip.  The keys are counted into 256 value bins of equal width between the
-// block's smallest and largest key, computed in fp32 (rounding to fp32,
-// subtracting and scaling are all monotone, so the bin index never decreases
-// as the key grows); wave 0 scans the histogram from the top bin down to the
-// bin holding the K-th key.  The keys in that bin and above -- each larger
-// than every key outside -- are gathered in LDS and ranked exactly by (key
-// desc, id asc) in wave 0.  NaN or infinite keys, or more than 64 candidates,
-// hand over to the wave-level selection.  S.sel[r], r < K, holds the r-th id
-// and its order key once the caller's next barrier has passed.  (Every wave
-// scanning the histogram itself, or every candidate ranking itself against
-// the gathered keys, saves barriers but was measured slower: the eight waves
-// share four SIMDs, so extra per-wave work costs more than a barrier.)
-struct TopkBlockLds {
-  TopkSlot cand[64];
-  TopkSlot sel[64];
-  uint32_t hist[256];
-  float mx[kGateUpWaves], mn[kGateUpWaves];
-  int bad[kGateUpWaves];
-  int cnt, cb, nb;
-};
-
-__device__ __forceinline__ void wave_maxmin_f32(float& mx, float& mn) {
-#define MOE_MM_STEP(C)                                                   \
-  mx = fmaxf(mx, __uint_as_float(dpp_u32<C>(__float_as_uint(mx))));     \
-  mn = fminf(mn, __uint_as_float(dpp_u32<C>(__float_as_uint(mn))));
-  MOE_MM_STEP(0xB1)    // quad_perm [1,0,3,2]
-  MOE_MM_STEP(0x4E)    // quad_perm [2,3,0,1]
-  MOE_MM_STEP(0x124)   // row_ror:4
-  MOE_MM_STEP(0x128)   // row_ror:8
-#undef MOE_MM_STEP
-  const auto rl = [](float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
-  mx = fmaxf(fmaxf(rl(mx, 0), rl(mx, 16)), fmaxf(rl(mx, 32), rl(mx, 48)));
-  mn = fminf(fminf(rl(mn, 0), rl(mn, 16)), fminf(rl(mn, 32), rl(mn, 48)));
-}
-
-__device__ __forceinline__ void topk_block(const double* __restrict__ keys, int E, int K,
-                                           const int32_t* __restrict__ tier_map,
-                                           int32_t* __restrict__ s_tm, TopkBlockLds& S, int lane,
-                                           int wave, int NW) {
-  const int t = threadIdx.x;
-  const bool ok = t < E;
-  const double k = keys[ok ? t : E - 1];
-  const int tm = tier_map[ok ? t : E - 1];
-  const bool bad = ok && !(fabs(k) < INFINITY);
-  const float kf = (float)k;
-  float mx = ok && !bad ? kf : -INFINITY, mn = ok && !bad ? kf : INFINITY;
-  wave_maxmin_f32(mx, mn);
-  const bool wbad = __ballot(bad) != 0;
-  // every bin is cleared, whatever the workgroup size (128 to 512 threads)
-  for (int i = t; i < 256; i += blockDim.x) S.hist[i] = 0u;
-  if (ok) s_tm[t] = tm;
-  if (lane == 0) {
-    S.mx[wave] = mx;
-    S.mn[wave] = mn;
-    S.bad[wave] = wbad ? 1 : 0;
-  }
-  if (t == 0) S.cnt = 0;
-  __syncthreads();
-  float hi = -INFINITY, lo = INFINITY;
-  int anybad = 0;
-  for (int w = 0; w < NW; w++) {
-    hi = fmaxf(hi, S.mx[w]);
-    lo = fminf(lo, S.mn[w]);
-    anybad |= S.bad[w];
-  }
-  // mode 0: histogram; 1: every key is a candidate; 2: wave-level selection
-  int mode = anybad ? 2 : (E <= 64 ? 1 : (hi > lo ? 0 : 2));
-  int bin = -1;
-  if (mode == 0) {
-    const float scale = 256.0f / (hi - lo);
-    if (ok) {
-      bin = (int)fminf(fmaxf((kf - lo) * scale, 0.0f), 255.0f);
-      atomicAdd(&S.hist[bin], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      int cum = 0, cb = -1, nb = 0;
-      for (int pass = 0; pass < 4 && cb < 0; pass++) {
-        const int c = wave_incl_scan((int)S.hist[255 - 64 * pass - lane]) + cum;
-        const uint64_t m = __ballot(c >= K);
-        if (m) {
-          const int l = (int)__builtin_ctzll(m);
-          cb = 255 - 64 * pass - l;
-          nb = __builtin_amdgcn_readlane(c, l);
-        } else {
-          cum = __builtin_amdgcn_readlane(c, 63);
-        }
-      }
-      if (lane == 0) {
-        S.cb = cb;
-        S.nb = nb;
-      }
-    }
-    __syncthreads();
-    if (S.cb < 0 || S.nb > 64) mode = 2;
-  }
-  if (mode != 2) {
-    if (ok && (mode == 1 || bin >= S.cb)) {
-      const int pos = atomicAdd(&S.cnt, 1);
-      S.cand[pos].u = order_key(k);
-      S.cand[pos].id = (uint32_t)t;
-    }
-    __syncthreads();
-    // fewer than K candidates cannot happen with a consistent histogram; if
-    // it ever did, the wave-level selection below still gives the exact ids
-    if (S.cnt < K) mode = 2;
-  }
-  if (wave != 0) return;
-  int sid;
-  uint64_t su;
-  if (mode == 2) {
-    topk_threshold<8>(keys, E, K, lane, S.sel, &sid, &su);
-  } else {
-    const int nc = S.cnt;
-    uint64_t mu = 0;
-    uint32_t mid_ = 0xFFFFFFFFu;
-    if (lane < nc) {
-      mu = S.cand[lane].u;
-      mid_ = S.cand[lane].id;
-    }
-    wave_sync_lds();
-    rank_select(mu, mid_, nc, K, lane, S.sel, &sid, &su);
-  }
-  if (lane < K) {
-    S.sel[lane].u = su;
-    S.sel[lane].id = (uint32_t)sid;
-  }
-}
+// shared expert; the shared-expert workgroups skip routing.  In a routed
+// workgroup wave 0 selects the first u + 1 ranks (the routing workgroup all
+// K) with the wave-level threshold selection while the other waves copy the
+// tier map into LDS.  (A selection spread over the whole workgroup, one key
+// per thread with a shared histogram, took as long: its barriers and the
+// other waves' instructions cost what the shorter per-wave work saves.)
+// Workgroup (K - 1, 0) publishes ids, weights and the work items for the
+// down kernel.
 
 template <typename A, int NC, int KPL>
 __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode1_gateup(const double* __restrict__ keys, int E, int K,
@@ -446,23 +318,21 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode1_gateup(const doub
                                                          int32_t* __restrict__ n_items) {
   __shared__ float red[kGateUpWaves][8][64];
   __shared__ int32_t s_tm[4096];
-  __shared__ TopkBlockLds s_tk;
+  __shared__ TopkSlot s_sel[64];    // the selection's scratch, then ranks 0..u (all K)
   const int nrg = I / 16;
   const int u = blockIdx.x / nrg, rg = blockIdx.x % nrg;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, NW = blockDim.x >> 6;
   int tier = kDenseTier, slot = 0, bits = 0;
   if (u < K) {
     const bool writer = u == K - 1 && rg == 0;
-    if (E <= (int)blockDim.x) {
-      topk_block(keys, E, K, tier_map, s_tm, s_tk, lane, wave, NW);
-    } else if (wave == 0) {
+    if (wave == 0) {
       const int rounds = writer ? K : u + 1;
       int sid;
       uint64_t su;
-      topk_threshold<KPL>(keys, E, rounds, lane, s_tk.cand, &sid, &su);
+      topk_threshold<KPL>(keys, E, rounds, lane, s_sel, &sid, &su);
       if (lane < rounds) {
-        s_tk.sel[lane].u = su;
-        s_tk.sel[lane].id = (uint32_t)sid;
+        s_sel[lane].u = su;
+        s_sel[lane].id = (uint32_t)sid;
       }
     } else {
       // tier map into LDS; four clamped loads in flight per thread per pass
@@ -483,8 +353,8 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode1_gateup(const doub
     if (writer && wave == 0) {
       // ids, weights and the down kernel's work items, after this
       // workgroup's own loads are on their way (it is one of K * I / 16)
-      const int sid = lane < K ? (int)s_tk.sel[lane].id : -1;
-      const double key = lane < K ? key_of_order(s_tk.sel[lane].u) : 0.0;
+      const int sid = lane < K ? (int)s_sel[lane].id : -1;
+      const double key = lane < K ? key_of_order(s_sel[lane].u) : 0.0;
       const float g = topk_weight(key, lane, K);
       if (lane < K) {
         ids[lane] = sid;
@@ -524,7 +394,7 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode1_gateup(const doub
         *n_items = K + (has_shared ? 1 : 0);
       }
     }
-    const int tm = s_tm[s_tk.sel[u].id];
+    const int tm = s_tm[s_sel[u].id];
     const int t = tm >> 16, sl = tm & 0xFFFF;
     const int ns = t == 0 ? n_slots.x : (t == 1 ? n_slots.y : n_slots.z);
     if (t < 0 || t > 2 || sl >= ns) return;
