@@ -158,7 +158,7 @@ __device__ __forceinline__ void to_frag(Frag<A>& f, const Raw<A>& r) {
 constexpr int kGateUpWaves = 8;
 
 template <typename A, int BITS, int NC>
-__device__ __forceinline__ void gateup_tile(const A* __restrict__ x, int T, int H, int I, int rg,
+__device__ __forceinline__ void gateup_tile(const A* __restrict__ x, bool arow, int H, int I, int rg,
                                             int tier, int slot, const Tables& tb, int wave, int NW,
                                             int lane, f32x4_t& accg, f32x4_t& accu) {
   const int lm = lane & 15, lg = lane >> 4;
@@ -192,7 +192,7 @@ __device__ __forceinline__ void gateup_tile(const A* __restrict__ x, int T, int 
 #pragma unroll
   for (int j = 0; j < NC; j++) {
     const int c = wave + NW * j;
-    if (c < nbg) xa[j].load_act(x + (size_t)lm * H + 128 * c + 32 * lg, lm < T);
+    if (c < nbg) xa[j].load_act(x + (size_t)lm * H + 128 * c + 32 * lg, arow);
   }
 #pragma unroll
   for (int j = 0; j < NC; j++) {
@@ -249,30 +249,30 @@ __device__ __forceinline__ void gateup_store(float (*red)[8][64], const f32x4_t&
 }
 
 template <typename A, int BITS, int NC>
-__device__ __forceinline__ void gateup_item(float (*red)[8][64], const A* __restrict__ x, int T,
+__device__ __forceinline__ void gateup_item(float (*red)[8][64], const A* __restrict__ x, int T, bool arow,
                                             int H, int I, int rg, int tier, int slot,
                                             const Tables& tb, int wave, int NW, int lane,
                                             const int rt[4], A* __restrict__ h) {
   f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  gateup_tile<A, BITS, NC>(x, T, H, I, rg, tier, slot, tb, wave, NW, lane, accg, accu);
+  gateup_tile<A, BITS, NC>(x, arow, H, I, rg, tier, slot, tb, wave, NW, lane, accg, accu);
   gateup_store<A>(red, accg, accu, wave, NW, lane, rt, T, h, I, rg);
 }
 
 template <typename A, int NC>
 __device__ __forceinline__ void gateup_dispatch(float (*red)[8][64], const A* __restrict__ x,
-                                                int T, int H, int I, int rg, int tier, int slot,
-                                                int bits, const Tables& tb, int wave, int NW,
+                                                int T, bool arow, int H, int I, int rg, int tier,
+                                                int slot, int bits, const Tables& tb, int wave, int NW,
                                                 int lane, const int rt[4], A* __restrict__ h) {
   if (tier == kDenseTier)
-    gateup_item<A, 0, NC>(red, x, T, H, I, rg, 0, 0, tb, wave, NW, lane, rt, h);
+    gateup_item<A, 0, NC>(red, x, T, arow, H, I, rg, 0, 0, tb, wave, NW, lane, rt, h);
   else if (bits == 4)
-    gateup_item<A, 4, NC>(red, x, T, H, I, rg, tier, slot, tb, wave, NW, lane, rt, h);
+    gateup_item<A, 4, NC>(red, x, T, arow, H, I, rg, tier, slot, tb, wave, NW, lane, rt, h);
   else if (bits == kMx4)
-    gateup_item<A, kMx4, NC>(red, x, T, H, I, rg, tier, slot, tb, wave, NW, lane, rt, h);
+    gateup_item<A, kMx4, NC>(red, x, T, arow, H, I, rg, tier, slot, tb, wave, NW, lane, rt, h);
   else if (bits == 3)
-    gateup_item<A, 3, NC>(red, x, T, H, I, rg, tier, slot, tb, wave, NW, lane, rt, h);
+    gateup_item<A, 3, NC>(red, x, T, arow, H, I, rg, tier, slot, tb, wave, NW, lane, rt, h);
   else
-    gateup_item<A, 2, NC>(red, x, T, H, I, rg, tier, slot, tb, wave, NW, lane, rt, h);
+    gateup_item<A, 2, NC>(red, x, T, arow, H, I, rg, tier, slot, tb, wave, NW, lane, rt, h);
 }
 
 template <typename A, int NC>
@@ -289,9 +289,13 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode_gateup(const Item*
   const int tier = items[u].tier;
   const int slot = items[u].slot, bits = items[u].bits & 0xFF;   // gate / up format
   const int4 routes = *reinterpret_cast<const int4*>(&items[u].route[4 * (lane >> 4)]);
+  // only the activation rows of tokens routed to this item are read (a
+  // group's item takes a few of its tokens; the other rows stay zero)
+  const int arow_route = items[u].route[lane & 15];
   if (u >= n || tier < 0) return;
   const int rt[4] = {routes.x, routes.y, routes.z, routes.w};
-  gateup_dispatch<A, NC>(red, x, T, H, I, rg, tier, slot, bits, tb, wave, NW, lane, rt, h);
+  const bool arow = (lane & 15) < T && arow_route >= 0;
+  gateup_dispatch<A, NC>(red, x, T, arow, H, I, rg, tier, slot, bits, tb, wave, NW, lane, rt, h);
 }
 
 // ---- A2 + A3 + A5 for one token ----------------------------------------------
@@ -406,7 +410,7 @@ __global__ __launch_bounds__(64 * kGateUpWaves) void k_decode1_gateup(const doub
   }
   // token 0 sits in accumulator element 0 of lanes 0..15; its h row is u
   const int rt[4] = {lane < 16 ? u : -1, -1, -1, -1};
-  gateup_dispatch<A, NC>(red, x, 1, H, I, rg, tier, slot, bits, tb, wave, NW, lane, rt, h);
+  gateup_dispatch<A, NC>(red, x, 1, (lane & 15) == 0, H, I, rg, tier, slot, bits, tb, wave, NW, lane, rt, h);
 }
 
 // ---- A6: down + weighted combine --------------------------------------------
