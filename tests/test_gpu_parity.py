@@ -619,6 +619,28 @@ def test_mxfp4_tiers(tier_bits, down_bits, act):
     check_y(y, ref["y"], act, f"prefill T=300, {tier_bits}/{down_bits} {act}")
 
 
+# Every expert chosen by every token, with h rows too large for the down
+# kernel to stage in LDS (T * (K + 1) rows of 1 KB): the token-group down
+# kernel then reads each tier table up to its last block, whose code field is
+# loaded from a window moved back to end inside the table.
+KE_WIDE = synth.LayerSpec(hidden=256, inter=512, n_experts=8, top_k=8, has_shared=True,
+                          act="bf16", n_slots=(2, 4, 2))
+
+
+@pytest.mark.parametrize("down_bits", [None, (MX, 2, 3)])
+def test_group_down_reads_every_table_to_its_end(down_bits):
+    spec = KE_WIDE.with_(down_bits=down_bits)
+    tl = make_layer(spec, seed=23)
+    for T in (6, 16):
+        x = synth.tokens(spec, T, 180 + T)
+        ref = O.moe_layer(act_f64(x, "bf16"), tl.ol, exact_keys=True)
+        for y_dt, want in ((M.MOE_F32, ref["y"]), (M.MOE_BF16, O.output_cast(ref["y"], "bf16"))):
+            y, ids, w = run_decode(tl, x, y_dt)
+            np.testing.assert_array_equal(ids, ref["ids"])
+            assert np.all(np.sort(ids, axis=1) == np.arange(spec.n_experts))
+            check_y(y, want, "bf16", f"decode T={T}, every expert, down bits {down_bits}")
+
+
 def test_full_size_mixed_formats():
     # full-size layer with both format families in gate/up (tier 0 MXFP4,
     # tiers 1-2 affine) and in down (tier 0 affine, tiers 1-2 MXFP4), so each
