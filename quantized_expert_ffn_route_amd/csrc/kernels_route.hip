@@ -216,6 +216,79 @@ __global__ __launch_bounds__(64 * kRouterGrpWaves) void k_router_keys_dec(const 
   }
 }
 
+// Token groups with bf16 activations and up to 2048 columns: each workgroup
+// takes two experts with eight waves, wave w scoring expert w & 1 for tokens
+// w / 2, w / 2 + 4, ...; so the fp64 arithmetic of the group (T dot products
+// per router row) is spread over four waves per expert instead of one.  Each
+// wave issues its router chunks and its tokens' x chunks (from L2, no LDS
+// staging and no barrier) before any arithmetic, converts its router row to
+// fp64 once, and sums its tokens' partials over the wave together.  Same
+// per-lane order and the same pairing of partial sums as k_router_keys, so
+// the keys are bit-identical.
+constexpr int kRouterSlices = 4;
+constexpr int kRouterSliceTok = kGroup / kRouterSlices;   // tokens per wave
+
+template <int MAXC>
+__global__ __launch_bounds__(64 * 2 * kRouterSlices) void k_router_keys_grp(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, const float* __restrict__ bias,
+    double* __restrict__ keys, int T, int H, int E) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e = blockIdx.x * 2 + (wave & 1), slice = wave >> 1;
+  const int nchunk = H / 8;
+  const bf16_t* wr = w + (size_t)(e < E ? e : E - 1) * H;
+  // every load unconditional (clamped chunk and token), so all are in flight
+  // together
+  uint4 wraw[MAXC], xraw[kRouterSliceTok][MAXC];
+#pragma unroll
+  for (int j = 0; j < MAXC; j++) {
+    const int q = lane + 64 * j;
+    wraw[j] = *reinterpret_cast<const uint4*>(wr + 8 * (q < nchunk ? q : nchunk - 1));
+  }
+#pragma unroll
+  for (int i = 0; i < kRouterSliceTok; i++) {
+    const int t = slice + kRouterSlices * i;
+    const bf16_t* xr = x + (size_t)(t < T ? t : T - 1) * H;
+#pragma unroll
+    for (int j = 0; j < MAXC; j++) {
+      const int q = lane + 64 * j;
+      xraw[i][j] = *reinterpret_cast<const uint4*>(xr + 8 * (q < nchunk ? q : nchunk - 1));
+    }
+  }
+  // keep every load above this point: the scheduler would otherwise move
+  // each one next to its use, one round trip per token
+  __builtin_amdgcn_sched_barrier(0);
+  double wv[MAXC][8];
+#pragma unroll
+  for (int j = 0; j < MAXC; j++) cvt8_f64<bf16_t>(&wraw[j], wv[j]);
+  double p[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    double acc = 0.0;
+    if (i < kRouterSliceTok) {
+#pragma unroll
+      for (int j = 0; j < MAXC; j++) {
+        double xv[8];
+        cvt8_f64<bf16_t>(&xraw[i < kRouterSliceTok ? i : 0][j], xv);
+        double a = acc;
+#pragma unroll
+        for (int k = 0; k < 8; k++) a = __builtin_fma(xv[k], wv[j][k], a);
+        acc = lane + 64 * j < nchunk ? a : acc;
+      }
+    }
+    p[i] = acc;
+  }
+  // token slice + 4c ends in lanes 8c .. 8c + 7
+  const double sum = wave_sum8_f64(p, lane);
+  const int c = lane >> 3, t = slice + kRouterSlices * c;
+  // (a wave past the last expert stores nothing; it has no early exit, which
+  // would let the compiler sink its loads next to their uses)
+  if ((lane & 7) == 0 && c < kRouterSliceTok && t < T && e < E) {
+    const double b = bias ? (double)bias[e] : 0.0;
+    keys[(size_t)t * E + e] = sum + b;
+  }
+}
+
 void launch_router_keys(int act, const void* x, const void* w, const float* b, double* keys,
                         int T, int H, int E, hipStream_t s) {
   const size_t xbytes = (size_t)T * H * (act == MOE_BF16 ? 2 : 4);
@@ -223,6 +296,19 @@ void launch_router_keys(int act, const void* x, const void* w, const float* b, d
     const int maxc = (H / 8 + 63) / 64;
     const dim3 grid1((E + kRouterDecWaves - 1) / kRouterDecWaves);
     const dim3 gridg((E + kRouterGrpWaves - 1) / kRouterGrpWaves);
+    if (T > 1 && act == MOE_BF16 && maxc <= 4) {
+      const dim3 grid2((E + 1) / 2), block2(64 * 2 * kRouterSlices);
+      if (maxc <= 1)
+        MOE_LAUNCH(MOE_K_ROUTER_KEYS, k_router_keys_grp<1>, grid2, block2, 0, s, (const bf16_t*)x,
+                   (const bf16_t*)w, b, keys, T, H, E);
+      else if (maxc <= 2)
+        MOE_LAUNCH(MOE_K_ROUTER_KEYS, k_router_keys_grp<2>, grid2, block2, 0, s, (const bf16_t*)x,
+                   (const bf16_t*)w, b, keys, T, H, E);
+      else
+        MOE_LAUNCH(MOE_K_ROUTER_KEYS, k_router_keys_grp<4>, grid2, block2, 0, s, (const bf16_t*)x,
+                   (const bf16_t*)w, b, keys, T, H, E);
+      return;
+    }
 #define MOE_RK(AT, MC)                                                                          \
   do {                                                                                          \
     if (T == 1)                                                                                 \
