@@ -584,6 +584,9 @@ __device__ __forceinline__ void down1_unit2(const Tables& tb, int tier, size_t i
     load_raw<bf16_t, BITS>(r0, tb.codes[tier][MOE_DOWN], tb.dm[tier][MOE_DOWN], idx);
     load_raw<bf16_t, BITS>(r1, tb.codes[tier][MOE_DOWN], tb.dm[tier][MOE_DOWN], idx + 64);
   }
+  // every load above this point: the scheduler would otherwise pair each
+  // dense load with its MFMA, one round trip per 16 bytes
+  __builtin_amdgcn_sched_barrier(0);
   const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
   Frag<bf16_t> b;
   to_frag<bf16_t, BITS>(b, r0);
@@ -694,6 +697,204 @@ __global__ __launch_bounds__(1024) void k_decode1_down(const Item* __restrict__ 
   if constexpr (sizeof(Y) == 4) *out = sum; else *out = to_bf16(sum);
 }
 
+// ---- A6 for a bf16 token group: two work items per MFMA ---------------------
+//
+// The one-token pairing above, for groups of up to 16 tokens.  An item's
+// routed tokens (in token order) are cut into slices of at most eight; two
+// slices of the same tier share an MFMA: A rows 0-7 carry slice X's tokens' h
+// rows and rows 8-15 slice Y's, weight-column lanes 0-7 hold this
+// workgroup's eight rows of X's expert and lanes 8-15 the same rows of Y's.
+// C[r < 8][n < 8] and C[r >= 8][n >= 8] are the two slices' partial rows; the
+// cross products are never read, so every lane dequantises a block that is
+// used (the general kernel repeats the other half's rows).  Each wave adds
+// its partials into its own LDS rows, [token][output row], X's lanes then
+// Y's in two instructions (a token routed to both items never meets itself
+// in one instruction), so the order of every sum is fixed; the waves' rows
+// are then summed in wave order.  Deterministic, no global atomics.
+
+constexpr int kMaxSlices = 512;      // two slices per item, up to 256 items
+
+struct alignas(16) Slice {
+  int32_t slot;
+  int16_t tier;      // 0..2, kDenseTier, or -1 (no slice)
+  int16_t fmt;       // down code format (0: dense)
+  int32_t ntok;      // A rows used (1..8)
+  int8_t tok[8];     // token of A row j
+  int16_t hrow[8];   // h row of A row j
+  float gw[8];       // mixing weight of A row j
+};
+
+template <typename Y>
+__global__ __launch_bounds__(1024) void k_decode_down_pair(const Item* __restrict__ items,
+                                                           const int32_t* __restrict__ n_items,
+                                                           int max_items,
+                                                           const bf16_t* __restrict__ h, int T,
+                                                           Tables tb, Y* __restrict__ y, int H,
+                                                           int I) {
+  __shared__ Slice s_sl[kMaxSlices];
+  __shared__ int16_t s_pair[kMaxSlices][2];
+  __shared__ float s_acc[16][kGroup][8];
+  __shared__ int s_npairs;
+  // the two row halves of a tile sit 8 apart in the grid, on one XCD, so its
+  // lines are fetched from HBM once (the grid is a multiple of 16)
+  const int rg = ((blockIdx.x >> 4) << 3) | (blockIdx.x & 7), half = (blockIdx.x >> 3) & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lm = lane & 15, lg = lane >> 4;
+  const int nbg = I / 128, nrg = H / 16;
+  const int n = min(*n_items, max_items);
+  for (int i = tid; i < 16 * kGroup * 8; i += blockDim.x) (&s_acc[0][0][0])[i] = 0.f;
+  // slices 2u and 2u + 1 of item u: its first eight routed tokens, then the rest
+  if (tid < n) {
+    const Item& it = items[tid];
+    const int4 hd = *reinterpret_cast<const int4*>(&it);   // expert, tier, slot, bits
+    // the item's 16 routes and weights in eight loads, all in flight together
+    int rt[kGroup];
+    float gv[kGroup];
+#pragma unroll
+    for (int k = 0; k < kGroup / 4; k++) {
+      const int4 r4 = reinterpret_cast<const int4*>(it.route)[k];
+      const float4 g4 = reinterpret_cast<const float4*>(it.gw)[k];
+      rt[4 * k] = r4.x; rt[4 * k + 1] = r4.y; rt[4 * k + 2] = r4.z; rt[4 * k + 3] = r4.w;
+      gv[4 * k] = g4.x; gv[4 * k + 1] = g4.y; gv[4 * k + 2] = g4.z; gv[4 * k + 3] = g4.w;
+    }
+    int m = 0;
+#pragma unroll
+    for (int t = 0; t < kGroup; t++) {
+      if (t < T && rt[t] >= 0) {
+        Slice& sl = s_sl[2 * tid + (m >> 3)];
+        sl.tok[m & 7] = (int8_t)t;
+        sl.hrow[m & 7] = (int16_t)rt[t];
+        sl.gw[m & 7] = gv[t];
+        m++;
+      }
+    }
+    const int tier = hd.y == kDenseTier || (hd.y >= 0 && hd.y < 3) ? hd.y : -1;
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      Slice& sl = s_sl[2 * tid + k];
+      const int nt = min(max(m - 8 * k, 0), 8);
+      sl.slot = hd.z;
+      sl.tier = (int16_t)(nt > 0 ? tier : -1);
+      sl.fmt = (int16_t)(tier == kDenseTier ? 0 : (hd.w >> 8));
+      sl.ntok = nt;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // pair the slices of each class (tiers 0..2, then dense) in slice order;
+    // an odd one out pairs with nothing
+    const int ns = 2 * n;
+    int cnt[4] = {0, 0, 0, 0};
+    for (int b = 0; b < ns; b += 64) {
+      const int sidx = b + lane, t = sidx < ns ? s_sl[sidx].tier : -1;
+      const int cls = t == kDenseTier ? 3 : t;
+#pragma unroll
+      for (int c = 0; c < 4; c++) cnt[c] += __popcll(__ballot(cls == c));
+    }
+    int base[4], np = 0;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      base[c] = np;
+      np += (cnt[c] + 1) >> 1;
+    }
+    const uint64_t below = (1ull << lane) - 1ull;
+    int seen[4] = {0, 0, 0, 0};
+    for (int b = 0; b < ns; b += 64) {
+      const int sidx = b + lane, t = sidx < ns ? s_sl[sidx].tier : -1;
+      const int cls = t == kDenseTier ? 3 : t;
+      int my_pair = -1, my_side = 0;
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const uint64_t msk = __ballot(cls == c);
+        if (cls == c) {
+          const int rank = seen[c] + __popcll(msk & below);
+          my_pair = base[c] + (rank >> 1);
+          my_side = rank & 1;
+        }
+        seen[c] += __popcll(msk);
+      }
+      // one wave's LDS stores land in program order: a partner's index
+      // overwrites the -1 written with its pair's first slice
+      if (my_pair >= 0 && my_side == 0) {
+        s_pair[my_pair][0] = (int16_t)sidx;
+        s_pair[my_pair][1] = (int16_t)-1;
+      }
+      if (my_pair >= 0 && my_side == 1) s_pair[my_pair][1] = (int16_t)sidx;
+    }
+    if (lane == 0) s_npairs = np;
+  }
+  __syncthreads();
+  const int units = s_npairs * nbg;
+  const int row = rg * 16 + half * 8 + (lm & 7);
+  const int j = lm & 7;
+  for (int p0 = 2 * wave; p0 < units; p0 += 32) {
+    // super-steps c and c + 1 of pair q
+    const int q = p0 / nbg, c = p0 % nbg;
+    const int sx = __builtin_amdgcn_readfirstlane(s_pair[q][0]);
+    const int sy = __builtin_amdgcn_readfirstlane(s_pair[q][1]);
+    const Slice& X = s_sl[sx];
+    const int tier = __builtin_amdgcn_readfirstlane(X.tier);
+    const int fmt = __builtin_amdgcn_readfirstlane(X.fmt);
+    const int xslot = __builtin_amdgcn_readfirstlane(X.slot);
+    const int yslot = __builtin_amdgcn_readfirstlane(s_sl[sy < 0 ? sx : sy].slot);
+    // lanes 8-15 of a pair with a Y take Y's weights and Y's token rows
+    const bool useY = lm >= 8 && sy >= 0;
+    const Slice& S = s_sl[useY ? sy : sx];
+    const int slot = useY ? yslot : xslot;
+    const size_t idx = (((size_t)slot * nrg + rg) * nbg + c) * 64 + 16 * lg + half * 8 + j;
+    const bf16_t* dn = reinterpret_cast<const bf16_t*>(tb.dense[MOE_DOWN]) + (size_t)row * I +
+                       128 * c + 32 * lg;
+    // A row lm: row j of its slice (its first row when the slice is shorter)
+    const int hr = S.hrow[j < S.ntok ? j : 0];
+    const uint4* ap = reinterpret_cast<const uint4*>(h + (size_t)hr * I + 128 * c + 32 * lg);
+    Frag<bf16_t> a0, a1;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const uint4 u0 = ap[i], u1 = ap[16 + i];    // +16 uint4 = +128 columns
+      a0.v[4 * i] = u0.x; a0.v[4 * i + 1] = u0.y; a0.v[4 * i + 2] = u0.z; a0.v[4 * i + 3] = u0.w;
+      a1.v[4 * i] = u1.x; a1.v[4 * i + 1] = u1.y; a1.v[4 * i + 2] = u1.z; a1.v[4 * i + 3] = u1.w;
+    }
+    f32x4_t pa, pb;
+    if (fmt == 0) down1_unit2<0>(tb, tier, idx, dn, a0, a1, pa, pb);
+    else if (fmt == 4) down1_unit2<4>(tb, tier, idx, dn, a0, a1, pa, pb);
+    else if (fmt == kMx4) down1_unit2<kMx4>(tb, tier, idx, dn, a0, a1, pa, pb);
+    else if (fmt == 3) down1_unit2<3>(tb, tier, idx, dn, a0, a1, pa, pb);
+    else down1_unit2<2>(tb, tier, idx, dn, a0, a1, pa, pb);
+    // C rows 4 * lg + i: lanes lg < 2 of columns 0-7 hold X's rows, lanes
+    // lg >= 2 of columns 8-15 Y's
+    const bool xl = lg < 2 && lm < 8, yl = sy >= 0 && lg >= 2 && lm >= 8;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int jr = 4 * (lg & 1) + i;
+      if (xl && jr < X.ntok) {
+        const float g = X.gw[jr];
+        atomicAdd(&s_acc[wave][X.tok[jr]][j], g * pa[i] + g * pb[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int jr = 4 * (lg & 1) + i;
+      if (yl && jr < S.ntok) {
+        const float g = S.gw[jr];
+        atomicAdd(&s_acc[wave][S.tok[jr]][j], g * pa[i] + g * pb[i]);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < T * 8) {
+    const int t = tid >> 3, col = tid & 7;
+    float pr[16];
+#pragma unroll
+    for (int w = 0; w < 16; w++) pr[w] = s_acc[w][t][col];
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; w++) sum += pr[w];
+    Y* out = y + (size_t)t * H + rg * 16 + half * 8 + col;
+    if constexpr (sizeof(Y) == 4) *out = sum; else *out = to_bf16(sum);
+  }
+}
+
 }  // namespace
 
 void launch_decode_gateup(int act, const Item* items, const int32_t* n_items, int max_items,
@@ -778,6 +979,17 @@ void launch_decode_down(int act, int y_dt, const Item* items, const int32_t* n_i
     else
       MOE_LAUNCH(MOE_K_DECODE_DOWN, k_decode1_down<float>, grid, dim3(1024), 0, s, items,
                  n_items, max_items, (const bf16_t*)h, tb, (float*)y, H, I);
+    return;
+  }
+  if (T > 1 && T <= kGroup && act == MOE_BF16 && max_items <= kMaxSlices / 2 &&
+      (I / 128) % 2 == 0) {
+    // a token group: two item slices per MFMA
+    if (y_dt == MOE_BF16)
+      MOE_LAUNCH(MOE_K_DECODE_DOWN, k_decode_down_pair<bf16_t>, grid, dim3(1024), 0, s, items,
+                 n_items, max_items, (const bf16_t*)h, T, tb, (bf16_t*)y, H, I);
+    else
+      MOE_LAUNCH(MOE_K_DECODE_DOWN, k_decode_down_pair<float>, grid, dim3(1024), 0, s, items,
+                 n_items, max_items, (const bf16_t*)h, T, tb, (float*)y, H, I);
     return;
   }
 #define MOE_DN(AT, YT, PB, ST)                                                                 \
