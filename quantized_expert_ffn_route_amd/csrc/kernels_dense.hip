@@ -223,7 +223,20 @@ __global__ __launch_bounds__(kDThreads) void k_dense(DArgs a) {
   }
   if (norms && n0 + (int)threadIdx.x < NN) a.wnorm2[n0 + threadIdx.x] = wsq;
 
-  // epilogue: lane holds C[4 lg + i][lm] of each 16x16 tile
+  // epilogue: lane holds C[4 lg + i][lm] of each 16x16 tile.  The router
+  // bias of the lane's four columns is read once, before any store (read
+  // inside the loop it would be fetched again after every store that might
+  // alias it, one round trip per output)
+  float bv[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (MODE == kDRouter || COMB) {
+    if (!gu && a.bias) {
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int n = n0 + wn * 64 + 16 * u + lm;
+        bv[u] = a.bias[n < NN ? n : NN - 1];
+      }
+    }
+  }
 #pragma unroll
   for (int t = 0; t < MTW; t++) {
 #pragma unroll
@@ -243,7 +256,7 @@ __global__ __launch_bounds__(kDThreads) void k_dense(DArgs a) {
           const int n = n0 + wn * 64 + 16 * u + lm;
           if (n < NN) {
             float v = acc[t][u][i];
-            if constexpr (MODE == kDRouter || COMB) v += a.bias ? a.bias[n] : 0.0f;
+            if constexpr (MODE == kDRouter || COMB) v += bv[u];
             a.outf[(size_t)m * NN + n] = v;
           }
         }
