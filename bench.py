@@ -583,7 +583,7 @@ TRAFFIC_KERNELS = [
     ("k_dense<0,", "route_router_approx"), ("k_dense<3,", "router_approx"),
     ("k_dense<1,", "prefill_shared_gateup"),
     ("k_dense<2,", "prefill_shared_down"), ("k_topk_recheck", "topk_recheck"),
-    ("k_combine", "combine"),
+    ("k_combine", "combine"), ("k_dense<4,", "combine"),
 ]
 
 

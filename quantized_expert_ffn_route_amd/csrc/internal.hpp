@@ -178,6 +178,12 @@ void launch_dense_shared_gateup(const void* x, int T, const void* w_gate, const 
 // rows[t][n] = fp32 h_s[t] . w_down[n].
 void launch_dense_shared_down(const void* h_s, int T, const void* w_down, float* rows, int H,
                               int I, hipStream_t s);
+// The shared expert's down projection with the combine in its epilogue:
+// y[t] = shared row + the token's K weighted route rows, in route order.
+void launch_dense_shared_down_combine(const void* h_s, int T, const void* w_down,
+                                      const float* route_rows, const int32_t* route_pos,
+                                      const float* topk_w, int K, int H, int I, void* y, int y_dt,
+                                      hipStream_t s);
 
 // ---- host packer (pack.cpp; no HIP calls) ----
 

@@ -32,7 +32,9 @@ constexpr int kDStages = 3;
 
 // kDRouterGateUp: one launch over the router's column tiles followed by the
 // shared expert's gate/up column tiles -- both multiply the same token rows.
-enum DenseMode { kDRouter = 0, kDGateUp = 1, kDDown = 2, kDRouterGateUp = 3 };
+// kDDownCombine: the shared expert's down projection whose epilogue adds the
+// token's K weighted route rows (the combine) and stores y.
+enum DenseMode { kDRouter = 0, kDGateUp = 1, kDDown = 2, kDRouterGateUp = 3, kDDownCombine = 4 };
 
 struct DArgs {
   const bf16_t* a;    // token rows [M][K]
@@ -49,6 +51,14 @@ struct DArgs {
   const bf16_t* g_up;
   bf16_t* g_out;
   int g_N;            // intermediate size
+  // kDDownCombine: route rows [T*K][N] fp32, the row of route (t, k) and its
+  // mixing weight, and the output y [M][N] (bf16 when y_bf16)
+  const float* route_rows;
+  const int32_t* route_pos;
+  const float* topk_w;
+  int topK;
+  void* y;
+  int y_bf16;
 };
 
 template <int N>
@@ -223,6 +233,75 @@ __global__ __launch_bounds__(kDThreads) void k_dense(DArgs a) {
   }
   if (norms && n0 + (int)threadIdx.x < NN) a.wnorm2[n0 + threadIdx.x] = wsq;
 
+  if constexpr (MODE == kDDownCombine) {
+    // the tile's shared rows go to LDS (the ring is free once every wave has
+    // left the loop), then each token row of the tile gets its K weighted
+    // route rows added in route order, as a float4 per thread: the same
+    // arithmetic as the separate combine, with no shared row in HBM
+    constexpr int TS = kDRowsB + 4;                       // padded row (floats)
+    static_assert(MROWS * TS * 4 <= kDStages * STAGE, "tile fits the ring");
+    float* tile = reinterpret_cast<float*>(s_ring);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < MTW; t++)
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+          tile[(wm * 16 * MTW + 16 * t + 4 * lg + i) * TS + wn * 64 + 16 * u + lm] = acc[t][u][i];
+    __syncthreads();
+    const int c4 = threadIdx.x & 31, n = n0 + 4 * c4;
+    const int K = a.topK;
+    constexpr int KB = 16;
+    for (int r = threadIdx.x >> 5; r < MROWS; r += kDThreads / 32) {
+      const int m = m0 + r;
+      if (m >= a.M || n >= a.N) continue;
+      float4 v = *reinterpret_cast<const float4*>(tile + r * TS + 4 * c4);
+      for (int k0 = 0; k0 < K; k0 += KB) {
+        float4 rv[KB];
+        float g[KB];
+        // every route's position and weight first, then every row: a row
+        // load issued between two position loads would make the second one's
+        // wait also wait for that row (loads complete in order).  Guards, not
+        // breaks, so the loops unroll and the arrays stay in registers.
+        int pos[KB];
+#pragma unroll
+        for (int j = 0; j < KB; j++) {
+          if (k0 + j < K) {
+            const size_t q = (size_t)m * K + k0 + j;
+            pos[j] = a.route_pos[q];
+            g[j] = a.topk_w[q];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < KB; j++) {
+          if (k0 + j < K) {
+            // each route row is read exactly once: keep it out of the caches
+            typedef float f4v __attribute__((ext_vector_type(4)));
+            const f4v x4 = __builtin_nontemporal_load(
+                reinterpret_cast<const f4v*>(a.route_rows + (size_t)pos[j] * a.N + n));
+            rv[j] = make_float4(x4.x, x4.y, x4.z, x4.w);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < KB; j++) {
+          if (k0 + j >= K) continue;
+          v.x = __builtin_fmaf(g[j], rv[j].x, v.x);
+          v.y = __builtin_fmaf(g[j], rv[j].y, v.y);
+          v.z = __builtin_fmaf(g[j], rv[j].z, v.z);
+          v.w = __builtin_fmaf(g[j], rv[j].w, v.w);
+        }
+      }
+      if (a.y_bf16) {
+        bf16_t* out = reinterpret_cast<bf16_t*>(a.y) + (size_t)m * a.N + n;
+        *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16(v.x, v.y), pack_bf16(v.z, v.w));
+      } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + (size_t)m * a.N + n) = v;
+      }
+    }
+    return;
+  }
+
   // epilogue: lane holds C[4 lg + i][lm] of each 16x16 tile.  The router
   // bias of the lane's four columns is read once, before any store (read
   // inside the loop it would be fetched again after every store that might
@@ -329,6 +408,21 @@ void launch_dense_shared_down(const void* h_s, int T, const void* w_down, float*
   d.b0 = reinterpret_cast<const bf16_t*>(w_down);
   d.outf = rows;
   launch_dense<kDDown, 2>(d, MOE_K_PREFILL_SHARED_DOWN, s);
+}
+
+void launch_dense_shared_down_combine(const void* h_s, int T, const void* w_down,
+                                      const float* route_rows, const int32_t* route_pos,
+                                      const float* topk_w, int K, int H, int I, void* y, int y_dt,
+                                      hipStream_t s) {
+  DArgs d = dargs(h_s, T, H, I);
+  d.b0 = reinterpret_cast<const bf16_t*>(w_down);
+  d.route_rows = route_rows;
+  d.route_pos = route_pos;
+  d.topk_w = topk_w;
+  d.topK = K;
+  d.y = y;
+  d.y_bf16 = y_dt == MOE_BF16;
+  launch_dense<kDDownCombine, 2>(d, MOE_K_COMBINE, s);
 }
 
 }  // namespace moe

@@ -741,13 +741,20 @@ int moe_forward_prefill(const moe_dims* dims, const moe_layer* layer, const void
                      prefill_tile_rows(dims->act), tiles, n_tiles, stream);
   launch_prefill_gateup(dims->act, offsets, sorted, tiles, n_tiles, w.max_tiles, layer->tier_map,
                         E, K, x, tb, h, H, I, stream);
+  // bf16 with a shared expert: its down projection runs after the routed one
+  // and adds the route rows in its epilogue (no shared rows in HBM)
+  const bool fused_combine = dims->has_shared && dims->act == MOE_BF16;
   if (dims->has_shared) {
     if (!shared_gu_done) launch_prefill_shared_gateup(dims->act, x, T, tb, h_s, H, I, stream);
-    launch_prefill_shared_down(dims->act, h_s, T, tb, shared_rows, H, I, stream);
+    if (!fused_combine) launch_prefill_shared_down(dims->act, h_s, T, tb, shared_rows, H, I, stream);
   }
   launch_prefill_down(dims->act, offsets, sorted, tiles, n_tiles, w.max_tiles, layer->tier_map, E,
                       K, h, tb, route_rows, H, I, stream);
-  launch_combine(y_dt, shared_rows, route_rows, route_pos, wts, T, K, H, y, stream);
+  if (fused_combine)
+    launch_dense_shared_down_combine(h_s, T, tb.dense[MOE_DOWN], route_rows, route_pos, wts, K, H,
+                                     I, y, y_dt, stream);
+  else
+    launch_combine(y_dt, shared_rows, route_rows, route_pos, wts, T, K, H, y, stream);
   return hip_status();
 }
 
