@@ -16,8 +16,9 @@ Also reported: per-kernel durations from the library's launch trace (HIP
 events attached to each kernel dispatch) over an eager pass of the same
 16 x 48 calls right after the timed region, the HBM roofline of the dominant
 decode kernel, prefill of 4096 tokens through one layer (rotating over the
-stack) with the MFMA roofline of its grouped GEMM, and the CPU oracle timed
-on a bounded sample.
+stack; timed as replays of one graph of 8 layer calls, its per-kernel figures
+from a traced eager pass) with the MFMA roofline of its grouped GEMM, and the
+CPU oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 64] [--warmup 16]
 """
@@ -769,16 +770,37 @@ def main():
         Yp = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
         wsp = torch.empty(M.workspace_bytes("prefill", d, layers[0].cs, T, M.MOE_BF16),
                           dtype=torch.uint8, device="cuda")
-        for k in range(2):
-            M.forward_prefill(d, layers[k].cs, Xp, Yp, M.MOE_BF16, ws=wsp)
-        torch.cuda.synchronize()
-        ptrace = M.Trace(64 * args.prefill_steps)
-        t0 = time.perf_counter()
-        with ptrace:
+        def prefill_pass():
             for k in range(args.prefill_steps):
                 M.forward_prefill(d, layers[k % N_LAYERS].cs, Xp, Yp, M.MOE_BF16, ws=wsp)
+
+        prefill_pass()                           # warm code objects
         torch.cuda.synchronize()
-        pwall = time.perf_counter() - t0
+        # timed: replays of one graph holding prefill_steps layer calls (no
+        # events between the kernels); per-kernel figures: a traced eager pass
+        pgraph = None
+        if not args.eager:
+            pgraph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(pgraph):
+                prefill_pass()
+            pgraph.replay()
+            torch.cuda.synchronize()
+        n_rep = 3
+        t0 = time.perf_counter()
+        for _ in range(n_rep):
+            if pgraph is None:
+                prefill_pass()
+            else:
+                pgraph.replay()
+        torch.cuda.synchronize()
+        pwall = (time.perf_counter() - t0) / n_rep
+        ptrace = M.Trace(64 * args.prefill_steps)
+        t1 = time.perf_counter()
+        with ptrace:
+            prefill_pass()
+        torch.cuda.synchronize()
+        pwall_traced = time.perf_counter() - t1
+        del pgraph
         pk = {}
         for name, ms in ptrace.durations_ms():
             pk.setdefault(name, []).append(ms)
@@ -792,6 +814,9 @@ def main():
             "workload": f"prefill {T} tokens, one full-size layer (rotating over the stack)",
             "tokens_per_s": round(T * args.prefill_steps / pwall, 1),
             "ms_per_layer": round(1e3 * pwall / args.prefill_steps, 3),
+            "timing": ("graph replays" if not args.eager else "eager launches")
+                      + f" of {args.prefill_steps} layer calls, mean of {n_rep}",
+            "ms_per_layer_traced_eager": round(1e3 * pwall_traced / args.prefill_steps, 3),
             "layer_tflops": round(layer_flops / (pwall / args.prefill_steps) / 1e12, 1),
             "kernels_avg_us": {n: round(1e3 * float(np.sum(v)) / steps, 2) for n, v in pk.items()},
             "roofline": {"bound": "mfma", "kernel": "k_prefill<routed gate/up>",
