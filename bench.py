@@ -70,6 +70,8 @@ def parse():
                     help="tokens of the one-thread oracle figure (0: skip)")
     ap.add_argument("--no-verify", action="store_true",
                     help="skip the verify-batch leg (T = 4, 8, 16 correlated tokens)")
+    ap.add_argument("--no-cold-tier", action="store_true",
+                    help="skip the leg with the 2-bit tier in pinned host memory")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-ceiling leg (torch GEMV over 48 x 25.8 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -533,6 +535,79 @@ def verify_batches(M, torch, spec, d, layers, args, sizes=(4, 8, 16), n_graphs=4
             "unit": "MoE-layer tokens/s", **out}
 
 
+def host_cold_tier(M, torch, spec, d, layers, args, n_graphs=4, tier=2):
+    """Batch-1 decode with one tier kept in system RAM (P1 "step 3: split every
+    layer into hot and cold"): the same 48 layers with tier `tier`'s tables
+    copied into pinned host memory mapped into the device's address space, so
+    the kernels read those experts over the host link.  Reports us per layer,
+    the host-resident bytes a layer-token reads (the routed experts of that
+    tier) and whether the outputs equal the all-HBM layers' bit for bit."""
+    import copy
+    H, K = spec.hidden, spec.top_k
+    host_layers = []
+    for lay in layers:
+        hl = copy.copy(lay)
+        hl.codes = [list(r) for r in lay.codes]
+        hl.dm = [list(r) for r in lay.dm]
+        for m in range(3):
+            hl.codes[tier][m] = lay.codes[tier][m].to("cpu").pin_memory()
+            hl.dm[tier][m] = lay.dm[tier][m].to("cpu").pin_memory()
+        hl.host_tiers = (tier,)
+        hl.cs = hl.c_struct()
+        host_layers.append(hl)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(args.seed + 31)
+    X = torch.randn((n_graphs, N_LAYERS, 1, H), generator=gen, device="cuda").to(torch.bfloat16)
+    Y = torch.empty((N_LAYERS, 1, H), dtype=torch.bfloat16, device="cuda")
+    Yd = torch.empty_like(Y)
+    IDS = torch.empty((n_graphs, N_LAYERS, 1, K), dtype=torch.int32, device="cuda")
+    ws = torch.empty(M.workspace_bytes("decode", d, layers[0].cs, 1, M.MOE_BF16),
+                     dtype=torch.uint8, device="cuda")
+
+    def token_pass(g, lays, out):
+        for l in range(N_LAYERS):
+            M.forward_decode(d, lays[l].cs, X[g, l], out[l], M.MOE_BF16, IDS[g, l], None, ws=ws)
+
+    # bit-for-bit against the all-HBM layers on the same inputs
+    token_pass(0, layers, Yd)
+    token_pass(0, host_layers, Y)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(Y.view(torch.int16), Yd.view(torch.int16)))
+    graphs = []
+    for g in range(n_graphs):
+        token_pass(g, host_layers, Y)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            token_pass(g, host_layers, Y)
+        graphs.append(graph)
+    for k in range(args.warmup):
+        graphs[k % n_graphs].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        graphs[k % n_graphs].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ids = IDS.cpu().numpy()
+    per_expert = sum(table_bytes(spec, spec.tier_bits[tier], m) for m in (0, 1)) + \
+        table_bytes(spec, down_format(spec, tier), 2)
+    n_cold = [sum(1 for e in ids[g, l, 0] if int(layers[l].tmap_host[e]) >> 16 == tier)
+              for g in range(n_graphs) for l in range(N_LAYERS)]
+    us_layer = 1e6 * wall / (args.steps * N_LAYERS)
+    out = {"workload": f"batch-1 decode through the 48-layer stack with tier {tier} "
+                       f"({spec.n_slots[tier]} experts, {fmt_name(spec.tier_bits[tier])}) in pinned "
+                       "host memory read over the host link",
+           "layer_tokens_per_s": round(N_LAYERS * args.steps / wall, 1),
+           "us_per_layer": round(us_layer, 3),
+           "cold_routes_per_token": round(float(np.mean(n_cold)), 3),
+           "host_bytes_per_layer": int(np.mean(n_cold) * per_expert),
+           "bit_identical_to_hbm": same}
+    log(f"host cold tier: {out}")
+    del graphs
+    return out
+
+
 def streaming_ceiling(torch, layer_bytes, args):
     """Measured ceiling for one layer's bytes: torch's own bf16 GEMV (one
     launch streaming a [rows x 2048] matrix of the layer's size) over 48
@@ -762,6 +837,7 @@ def main():
 
     ceiling = None if args.no_ceiling else streaming_ceiling(torch, layer_bytes or 25_838_079, args)
     verify = None if args.no_verify else verify_batches(M, torch, spec, d, layers, args)
+    cold = None if args.no_cold_tier else host_cold_tier(M, torch, spec, d, layers, args)
 
     prefill = None
     if not args.no_prefill:
@@ -866,6 +942,7 @@ def main():
         "layer_roofline": layer_roofline,
         "streaming_ceiling": ceiling,
         "verify": verify,
+        "host_cold_tier": cold,
         "kernels": kernels,
         "prefill": prefill,
         "cpu_baseline": cpu,

@@ -119,7 +119,12 @@ typedef struct {
  *             ((s*(R/16) + r/16)*(C/128) + j/4)*64 + 16*(j%4) + r%16
  *           and its code field is codes[index*4*bits .. +4*bits) (bit layout
  *           below), dm[index] = bits(d) | bits(m) << 16.  May be NULL for a
- *           tier with n_slots == 0.
+ *           tier with n_slots == 0.  A tier's codes and dm may instead live
+ *           in pinned host memory mapped into the device's address space
+ *           (hipHostMalloc; pass the address hipHostGetDevicePointer
+ *           returns): the kernels then read that tier over the host link,
+ *           the cold tier of [P1] "step 3: split every layer into hot and
+ *           cold" kept in system RAM.  Results are unchanged.
  *           Code field of a b-bit block: b little-endian 32-bit words; each
  *           word's low half holds even-numbered codes and its high half the
  *           following odd codes at the same offsets, packed from bit 0:
@@ -198,7 +203,9 @@ size_t moe_tier_table_bytes(const moe_dims* dims, int32_t bits, int32_t n_slots,
  *   slot_expert_out host [E] int32: expert id at each rank, or NULL.
  *   dst             tables to fill, or NULL.  If dst_on_device != 0, dst's
  *                   codes/dm pointers and dst->tier_map are device buffers of
- *                   moe_tier_table_bytes() / E*4 bytes; the call packs on the
+ *                   moe_tier_table_bytes() / E*4 bytes (a tier's codes/dm may
+ *                   instead be pinned host memory mapped into the device's
+ *                   address space, see moe_layer); the call packs on the
  *                   host, copies on `stream` and synchronises it.  If
  *                   dst_on_device == 0 they are host buffers and no HIP call
  *                   is made (dst->tier_map may then be NULL).

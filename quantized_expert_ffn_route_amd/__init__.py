@@ -166,6 +166,31 @@ def _stream(stream) -> Optional[int]:
     return torch.cuda.current_stream().cuda_stream
 
 
+_HIP = None
+
+
+def _mapped_ptr(t) -> Optional[int]:
+    """Device address of a pinned host tensor (hipHostGetDevicePointer).
+
+    Raises unless the memory is pinned and mapped into the device's address
+    space, so no kernel is ever handed a host address it cannot read."""
+    global _HIP
+    if t is None:
+        return None
+    if not t.is_pinned():
+        raise ValueError("host-resident tier tables must be pinned host memory")
+    if _HIP is None:
+        _HIP = ctypes.CDLL("libamdhip64.so")
+        _HIP.hipHostGetDevicePointer.restype = ctypes.c_int
+        _HIP.hipHostGetDevicePointer.argtypes = [POINTER(c_void_p), c_void_p, ctypes.c_uint]
+    dptr = c_void_p()
+    rc = _HIP.hipHostGetDevicePointer(ctypes.byref(dptr), c_void_p(t.data_ptr()), 0)
+    if rc != 0 or not dptr.value:
+        raise RuntimeError(f"hipHostGetDevicePointer failed ({rc}): the pinned table is not "
+                           "mapped into the device's address space")
+    return dptr.value
+
+
 def _i32x3(v: Sequence[int]):
     return (c_int32 * 3)(*[int(a) for a in v])
 
@@ -334,10 +359,12 @@ class DeviceLayer:
     """
 
     def __init__(self, d: MoeDims, n_slots, tier_bits, router, shared=None, device="cuda",
-                 down_bits=None):
+                 down_bits=None, host_tiers=()):
         import torch
 
         self.d = d
+        # tiers whose tables sit in pinned, device-mapped host memory
+        self.host_tiers = tuple(int(t) for t in host_tiers)
         self.n_slots = tuple(int(v) for v in n_slots)
         self.tier_bits = tuple(int(v) for v in tier_bits)
         # down matrices: their own ladder, or the tier's width (0)
@@ -367,12 +394,14 @@ class DeviceLayer:
                 bits = self.matrix_bits(t, m)
                 nc = tier_table_bytes(d, bits, self.n_slots[t], m, MOE_CODES)
                 nd = tier_table_bytes(d, bits, self.n_slots[t], m, MOE_DM)
-                self.codes[t][m] = torch.zeros(nc, dtype=torch.uint8, device=device)
+                on_host = t in self.host_tiers
+                kw = {"pin_memory": True} if on_host else {"device": device}
+                self.codes[t][m] = torch.zeros(nc, dtype=torch.uint8, **kw)
                 # (d, m) words, or one E8M0 byte per block for MXFP4
                 if bits == MOE_MXFP4:
-                    self.dm[t][m] = torch.zeros(nd, dtype=torch.uint8, device=device)
+                    self.dm[t][m] = torch.zeros(nd, dtype=torch.uint8, **kw)
                 else:
-                    self.dm[t][m] = torch.zeros(nd // 4, dtype=torch.int32, device=device)
+                    self.dm[t][m] = torch.zeros(nd // 4, dtype=torch.int32, **kw)
         self.shared = None if shared is None else [to_dev(s, act_t) for s in shared]
 
     def matrix_bits(self, t: int, m: int) -> int:
@@ -389,8 +418,9 @@ class DeviceLayer:
         L.down_bits = _i32x3(self.down_bits)
         for t in range(3):
             for m in range(3):
-                L.codes[t][m] = _ptr(self.codes[t][m])
-                L.dm[t][m] = _ptr(self.dm[t][m])
+                ptr = _mapped_ptr if t in self.host_tiers else _ptr
+                L.codes[t][m] = ptr(self.codes[t][m])
+                L.dm[t][m] = ptr(self.dm[t][m])
         if self.shared is not None:
             for m in range(3):
                 L.w_shared[m] = _ptr(self.shared[m])

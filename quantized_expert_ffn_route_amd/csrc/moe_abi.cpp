@@ -518,13 +518,16 @@ int moe_build_tiers(const moe_dims* dims, const uint64_t* popularity, const int3
   if (status != MOE_OK) return status;
 
   if (dst_on_device) {
+    // a tier's tables are device memory or pinned, device-mapped host memory
+    // (a tier kept in host memory): the runtime takes the direction from the
+    // destination pointer
     for (int t = 0; t < 3; t++) {
       if (n_slots[t] == 0) continue;
       for (int m = 0; m < 3; m++) {
         if (hipMemcpyAsync(dst->codes[t][m], hc[t][m], stage_codes[3 * t + m].size(),
-                           hipMemcpyHostToDevice, stream) != hipSuccess ||
+                           hipMemcpyDefault, stream) != hipSuccess ||
             hipMemcpyAsync(dst->dm[t][m], hd[t][m], stage_dm[3 * t + m].size(),
-                           hipMemcpyHostToDevice, stream) != hipSuccess)
+                           hipMemcpyDefault, stream) != hipSuccess)
           return MOE_EHIP;
       }
     }

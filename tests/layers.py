@@ -49,11 +49,13 @@ def popularity_from_calibration(spec, w_router, bias, seed, n=1024):
 
 
 def make_layer(spec: synth.LayerSpec, seed: int = 0, source: str = "f32",
-               router_override=None, device: bool = True, n_calib: int = 1024) -> TestLayer:
+               router_override=None, device: bool = True, n_calib: int = 1024,
+               host_tiers=()) -> TestLayer:
     """Build one layer for both sides.
 
     source="f32": fp32 weights quantised by each side's own quantiser.
     source="codes": random pre-quantised blocks (full-size layers).
+    host_tiers: tiers whose library tables sit in pinned host memory.
     """
     import quantized_expert_ffn_route_amd as M
 
@@ -118,7 +120,7 @@ def make_layer(spec: synth.LayerSpec, seed: int = 0, source: str = "f32",
     tmap = tmap_o
     if device:
         dl = M.DeviceLayer(d, spec.n_slots, spec.tier_bits, (w_router, bias), shared,
-                           down_bits=spec.down_bits)
+                           down_bits=spec.down_bits, host_tiers=host_tiers)
         tmap, _ = dl.load_experts(pop, src)
         del src_arrays
     return TestLayer(spec=spec, ol=ol, dl=dl, tier_map=tmap, popularity=pop)

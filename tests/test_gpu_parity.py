@@ -795,3 +795,28 @@ def test_check_layer_flags_bad_tier_maps(mid):
         mid.dl.tier_map.copy_(good)
         torch.cuda.synchronize()
     assert M.check_layer(d, L) == M.MOE_OK
+
+
+# The coldest tier kept in system RAM (P1 "step 3: split every layer into hot
+# and cold"): its tables in pinned host memory mapped into the device's
+# address space, read by the same kernels over the host link.  Routing, ids
+# and outputs are bit-identical to the layer whose tables all sit in HBM.
+def test_host_resident_cold_tier(mid):
+    hl = make_layer(MID, seed=5, host_tiers=(2,))
+    for m in range(3):
+        assert hl.dl.codes[2][m].device.type == "cpu" and hl.dl.codes[2][m].is_pinned()
+        assert hl.dl.codes[0][m].is_cuda and hl.dl.codes[1][m].is_cuda
+    np.testing.assert_array_equal(hl.tier_map, mid.tier_map)
+    assert M.check_layer(hl.dl.d, hl.dl.c_struct()) == M.MOE_OK
+    for T in (1, 5, 40):
+        x = synth.tokens(MID, T, 300 + T)
+        ref = O.moe_layer(act_f64(x, "bf16"), mid.ol)
+        for name, run in (("decode", run_decode), ("prefill", run_prefill)):
+            yd, idd, wd = run(mid, x)[:3]
+            yh, idh, wh = run(hl, x)[:3]
+            np.testing.assert_array_equal(idh, ref["ids"])
+            np.testing.assert_array_equal(idh, idd)
+            np.testing.assert_array_equal(wh.view(np.uint32), wd.view(np.uint32))
+            assert torch.equal(yh.view(torch.int32), yd.view(torch.int32)), (name, T)
+            check_y(yh, ref["y"], "bf16", f"{name} T={T}, 2-bit tier in host memory")
+
