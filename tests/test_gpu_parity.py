@@ -239,6 +239,49 @@ def test_decode_graph_replays_match_eager(mid, full):
         del graph
 
 
+def test_prefill_graph_replays_match_eager(mid, full):
+    # the benchmark times captured prefill calls: every replay, with new
+    # inputs copied in and eager calls on the same workspace in between, must
+    # give the eager results bit for bit (ids, weights, sort, outputs)
+    for tl, T in ((mid, 333), (full, 4096)):
+        spec, d, L = tl.spec, tl.dl.d, tl.dl.c_struct()
+        H, K, E = spec.hidden, spec.top_k, spec.n_experts
+        X = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        Y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        IDS = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        W = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        OFF = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+        SRT = torch.empty(T * K, dtype=torch.int32, device="cuda")
+        ws = torch.empty(M.workspace_bytes("prefill", d, L, T, M.MOE_BF16), dtype=torch.uint8,
+                         device="cuda")
+        xs = [synth.tokens(spec, T, 140 + i) for i in range(3)]
+        outs = (Y, IDS, W, OFF, SRT)
+        eager = []
+        for i in range(3):
+            X.copy_(dev(xs[i], "bf16"))
+            M.forward_prefill(d, L, X, Y, M.MOE_BF16, IDS, W, OFF, SRT, ws=ws)
+            torch.cuda.synchronize()
+            eager.append([o.clone() for o in outs])
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            M.forward_prefill(d, L, X, Y, M.MOE_BF16, IDS, W, OFF, SRT, ws=ws)
+        torch.cuda.synchronize()
+        other = dev(synth.tokens(spec, T, 150), "bf16")
+        for rep in range(3):
+            for i in range(3):
+                X.copy_(dev(xs[i], "bf16"))
+                graph.replay()
+                torch.cuda.synchronize()
+                for o, e in zip(outs, eager[i]):
+                    assert torch.equal(o.view(torch.int16) if o.dtype == torch.bfloat16 else o,
+                                       e.view(torch.int16) if e.dtype == torch.bfloat16 else e), \
+                        (spec.hidden, T, rep, i)
+                # eager work on the same workspace between replays
+                M.forward_prefill(d, L, other, torch.empty_like(Y), M.MOE_BF16, ws=ws)
+                torch.cuda.synchronize()
+        del graph
+
+
 @pytest.mark.parametrize("T", [4, 8, 16])
 def test_verify_full_correlated(full, T):
     x = synth.correlated_tokens(full.spec, T, 16 + T)
