@@ -540,3 +540,33 @@ def test_check_layer_argument_errors_without_gpu():
     L.tier_map = None
     assert lib.moe_check_layer(ctypes.byref(d), ctypes.byref(L), None) == M.MOE_EINVAL
     assert lib.moe_check_layer(None, ctypes.byref(L), None) == M.MOE_EINVAL
+
+
+def test_c_program_uses_the_abi(tmp_path):
+    # the header compiled as C11 and the library called from a C program:
+    # no Python, no torch (host-only calls, no GPU)
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    exe = tmp_path / "c_abi_host"
+    lib_dir = os.path.dirname(M.library_path())
+    build = subprocess.run(
+        [cc, "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+         f"-I{os.path.join(ROOT, 'include')}", f"-I{os.path.join(rocm, 'include')}",
+         os.path.join(ROOT, "tests", "c_abi_host.c"), "-o", str(exe), f"-L{lib_dir}", "-lmoe",
+         f"-Wl,-rpath,{lib_dir}"], capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    # the HIP runtime the library links against: torch's copy if it ships one
+    env = dict(os.environ)
+    try:
+        import torch
+        env["LD_LIBRARY_PATH"] = os.pathsep.join(
+            [os.path.join(os.path.dirname(torch.__file__), "lib"), env.get("LD_LIBRARY_PATH", "")])
+    except ImportError:
+        pass
+    run = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=60)
+    assert run.returncode == 0 and run.stdout.strip() == "ok", run.stdout + run.stderr
