@@ -180,7 +180,15 @@ def _mapped_ptr(t) -> Optional[int]:
     if not t.is_pinned():
         raise ValueError("host-resident tier tables must be pinned host memory")
     if _HIP is None:
-        _HIP = ctypes.CDLL("libamdhip64.so")
+        # the HIP runtime already loaded with the library (same soname)
+        for name in ("libamdhip64.so.7", "libamdhip64.so"):
+            try:
+                _HIP = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        if _HIP is None:
+            raise MoeLibraryMissing("the HIP runtime (libamdhip64) cannot be loaded")
         _HIP.hipHostGetDevicePointer.restype = ctypes.c_int
         _HIP.hipHostGetDevicePointer.argtypes = [POINTER(c_void_p), c_void_p, ctypes.c_uint]
     dptr = c_void_p()
