@@ -589,6 +589,23 @@ def host_cold_tier(M, torch, spec, d, layers, args, n_graphs=4, tier=2):
         graphs[k % n_graphs].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # a 4096-token prefill touches every expert, so it reads the whole tier
+    # over the host link: three calls on layer 0, after one untimed
+    pf = None
+    if not args.no_prefill:
+        T = args.prefill_tokens
+        Xp = torch.randn((T, H), generator=gen, device="cuda").to(torch.bfloat16)
+        Yp = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        wsp = torch.empty(M.workspace_bytes("prefill", d, host_layers[0].cs, T, M.MOE_BF16),
+                          dtype=torch.uint8, device="cuda")
+        M.forward_prefill(d, host_layers[0].cs, Xp, Yp, M.MOE_BF16, ws=wsp)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(3):
+            M.forward_prefill(d, host_layers[0].cs, Xp, Yp, M.MOE_BF16, ws=wsp)
+        torch.cuda.synchronize()
+        pf = round(1e3 * (time.perf_counter() - t1) / 3, 3)
+        del Xp, Yp, wsp
     ids = IDS.cpu().numpy()
     per_expert = sum(table_bytes(spec, spec.tier_bits[tier], m) for m in (0, 1)) + \
         table_bytes(spec, down_format(spec, tier), 2)
@@ -602,7 +619,10 @@ def host_cold_tier(M, torch, spec, d, layers, args, n_graphs=4, tier=2):
            "us_per_layer": round(us_layer, 3),
            "cold_routes_per_token": round(float(np.mean(n_cold)), 3),
            "host_bytes_per_layer": int(np.mean(n_cold) * per_expert),
-           "bit_identical_to_hbm": same}
+           "bit_identical_to_hbm": same,
+           "tier_bytes": int(spec.n_slots[tier] * per_expert),
+           "prefill_ms_per_layer": pf,
+           "prefill_tokens": None if pf is None else args.prefill_tokens}
     log(f"host cold tier: {out}")
     del graphs
     return out
