@@ -340,6 +340,15 @@ def prof_summary(out_dir, command, title):
             print(f"| `{n}` | {a[0]} | {a[1] / a[0]:.2f} | {a[2]:.2f} | {a[3]:.2f} | {a[4]} | {a[5]} "
                   f"| {a[6]} | {a[7]} |")
         print()
+        # the streaming ceiling leg: torch's bf16 GEMV over one layer's bytes
+        # (a library kernel, matched by the trace's include regex)
+        ceil = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
+                if r.get("Kernel_Name", "").startswith("Cijk_") or "gemv" in r.get("Kernel_Name", "")]
+        if ceil:
+            print("Streaming ceiling leg (`torch.mv`, bf16, one layer's bytes per launch): "
+                  f"{len(ceil)} launches, {np.median(ceil):.2f} us median "
+                  f"[{np.percentile(ceil, 10):.2f}-{np.percentile(ceil, 90):.2f}], "
+                  f"{np.mean(ceil):.2f} us mean.\n")
         # the decode kernels by phase of the bench run: eager warm-up passes
         # before capture, graph replays, and the traced eager pass (the last
         # N_GRAPHS x N_LAYERS launches) whose events give the bench line's
